@@ -1,0 +1,239 @@
+"""Quantizers and dequantizers (oracle; test infrastructure).
+
+Each scheme takes a bf16 tensor x[rows, cols] (activations: rows = tokens M;
+weights: rows = output channels N; cols = K, the contraction axis) and returns
+codes plus scales in the canonical layouts:
+
+=============  ============================  ===============================
+scheme         codes                         scales (zeros)
+=============  ============================  ===============================
+fp8_tensor     u8 e4m3fn [rows, cols]        f32 [1]
+fp8_row        u8 e4m3fn [rows, cols]        f32 [rows]
+fp8_block128   u8 e4m3fn [rows, cols]        act f32 [rows, cols/128];
+                                             wt  f32 [rows/128, cols/128]
+mxfp8          u8 e4m3fn [rows, cols]        u8 e8m0 [rows, cols/32]
+mxfp4          u8 two e2m1 [rows, cols/2]    u8 e8m0 [rows, cols/32]
+w4a16_asym     u32 eight int4 [rows, cols/8] bf16 [rows, cols/128]
+                                             (u8 zero-points [rows, cols/128])
+w4a16_sym      as w4a16_asym, zero-point fixed at 8
+=============  ============================  ===============================
+
+Sources: FP8 scale granularities (tensor, token, 128x128 block, all dynamic
+and symmetric) from "[vLLM] Other quantization: FP8, ModelOpt, INC, TorchAO,
+Quark", section "FP8".  MX scales (one e8m0 exponent per 32 K-elements) and
+fp4 packing from "vLLM-Omni Online Quantization complete guide", section "How
+online quantization works underneath", steps 2-3.  int4 group-128 from
+"vLLM-Omni accelerates inference with AutoRound quantization", section
+"Usage" (the auto-round command and the checkpoint's quantization_config).
+
+Readings where the pages are silent (all listed in the design notes):
+* FP8 scale s = fp32(amax / 448); the fp32 quotient fp32(x / s) is formed
+  first, then rounded to e4m3fn (round-to-nearest-even, saturating).
+  If s comes out 0 (amax = 0, or amax so small that amax/448 underflows),
+  s = 1.
+* MX shared exponent X = clamp(floor(log2 amax) - emax, -127, 127), emax = 8
+  for e4m3 and 2 for e2m1; the element is rounded from x * 2^-X; amax = 0
+  gives X = -127 (code 0).
+* int4 round-to-nearest: range [min(0, min x), max(0, max x)],
+  s = bf16(fp32(fp32(xmax - xmin) / 15)), z = clamp(rne(fp32(-xmin / s)), 0, 15),
+  q = clamp(rne(fp32(x / s)) + z, 0, 15).  Symmetric: z = 8,
+  s = bf16(fp32(amax / 7)).  A zero s (all-zero group, or underflow) gives
+  s = 1, z = 0 (asym) / 8 (sym).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import (
+    E2M1_MAX, E4M3_MAX, bf16_to_f32, e2m1_decode, e2m1_encode, e4m3_decode,
+    e4m3_encode, e8m0_decode, f32_to_bf16_rne, pack_fp4, pack_int4,
+    unpack_fp4, unpack_int4,
+)
+
+SCHEMES = ("fp8_tensor", "fp8_row", "fp8_block128", "mxfp8", "mxfp4",
+           "w4a16_asym", "w4a16_sym")
+ROLES = ("activation", "weight")
+
+_F32 = np.float32
+
+
+def _check(x_bits, scheme, role):
+    if scheme not in SCHEMES:
+        raise ValueError(f"unknown scheme {scheme!r}")
+    if role not in ROLES:
+        raise ValueError(f"unknown role {role!r}")
+    x_bits = np.asarray(x_bits)
+    if x_bits.dtype != np.uint16 or x_bits.ndim != 2:
+        raise ValueError("x must be a 2-D array of bf16 bit patterns (uint16)")
+    rows, cols = x_bits.shape
+    if scheme.startswith("w4a16") and role != "weight":
+        raise ValueError("W4A16 quantizes weights only")
+    if scheme in ("mxfp8", "mxfp4") and cols % 32:
+        raise ValueError("MX schemes need K % 32 == 0")
+    if (scheme == "fp8_block128" or scheme.startswith("w4a16")) and cols % 128:
+        raise ValueError("block-128 / group-128 schemes need K % 128 == 0")
+    if scheme == "fp8_block128" and role == "weight" and rows % 128:
+        raise ValueError("128x128 weight blocks need rows % 128 == 0")
+    return x_bits, rows, cols
+
+
+# ---------------------------------------------------------------- FP8, fp32 scale
+def _fp8_scale(amax_f32: np.ndarray) -> np.ndarray:
+    """s = fp32(amax / 448), or 1 where that is 0."""
+    s = (amax_f32.astype(_F32) / _F32(E4M3_MAX)).astype(_F32)
+    return np.where(s == 0, _F32(1.0), s).astype(_F32)
+
+
+def _fp8_codes(x_f32: np.ndarray, s_f32: np.ndarray) -> np.ndarray:
+    """e4m3fn(RNE_sat(fp32(x / s))) elementwise; s broadcasts against x."""
+    q = (x_f32 / s_f32).astype(_F32)        # IEEE binary32 division, RNE
+    return e4m3_encode(q.astype(np.float64))
+
+
+def _quant_fp8_tensor(x):
+    amax = np.max(np.abs(x)) if x.size else _F32(0)
+    s = _fp8_scale(np.asarray([amax], dtype=_F32))
+    return _fp8_codes(x, s[0]), s
+
+
+def _quant_fp8_row(x):
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], _F32)
+    s = _fp8_scale(amax)
+    return _fp8_codes(x, s[:, None]), s
+
+
+def _quant_fp8_block(x, role):
+    rows, cols = x.shape
+    g = cols // 128
+    if role == "activation":
+        xb = x.reshape(rows, g, 128)
+        amax = np.max(np.abs(xb), axis=2) if rows else np.zeros((0, g), _F32)
+        s = _fp8_scale(amax)                                  # [rows, g]
+        codes = _fp8_codes(xb, s[:, :, None]).reshape(rows, cols)
+    else:
+        rb = rows // 128
+        xb = x.reshape(rb, 128, g, 128)
+        amax = np.max(np.abs(xb), axis=(1, 3)) if rb else np.zeros((0, g), _F32)
+        s = _fp8_scale(amax)                                  # [rows/128, g]
+        codes = _fp8_codes(xb, s[:, None, :, None]).reshape(rows, cols)
+    return codes, s
+
+
+# ---------------------------------------------------------------- MX, e8m0 scale
+def mx_exponent(amax_f32, emax: int) -> np.ndarray:
+    """Shared exponent X = clamp(floor(log2 amax) - emax, -127, 127); amax=0 -> -127."""
+    a = np.asarray(amax_f32, dtype=np.float64)
+    _, e = np.frexp(a)                  # a = m * 2^e with m in [0.5, 1): floor(log2 a) = e - 1
+    X = np.where(a > 0, (e - 1) - emax, -127)
+    return np.clip(X, -127, 127).astype(np.int64)
+
+
+def _quant_mx(x, fmt):
+    rows, cols = x.shape
+    xb = x.reshape(rows, cols // 32, 32).astype(np.float64)
+    amax = np.max(np.abs(xb), axis=2) if rows else np.zeros((0, cols // 32))
+    emax = 8 if fmt == "mxfp8" else 2
+    X = mx_exponent(amax, emax)                                # [rows, cols/32]
+    v = xb * np.ldexp(1.0, -X)[:, :, None]                     # exact scaling
+    if fmt == "mxfp8":
+        codes = e4m3_encode(v).reshape(rows, cols)
+    else:
+        codes = pack_fp4(e2m1_encode(v).reshape(rows, cols))
+    return codes, (X + 127).astype(np.uint8)
+
+
+# ---------------------------------------------------------------- int4 RTN
+def _rne_int(v_f32):
+    return np.rint(v_f32.astype(np.float64))                   # half to even
+
+
+def _quant_int4(x, sym: bool):
+    rows, cols = x.shape
+    xg = x.reshape(rows, cols // 128, 128)
+    if sym:
+        amax = np.max(np.abs(xg), axis=2) if rows else np.zeros((0, cols // 128), _F32)
+        s32 = (amax.astype(_F32) / _F32(7.0)).astype(_F32)
+        s_bits = f32_to_bf16_rne(s32)
+        s = bf16_to_f32(s_bits)
+        zero_s = s == 0
+        s = np.where(zero_s, _F32(1.0), s).astype(_F32)
+        s_bits = np.where(zero_s, f32_to_bf16_rne(np.ones_like(s)), s_bits)
+        z = np.full(s.shape, 8.0)
+    else:
+        xmin = np.minimum(np.min(xg, axis=2), _F32(0)) if rows else np.zeros((0, cols // 128), _F32)
+        xmax = np.maximum(np.max(xg, axis=2), _F32(0)) if rows else np.zeros((0, cols // 128), _F32)
+        d = (xmax.astype(_F32) - xmin.astype(_F32)).astype(_F32)
+        s32 = (d / _F32(15.0)).astype(_F32)
+        s_bits = f32_to_bf16_rne(s32)
+        s = bf16_to_f32(s_bits)
+        zero_s = s == 0
+        s = np.where(zero_s, _F32(1.0), s).astype(_F32)
+        s_bits = np.where(zero_s, f32_to_bf16_rne(np.ones_like(s)), s_bits)
+        z = np.clip(_rne_int((-xmin.astype(_F32) / s).astype(_F32)), 0, 15)
+        z = np.where(zero_s, 0.0, z)
+    q = _rne_int((xg / s[:, :, None]).astype(_F32)) + z[:, :, None]
+    q = np.clip(q, 0, 15).astype(np.uint8).reshape(rows, cols)
+    return pack_int4(q), s_bits.astype(np.uint16), z.astype(np.uint8)
+
+
+# ---------------------------------------------------------------- public API
+def quantize(x_bits, scheme: str, role: str = "activation") -> dict:
+    """Quantize a bf16 tensor; returns {"codes", "scales", "zeros"} (canonical layouts)."""
+    x_bits, rows, cols = _check(x_bits, scheme, role)
+    x = bf16_to_f32(x_bits)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input is outside the quantizer's domain")
+    zeros = None
+    if scheme == "fp8_tensor":
+        codes, scales = _quant_fp8_tensor(x)
+    elif scheme == "fp8_row":
+        codes, scales = _quant_fp8_row(x)
+    elif scheme == "fp8_block128":
+        codes, scales = _quant_fp8_block(x, role)
+    elif scheme in ("mxfp8", "mxfp4"):
+        codes, scales = _quant_mx(x, scheme)
+    else:
+        codes, scales, zeros = _quant_int4(x, scheme == "w4a16_sym")
+    return {"scheme": scheme, "role": role, "rows": rows, "cols": cols,
+            "codes": codes, "scales": scales, "zeros": zeros}
+
+
+def _expand_scale_f32(q) -> np.ndarray:
+    """Per-element fp32 scale [rows, cols] for the fp32-scaled FP8 schemes."""
+    rows, cols, s = q["rows"], q["cols"], np.asarray(q["scales"], dtype=_F32)
+    if q["scheme"] == "fp8_tensor":
+        return np.full((rows, cols), s.reshape(-1)[0], dtype=_F32)
+    if q["scheme"] == "fp8_row":
+        return np.repeat(s.reshape(rows, 1), cols, axis=1)
+    if q["role"] == "activation":
+        return np.repeat(s.reshape(rows, cols // 128), 128, axis=1)
+    return np.repeat(np.repeat(s.reshape(rows // 128, cols // 128), 128, axis=0), 128, axis=1)
+
+
+def _decoded(q):
+    """(element values, per-element scale) in float64, both exact."""
+    scheme, rows, cols = q["scheme"], q["rows"], q["cols"]
+    if scheme in ("fp8_tensor", "fp8_row", "fp8_block128"):
+        return e4m3_decode(q["codes"]), _expand_scale_f32(q).astype(np.float64)
+    if scheme in ("mxfp8", "mxfp4"):
+        vals = e4m3_decode(q["codes"]) if scheme == "mxfp8" else e2m1_decode(unpack_fp4(q["codes"]))
+        sc = np.repeat(e8m0_decode(q["scales"]).reshape(rows, cols // 32), 32, axis=1)
+        return vals, sc
+    codes = unpack_int4(q["codes"]).astype(np.float64)
+    z = np.repeat(np.asarray(q["zeros"], dtype=np.float64).reshape(rows, cols // 128), 128, axis=1)
+    s = np.repeat(bf16_to_f32(q["scales"]).astype(np.float64).reshape(rows, cols // 128), 128, axis=1)
+    return codes - z, s
+
+
+def dequant_exact(q) -> np.ndarray:
+    """Exact dequantized values decode(q) * scale in float64 (the GEMM operand)."""
+    vals, sc = _decoded(q)
+    return vals * sc
+
+
+def dequantize(q) -> np.ndarray:
+    """bf16 bits of bf16_RNE(fp32(decode(q) * scale)) (int4: (q - z) * s)."""
+    vals, sc = _decoded(q)
+    prod = (vals.astype(_F32) * sc.astype(_F32)).astype(_F32)   # one fp32 rounding
+    with np.errstate(over="ignore"):
+        return f32_to_bf16_rne(prod)
