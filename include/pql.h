@@ -1,0 +1,174 @@
+/*
+ * pql.h -- C ABI of libpql, the quantized-linear hot path for AMD MI355X (gfx950).
+ *
+ * Two steps, as the pages describe the online-quantized linear layer:
+ *   1. quantize bf16 activations (every call) and weights (once, at load) into
+ *      block-scaled low-precision codes plus scales;
+ *   2. a scaled GEMM on those codes, C = A * W^T, returning bf16.
+ * ("vLLM-Omni Online Quantization complete guide", section "How online
+ *  quantization works underneath", steps 1-3; "[vLLM] Other quantization: FP8,
+ *  ModelOpt, INC, TorchAO, Quark", section "FP8"; "vLLM-Omni accelerates
+ *  inference with AutoRound quantization", section "Usage".)
+ *
+ * Conventions for every call:
+ *   - Operands: A is [M, K] (tokens x input channels), W is [N, K] (output x
+ *     input channels, a linear layer's own layout), C is [M, N].  K is the
+ *     contraction axis and is contiguous in every operand.
+ *   - All pointers except the size outputs are DEVICE pointers on the current
+ *     HIP device.  The caller allocates and owns every buffer, including
+ *     workspace; the library allocates no device memory and keeps no state
+ *     besides a per-device property cache and a thread-local error message.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and the call returns without synchronizing.  Calls are re-entrant.
+ *   - Every argument check runs before anything is enqueued; on any error
+ *     nothing is enqueued and pql_last_error() describes the problem.
+ *   - Element sizes: bf16 = 2 bytes, fp32 = 4 bytes.  Leading dimensions
+ *     (ldx, ldy, lda, ldc) are in elements.  Device pointers must be 16-byte
+ *     aligned and leading dimensions multiples of 8 elements.
+ *
+ * Canonical layouts (per scheme; rows = M for activations, N for weights,
+ * cols = K):
+ *   FP8_TENSOR    codes u8 e4m3fn [rows, cols]          scales f32 [1]
+ *   FP8_ROW       codes u8 e4m3fn [rows, cols]          scales f32 [rows]
+ *   FP8_BLOCK128  codes u8 e4m3fn [rows, cols]          scales f32 [rows, cols/128] (activation)
+ *                                                       scales f32 [rows/128, cols/128] (weight)
+ *   MXFP8         codes u8 e4m3fn [rows, cols]          scales u8 e8m0 [rows, cols/32]
+ *   MXFP4         codes u8 [rows, cols/2], two e2m1,    scales u8 e8m0 [rows, cols/32]
+ *                 element 2j in the low nibble
+ *   W4A16_ASYM    codes u32 [rows, cols/8], element k   scales bf16 [rows, cols/128]
+ *                 at bits 4*(k mod 8)                   zeros u8 [rows, cols/128] (0..15)
+ *   W4A16_SYM     as W4A16_ASYM with every zero-point 8
+ * All of these are K-contiguous, which is the operand order the matrix cores
+ * consume, so weights need no re-layout after quantization.
+ */
+#ifndef PQL_H
+#define PQL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PQL_VERSION 1
+
+typedef enum pql_status {
+  PQL_OK = 0,
+  PQL_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, stride or alignment */
+  PQL_ERR_UNSUPPORTED = 2,      /* scheme x role not defined, or device is not gfx950 */
+  PQL_ERR_WORKSPACE = 3,        /* workspace missing or smaller than pql_workspace_size() */
+  PQL_ERR_HIP = 4               /* HIP runtime error (no device, launch failure) */
+} pql_status;
+
+/* Quantization schemes.
+ *   FP8_TENSOR / FP8_ROW / FP8_BLOCK128: dynamic symmetric FP8 e4m3fn with an
+ *     fp32 scale per tensor, per row (per token for activations, per output
+ *     channel for weights) or per block (1x128 for activations, 128x128 for
+ *     weights) ("[vLLM] Other quantization...", section "FP8").
+ *     s = fp32(amax / 448) (1 if that is 0); code = e4m3fn(fp32(x / s)),
+ *     round to nearest even, saturating at +-448, sign of zero kept.
+ *   MXFP8 / MXFP4: OCP MX, one e8m0 exponent per 32 consecutive K-elements
+ *     ("vLLM-Omni Online Quantization complete guide", section "How online
+ *     quantization works underneath", steps 2-3).
+ *     X = clamp(floor(log2 amax) - emax, -127, 127) (emax 8 for e4m3, 2 for
+ *     e2m1; amax = 0 gives -127), scale code X + 127, code = RNE_sat(x * 2^-X).
+ *   W4A16_ASYM / W4A16_SYM: int4 weights, group 128 along K, bf16 scale and
+ *     4-bit zero-point per group; activations stay bf16 ("vLLM-Omni
+ *     accelerates inference with AutoRound quantization", section "Usage").
+ *     Weight quantization is round-to-nearest:
+ *       asym: s = bf16(fp32(fp32(max(0,max x) - min(0,min x)) / 15)),
+ *             z = clamp(rne(fp32(-min(0,min x) / s)), 0, 15)
+ *       sym:  s = bf16(fp32(max|x| / 7)), z = 8
+ *       q = clamp(rne(fp32(x / s)) + z, 0, 15); s = 0 is replaced by 1 (z = 0 asym).
+ */
+typedef enum pql_scheme {
+  PQL_FP8_TENSOR = 0,
+  PQL_FP8_ROW = 1,
+  PQL_FP8_BLOCK128 = 2,
+  PQL_MXFP8 = 3,
+  PQL_MXFP4 = 4,
+  PQL_W4A16_ASYM = 5,
+  PQL_W4A16_SYM = 6
+} pql_scheme;
+
+typedef enum pql_role { PQL_ACTIVATION = 0, PQL_WEIGHT = 1 } pql_role;
+
+typedef enum pql_op {
+  PQL_OP_QUANTIZE = 0,
+  PQL_OP_DEQUANTIZE = 1,
+  PQL_OP_QGEMM = 2,
+  PQL_OP_QLINEAR = 3
+} pql_op;
+
+/* Library version (PQL_VERSION). */
+int pql_version(void);
+
+/* Text of the last error on the calling thread ("" if none).  The pointer
+ * stays valid until the thread's next pql call. */
+const char* pql_last_error(void);
+
+/* Byte sizes of the codes, scales and zero-point buffers of a quantized
+ * [rows, cols] tensor in the canonical layout (zeros_bytes is 0 except for
+ * W4A16).  Size outputs are host pointers; any may be NULL.
+ * Errors: INVALID_ARGUMENT for negative sizes or cols / rows that the scheme
+ * cannot block (cols % 32 for FP8 tensor/row and MX, cols % 128 for
+ * FP8_BLOCK128 and W4A16, rows % 128 for FP8_BLOCK128 weights);
+ * UNSUPPORTED for W4A16 activations or an unknown scheme / role. */
+pql_status pql_quantized_sizes(int scheme, int role, int64_t rows, int64_t cols,
+                               size_t* codes_bytes, size_t* scales_bytes,
+                               size_t* zeros_bytes);
+
+/* Workspace bytes a call needs (host output).  op = PQL_OP_QUANTIZE: the
+ * per-tensor scheme needs a small partial-maximum buffer, the others 0.
+ * op = PQL_OP_QLINEAR: room for the activation's codes and scales (0 for
+ * W4A16).  Other ops need none.  `role` matters for QUANTIZE only. */
+pql_status pql_workspace_size(int op, int scheme, int role, int64_t M, int64_t N,
+                              int64_t K, size_t* bytes);
+
+/* Quantize a bf16 tensor x[rows, cols] (row stride ldx elements) into the
+ * canonical layout.  Activation role: rows = M; weight role: rows = N.
+ * `zeros` is written for W4A16 only (may be NULL otherwise).  The scales are
+ * dynamic (computed from x).  FP8_TENSOR needs `workspace` of at least
+ * pql_workspace_size(PQL_OP_QUANTIZE, ...) bytes; other schemes ignore it.
+ * rows = 0 is a no-op. */
+pql_status pql_quantize(int scheme, int role, const void* x, int64_t rows, int64_t cols,
+                        int64_t ldx, void* codes, void* scales, void* zeros,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* y[rows, cols] (bf16, row stride ldy) = bf16_RNE(fp32(decode(code) * scale))
+ * (W4A16: bf16_RNE((q - z) * s)).  Inputs in the canonical layout. */
+pql_status pql_dequantize(int scheme, int role, const void* codes, const void* scales,
+                          const void* zeros, int64_t rows, int64_t cols, void* y,
+                          int64_t ldy, void* stream);
+
+/* C[M, N] (bf16, row stride ldc) = A_hat * W_hat^T on already-quantized
+ * operands, fp32 accumulation, bf16 round-to-nearest-even output.
+ *   FP8 / MX schemes: a = activation codes [M, K], a_scales its scales
+ *   (canonical activation layout); w_codes / w_scales the weight's.
+ *   W4A16: a = bf16 activation [M, K] (contiguous), a_scales unused (NULL),
+ *   w_zeros required.
+ * K must be a multiple of 128; M, N >= 1 may be ragged (tails are masked);
+ * FP8_BLOCK128 needs N % 128 == 0 (the weight's 128-row blocks). */
+pql_status pql_qgemm(int scheme, const void* a, const void* a_scales, const void* w_codes,
+                     const void* w_scales, const void* w_zeros, int64_t M, int64_t N,
+                     int64_t K, void* c, int64_t ldc, void* stream);
+
+/* The linear layer's forward: quantize the bf16 activation a[M, K] (row
+ * stride lda) with the scheme's activation rule into `workspace`, then
+ * qgemm against the quantized weight.  W4A16 uses a as-is (lda must equal K)
+ * and needs no workspace.  C as for pql_qgemm. */
+pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda,
+                       const void* w_codes, const void* w_scales, const void* w_zeros,
+                       int64_t N, void* c, int64_t ldc, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Name of the kernel that `op` would launch for these sizes (for "no silent
+ * fallback" checks); "" if the combination is invalid.  Static string. */
+const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, int64_t K);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQL_H */

@@ -1,0 +1,283 @@
+"""Quantized-linear hot path for AMD MI355X (gfx950): Python binding of libpql.
+
+Argument marshalling only: every step of quantize / dequantize / qgemm /
+qlinear runs in the HIP kernels of ``libpql.so`` (declared in
+``include/pql.h``).  torch supplies device memory and the current stream.
+There is no CPU fallback: if the library is missing, every call raises.
+
+    import precision_quantized_linear_amd as pql
+    wq = pql.quantize(w, "mxfp8", "weight")      # once, at load
+    y = pql.qlinear(x, wq)                        # every call: quantize x, GEMM
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpql.so")
+
+SCHEMES = {"fp8_tensor": 0, "fp8_row": 1, "fp8_block128": 2, "mxfp8": 3, "mxfp4": 4,
+           "w4a16_asym": 5, "w4a16_sym": 6}
+ROLES = {"activation": 0, "weight": 1}
+OPS = {"quantize": 0, "dequantize": 1, "qgemm": 2, "qlinear": 3}
+
+PQL_OK, PQL_ERR_INVALID_ARGUMENT, PQL_ERR_UNSUPPORTED, PQL_ERR_WORKSPACE, PQL_ERR_HIP = range(5)
+
+_lib = None
+
+
+class PqlError(RuntimeError):
+    """A HIP runtime failure reported by libpql."""
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpql.so (built in-tree by ``precision_quantized_linear_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; run `python -m precision_quantized_linear_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, sz, vp, ci = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
+        L.pql_version.restype = ci
+        L.pql_last_error.restype = ctypes.c_char_p
+        L.pql_kernel_name.restype = ctypes.c_char_p
+        L.pql_kernel_name.argtypes = [ci, ci, ci, i64, i64, i64]
+        L.pql_quantized_sizes.argtypes = [ci, ci, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.pql_workspace_size.argtypes = [ci, ci, ci, i64, i64, i64, ctypes.POINTER(sz)]
+        L.pql_quantize.argtypes = [ci, ci, vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+        L.pql_dequantize.argtypes = [ci, ci, vp, vp, vp, i64, i64, vp, i64, vp]
+        L.pql_qgemm.argtypes = [ci, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp]
+        L.pql_qlinear.argtypes = [ci, vp, i64, i64, i64, vp, vp, vp, i64, vp, i64, vp, sz, vp]
+        for f in ("pql_quantized_sizes", "pql_workspace_size", "pql_quantize", "pql_dequantize",
+                  "pql_qgemm", "pql_qlinear"):
+            getattr(L, f).restype = ci
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status == PQL_OK:
+        return
+    msg = f"{what}: {lib().pql_last_error().decode()}"
+    if status in (PQL_ERR_INVALID_ARGUMENT, PQL_ERR_WORKSPACE):
+        raise ValueError(msg)
+    if status == PQL_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise PqlError(msg)
+
+
+def _scheme(s) -> int:
+    if isinstance(s, int):
+        return s
+    if s not in SCHEMES:
+        raise ValueError(f"unknown scheme {s!r}; supported: {sorted(SCHEMES)}")
+    return SCHEMES[s]
+
+
+def _role(r) -> int:
+    if isinstance(r, int):
+        return r
+    if r not in ROLES:
+        raise ValueError(f"unknown role {r!r}")
+    return ROLES[r]
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclass
+class QTensor:
+    """A quantized [rows, cols] tensor in the canonical layout of include/pql.h."""
+    scheme: str
+    role: str
+    rows: int
+    cols: int
+    codes: torch.Tensor
+    scales: torch.Tensor
+    zeros: torch.Tensor | None = None
+
+    @property
+    def device(self):
+        return self.codes.device
+
+
+def quantized_sizes(scheme, role, rows: int, cols: int):
+    c, s, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().pql_quantized_sizes(_scheme(scheme), _role(role), rows, cols,
+                                     ctypes.byref(c), ctypes.byref(s), ctypes.byref(z)), "quantized_sizes")
+    return c.value, s.value, z.value
+
+
+def workspace_size(op, scheme, role="activation", M=0, N=0, K=0) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().pql_workspace_size(OPS[op] if isinstance(op, str) else op, _scheme(scheme), _role(role),
+                                    M, N, K, ctypes.byref(b)), "workspace_size")
+    return b.value
+
+
+def kernel_name(op, scheme, role="activation", M=0, N=0, K=0) -> str:
+    return lib().pql_kernel_name(OPS[op] if isinstance(op, str) else op, _scheme(scheme), _role(role),
+                                 M, N, K).decode()
+
+
+def _alloc_q(scheme: str, role: str, rows: int, cols: int, device) -> QTensor:
+    cb, sb, zb = quantized_sizes(scheme, role, rows, cols)
+    if scheme.startswith("w4a16"):
+        codes = torch.empty((rows, cols // 8), dtype=torch.int32, device=device)
+        scales = torch.empty((rows, cols // 128), dtype=torch.bfloat16, device=device)
+        zeros = torch.empty((rows, cols // 128), dtype=torch.uint8, device=device)
+    else:
+        codes = torch.empty((rows, cols if scheme != "mxfp4" else cols // 2), dtype=torch.uint8, device=device)
+        if scheme in ("mxfp8", "mxfp4"):
+            scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
+        elif scheme == "fp8_tensor":
+            scales = torch.empty((1,), dtype=torch.float32, device=device)
+        elif scheme == "fp8_row":
+            scales = torch.empty((rows,), dtype=torch.float32, device=device)
+        elif role == "activation":
+            scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=device)
+        else:
+            scales = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=device)
+        zeros = None
+    assert codes.numel() * codes.element_size() == cb and scales.numel() * scales.element_size() == sb
+    return QTensor(scheme, role, rows, cols, codes, scales, zeros)
+
+
+def _as_2d_bf16(x: torch.Tensor) -> torch.Tensor:
+    if x.dtype != torch.bfloat16:
+        raise ValueError("expected a bfloat16 tensor")
+    if not x.is_cuda:
+        raise ValueError("expected a tensor on a HIP device")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit stride along K")
+    return x
+
+
+def quantize(x: torch.Tensor, scheme: str, role: str = "activation", workspace: torch.Tensor | None = None,
+             out: QTensor | None = None) -> QTensor:
+    """Quantize a bf16 [rows, K] tensor (activation: rows = tokens; weight: rows = out channels).
+    ``out`` reuses the buffers of an earlier result of the same scheme, role and shape."""
+    x = _as_2d_bf16(x)
+    rows, cols = x.shape
+    if out is not None:
+        if (out.scheme, out.role, out.rows, out.cols) != (scheme, role, rows, cols):
+            raise ValueError("out does not match the scheme, role and shape")
+        q = out
+    else:
+        q = _alloc_q(scheme, role, rows, cols, x.device)
+    wsb = workspace_size("quantize", scheme, role)
+    if wsb and workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    _check(lib().pql_quantize(_scheme(scheme), _role(role), x.data_ptr(), rows, cols, x.stride(0),
+                              q.codes.data_ptr(), q.scales.data_ptr(), _ptr(q.zeros), _ptr(workspace),
+                              0 if workspace is None else workspace.numel() * workspace.element_size(),
+                              _stream(x.device)), "quantize")
+    return q
+
+
+def dequantize(q: QTensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """bf16 [rows, cols] = bf16(decode(code) * scale)."""
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=torch.bfloat16, device=q.device)
+    _check(lib().pql_dequantize(_scheme(q.scheme), _role(q.role), q.codes.data_ptr(), q.scales.data_ptr(),
+                                _ptr(q.zeros), q.rows, q.cols, out.data_ptr(), out.stride(0),
+                                _stream(q.device)), "dequantize")
+    return out
+
+
+def qgemm(a, w: QTensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] = A_hat * W_hat^T on quantized operands (W4A16: ``a`` is the bf16 activation)."""
+    if w.role != "weight":
+        raise ValueError("the second operand must be a quantized weight")
+    if isinstance(a, QTensor):
+        if a.scheme != w.scheme:
+            raise ValueError("activation and weight schemes differ")
+        M, K = a.rows, a.cols
+        a_ptr, as_ptr = a.codes.data_ptr(), a.scales.data_ptr()
+    else:
+        a = _as_2d_bf16(a)
+        if a.stride(0) != a.shape[1]:
+            a = a.contiguous()
+        M, K = a.shape
+        a_ptr, as_ptr = a.data_ptr(), None
+    if K != w.cols:
+        raise ValueError(f"K mismatch: {K} vs {w.cols}")
+    if out is None:
+        out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=w.device)
+    _check(lib().pql_qgemm(_scheme(w.scheme), a_ptr, as_ptr, w.codes.data_ptr(), w.scales.data_ptr(),
+                           _ptr(w.zeros), M, w.rows, K, out.data_ptr(), out.stride(0),
+                           _stream(w.device)), "qgemm")
+    return out
+
+
+def qlinear(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None,
+            workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The quantized linear layer's forward: flatten x[..., K] to 2-D, quantize it with the
+    weight's scheme (activation rule), GEMM against ``w``, restore the leading shape."""
+    if w.role != "weight":
+        raise ValueError("w must be a quantized weight")
+    lead = x.shape[:-1]
+    x2 = x.reshape(-1, x.shape[-1])
+    if x2.stride(-1) != 1 or (w.scheme.startswith("w4a16") and x2.stride(0) != x2.shape[1]):
+        x2 = x2.contiguous()
+    x2 = _as_2d_bf16(x2)
+    M, K = x2.shape
+    if K != w.cols:
+        raise ValueError(f"K mismatch: {K} vs {w.cols}")
+    if out is None:
+        out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    wsb = workspace_size("qlinear", w.scheme, "activation", M, w.rows, K)
+    if wsb and workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    _check(lib().pql_qlinear(_scheme(w.scheme), x2.data_ptr(), M, K, x2.stride(0), w.codes.data_ptr(),
+                             w.scales.data_ptr(), _ptr(w.zeros), w.rows, out.data_ptr(), out.stride(0),
+                             _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                             _stream(x.device)), "qlinear")
+    return out.reshape(*lead, w.rows)
+
+
+def from_numpy(q: dict, device) -> QTensor:
+    """Upload a quantized tensor given as NumPy arrays in the canonical layout."""
+    scheme = q["scheme"]
+
+    def up(a, dtype):
+        import numpy as np
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype is not None:
+            t = t.view(dtype)
+        return t.to(device)
+
+    if scheme.startswith("w4a16"):
+        codes = up(q["codes"].view("int32"), None)
+        scales = up(q["scales"].view("int16"), torch.bfloat16)
+        zeros = up(q["zeros"], None)
+    else:
+        codes = up(q["codes"], None)
+        sc = q["scales"]
+        scales = up(sc, None)
+        zeros = None
+    return QTensor(scheme, q["role"], q["rows"], q["cols"], codes, scales, zeros)
+
+
+def to_numpy(q: QTensor) -> dict:
+    """Download a quantized tensor into NumPy arrays in the canonical layout."""
+    import numpy as np
+    codes = q.codes.cpu().numpy()
+    if q.scheme.startswith("w4a16"):
+        codes = codes.view(np.uint32)
+        scales = q.scales.view(torch.int16).cpu().numpy().view(np.uint16)
+        zeros = q.zeros.cpu().numpy()
+    else:
+        scales = q.scales.cpu().numpy()
+        zeros = None
+    return {"scheme": q.scheme, "role": q.role, "rows": q.rows, "cols": q.cols,
+            "codes": codes, "scales": scales, "zeros": zeros}

@@ -1,0 +1,365 @@
+// C ABI of libpql (declared in include/pql.h): argument validation, size
+// queries, device checks and dispatch to the kernel launchers.
+//
+// Every check runs before anything is enqueued; errors raise instead of
+// silently reinterpreting data, in the spirit of the pages' own loaders (an
+// unknown method or an unsupported platform is an error, never a fallback:
+// "vLLM-Omni Online Quantization complete guide", sections "Hardware support
+// matrix" and "Configuration").
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/pql.h"
+#include "pql_internal.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+pql_status fail(pql_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+pql_status ok() {
+  g_error.clear();
+  return PQL_OK;
+}
+
+const char* scheme_name(int s) {
+  switch (s) {
+    case PQL_FP8_TENSOR: return "FP8_TENSOR";
+    case PQL_FP8_ROW: return "FP8_ROW";
+    case PQL_FP8_BLOCK128: return "FP8_BLOCK128";
+    case PQL_MXFP8: return "MXFP8";
+    case PQL_MXFP4: return "MXFP4";
+    case PQL_W4A16_ASYM: return "W4A16_ASYM";
+    case PQL_W4A16_SYM: return "W4A16_SYM";
+  }
+  return "?";
+}
+
+bool is_w4a16(int s) { return s == PQL_W4A16_ASYM || s == PQL_W4A16_SYM; }
+bool is_mx(int s) { return s == PQL_MXFP8 || s == PQL_MXFP4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+int64_t k_granule(int scheme) { return (scheme == PQL_FP8_BLOCK128 || is_w4a16(scheme)) ? 128 : 32; }
+
+pql_status check_scheme_role(int scheme, int role) {
+  if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM)
+    return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
+  if (role != PQL_ACTIVATION && role != PQL_WEIGHT) return fail(PQL_ERR_UNSUPPORTED, "unknown role %d", role);
+  if (is_w4a16(scheme) && role == PQL_ACTIVATION)
+    return fail(PQL_ERR_UNSUPPORTED, "%s quantizes weights only; activations stay bf16", scheme_name(scheme));
+  return PQL_OK;
+}
+
+// Shape rules shared by quantize / dequantize / sizes.
+pql_status check_shape(int scheme, int role, int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0) return fail(PQL_ERR_INVALID_ARGUMENT, "rows must be >= 0 and cols > 0 (got %lld, %lld)",
+                                         (long long)rows, (long long)cols);
+  const int64_t gk = k_granule(scheme);
+  if (cols % gk) return fail(PQL_ERR_INVALID_ARGUMENT, "%s needs cols %% %lld == 0 (got %lld)", scheme_name(scheme),
+                             (long long)gk, (long long)cols);
+  if (scheme == PQL_FP8_BLOCK128 && role == PQL_WEIGHT && rows % 128)
+    return fail(PQL_ERR_INVALID_ARGUMENT, "FP8_BLOCK128 weights need rows %% 128 == 0 (got %lld)", (long long)rows);
+  if (cols > (int64_t(1) << 20)) return fail(PQL_ERR_INVALID_ARGUMENT, "cols above 2^20 is not supported");
+  if (rows > (int64_t(1) << 31) - 1) return fail(PQL_ERR_INVALID_ARGUMENT, "rows above 2^31-1 is not supported");
+  return PQL_OK;
+}
+
+struct Sizes { size_t codes, scales, zeros; };
+
+Sizes sizes_of(int scheme, int role, int64_t rows, int64_t cols) {
+  Sizes s{0, 0, 0};
+  const size_t R = (size_t)rows, C = (size_t)cols;
+  switch (scheme) {
+    case PQL_FP8_TENSOR: s.codes = R * C; s.scales = 4; break;
+    case PQL_FP8_ROW: s.codes = R * C; s.scales = 4 * R; break;
+    case PQL_FP8_BLOCK128:
+      s.codes = R * C;
+      s.scales = role == PQL_ACTIVATION ? 4 * R * (C / 128) : 4 * (R / 128) * (C / 128);
+      break;
+    case PQL_MXFP8: s.codes = R * C; s.scales = R * (C / 32); break;
+    case PQL_MXFP4: s.codes = R * C / 2; s.scales = R * (C / 32); break;
+    default: s.codes = R * C / 2; s.scales = 2 * R * (C / 128); s.zeros = R * (C / 128); break;
+  }
+  return s;
+}
+
+constexpr size_t kTensorWs = 4 * (size_t)pql::kTensorAmaxBlocks;
+
+// gfx950 check, cached per device.
+std::atomic<int> g_dev_state[64];
+
+pql_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PQL_ERR_HIP, "no usable HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(PQL_ERR_HIP, "device index %d out of range", dev);
+  int st = g_dev_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(PQL_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_relaxed);
+    if (st == 2) return fail(PQL_ERR_UNSUPPORTED, "device %d is %s; libpql targets gfx950 only", dev, prop.gcnArchName);
+  }
+  if (st == 2) return fail(PQL_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return PQL_OK;
+}
+
+pql_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PQL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Quantize without re-validating (shared by pql_quantize and pql_qlinear).
+hipError_t do_quantize(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx, void* codes,
+                       void* scales, void* zeros, void* ws, hipStream_t st) {
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint8_t* cb = static_cast<uint8_t*>(codes);
+  switch (scheme) {
+    case PQL_FP8_TENSOR:
+      return pql::launch_quant_fp8_tensor(xb, rows, cols, ldx, cb, static_cast<float*>(scales),
+                                          static_cast<float*>(ws), st);
+    case PQL_FP8_ROW: return pql::launch_quant_fp8_row(xb, rows, cols, ldx, cb, static_cast<float*>(scales), st);
+    case PQL_FP8_BLOCK128:
+      return role == PQL_ACTIVATION
+                 ? pql::launch_quant_fp8_block_act(xb, rows, cols, ldx, cb, static_cast<float*>(scales), st)
+                 : pql::launch_quant_fp8_block_wt(xb, rows, cols, ldx, cb, static_cast<float*>(scales), st);
+    case PQL_MXFP8:
+    case PQL_MXFP4:
+      return pql::launch_quant_mx(scheme == PQL_MXFP4, xb, rows, cols, ldx, cb, static_cast<uint8_t*>(scales), st);
+    default:
+      return pql::launch_quant_int4(scheme == PQL_W4A16_SYM, xb, rows, cols, ldx, static_cast<uint32_t*>(codes),
+                                    static_cast<uint16_t*>(scales), static_cast<uint8_t*>(zeros), st);
+  }
+}
+
+hipError_t do_qgemm(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
+                    const void* w_zeros, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, hipStream_t st) {
+  if (is_w4a16(scheme))
+    return pql::launch_gemm_w4a16(static_cast<const uint16_t*>(a), static_cast<const uint32_t*>(w_codes),
+                                  static_cast<const uint16_t*>(w_scales), static_cast<const uint8_t*>(w_zeros), M, N,
+                                  K, static_cast<uint16_t*>(c), ldc, st);
+  pql::GemmArgs g;
+  g.a = static_cast<const uint8_t*>(a);
+  g.w = static_cast<const uint8_t*>(w_codes);
+  g.a_scales = a_scales;
+  g.w_scales = w_scales;
+  g.a_scale_stride = scheme == PQL_FP8_TENSOR ? 0 : 1;
+  g.w_scale_stride = scheme == PQL_FP8_TENSOR ? 0 : 1;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.c = static_cast<uint16_t*>(c);
+  g.ldc = ldc;
+  pql::GemmKind kind = scheme == PQL_FP8_BLOCK128 ? pql::GEMM_FP8_BLOCK
+                       : scheme == PQL_MXFP8      ? pql::GEMM_MXFP8
+                       : scheme == PQL_MXFP4      ? pql::GEMM_MXFP4
+                                                  : pql::GEMM_FP8_ROWSCALE;
+  return pql::launch_gemm(kind, g, st);
+}
+
+pql_status check_gemm_shape(int scheme, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N <= 0 || K <= 0)
+    return fail(PQL_ERR_INVALID_ARGUMENT, "need M >= 0, N > 0, K > 0 (got %lld, %lld, %lld)", (long long)M,
+                (long long)N, (long long)K);
+  if (K % 128) return fail(PQL_ERR_INVALID_ARGUMENT, "qgemm needs K %% 128 == 0 (got %lld)", (long long)K);
+  if (K > (int64_t(1) << 20)) return fail(PQL_ERR_INVALID_ARGUMENT, "K above 2^20 is not supported");
+  if (M > (int64_t(1) << 30) || N > (int64_t(1) << 30))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "M and N above 2^30 are not supported");
+  if (scheme == PQL_FP8_BLOCK128 && N % 128)
+    return fail(PQL_ERR_INVALID_ARGUMENT, "FP8_BLOCK128 needs N %% 128 == 0 (got %lld)", (long long)N);
+  return PQL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pql_version(void) { return PQL_VERSION; }
+
+const char* pql_last_error(void) { return g_error.c_str(); }
+
+pql_status pql_quantized_sizes(int scheme, int role, int64_t rows, int64_t cols, size_t* codes_bytes,
+                               size_t* scales_bytes, size_t* zeros_bytes) {
+  pql_status st = check_scheme_role(scheme, role);
+  if (st != PQL_OK) return st;
+  if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
+  const Sizes s = sizes_of(scheme, role, rows, cols);
+  if (codes_bytes) *codes_bytes = s.codes;
+  if (scales_bytes) *scales_bytes = s.scales;
+  if (zeros_bytes) *zeros_bytes = s.zeros;
+  return ok();
+}
+
+pql_status pql_workspace_size(int op, int scheme, int role, int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(PQL_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (op < PQL_OP_QUANTIZE || op > PQL_OP_QLINEAR) return fail(PQL_ERR_INVALID_ARGUMENT, "unknown op %d", op);
+  *bytes = 0;
+  if (op == PQL_OP_QUANTIZE) {
+    pql_status st = check_scheme_role(scheme, role);
+    if (st != PQL_OK) return st;
+    if (scheme == PQL_FP8_TENSOR) *bytes = kTensorWs;
+    return ok();
+  }
+  if (op == PQL_OP_QLINEAR) {
+    if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
+    pql_status st = check_gemm_shape(scheme, M, N, K);
+    if (st != PQL_OK) return st;
+    if (is_w4a16(scheme)) return ok();
+    const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
+    *bytes = round256(s.codes) + round256(s.scales) + (scheme == PQL_FP8_TENSOR ? kTensorWs : 0);
+    return ok();
+  }
+  return ok();
+}
+
+pql_status pql_quantize(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx, void* codes,
+                        void* scales, void* zeros, void* workspace, size_t workspace_bytes, void* stream) {
+  pql_status st = check_scheme_role(scheme, role);
+  if (st != PQL_OK) return st;
+  if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
+  if (ldx < cols || ldx % 8) return fail(PQL_ERR_INVALID_ARGUMENT, "ldx must be >= cols and a multiple of 8 (got %lld)",
+                                         (long long)ldx);
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(PQL_ERR_INVALID_ARGUMENT, "x, codes and scales must be non-NULL");
+  if (is_w4a16(scheme) && !zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for W4A16");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "x, codes and scales must be 16-byte aligned");
+  if (scheme == PQL_FP8_TENSOR) {
+    if (!workspace || workspace_bytes < kTensorWs)
+      return fail(PQL_ERR_WORKSPACE, "FP8_TENSOR needs a %zu-byte workspace (got %zu)", kTensorWs,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PQL_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+  if ((st = check_device()) != PQL_OK) return st;
+  return launched(do_quantize(scheme, role, x, rows, cols, ldx, codes, scales, zeros, workspace,
+                              static_cast<hipStream_t>(stream)),
+                  "quantize launch");
+}
+
+pql_status pql_dequantize(int scheme, int role, const void* codes, const void* scales, const void* zeros,
+                          int64_t rows, int64_t cols, void* y, int64_t ldy, void* stream) {
+  pql_status st = check_scheme_role(scheme, role);
+  if (st != PQL_OK) return st;
+  if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
+  if (ldy < cols || ldy % 8) return fail(PQL_ERR_INVALID_ARGUMENT, "ldy must be >= cols and a multiple of 8 (got %lld)",
+                                         (long long)ldy);
+  if (rows == 0) return ok();
+  if (!codes || !scales || !y) return fail(PQL_ERR_INVALID_ARGUMENT, "codes, scales and y must be non-NULL");
+  if (is_w4a16(scheme) && !zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for W4A16");
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(y))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "codes, scales and y must be 16-byte aligned");
+  if ((st = check_device()) != PQL_OK) return st;
+  int kind;
+  switch (scheme) {
+    case PQL_FP8_TENSOR: kind = 0; break;
+    case PQL_FP8_ROW: kind = 1; break;
+    case PQL_FP8_BLOCK128: kind = role == PQL_ACTIVATION ? 2 : 3; break;
+    case PQL_MXFP8: kind = 4; break;
+    case PQL_MXFP4: kind = 5; break;
+    default: kind = 6; break;
+  }
+  return launched(pql::launch_dequant(kind, codes, scales, static_cast<const uint8_t*>(zeros), rows, cols,
+                                      static_cast<uint16_t*>(y), ldy, static_cast<hipStream_t>(stream)),
+                  "dequantize launch");
+}
+
+pql_status pql_qgemm(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
+                     const void* w_zeros, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, void* stream) {
+  if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
+  pql_status st = check_gemm_shape(scheme, M, N, K);
+  if (st != PQL_OK) return st;
+  if (ldc < N) return fail(PQL_ERR_INVALID_ARGUMENT, "ldc must be >= N (got %lld)", (long long)ldc);
+  if (M == 0) return ok();
+  if (!a || !w_codes || !w_scales || !c) return fail(PQL_ERR_INVALID_ARGUMENT, "a, w_codes, w_scales and c must be non-NULL");
+  if (!is_w4a16(scheme) && !a_scales) return fail(PQL_ERR_INVALID_ARGUMENT, "a_scales must be non-NULL");
+  if (is_w4a16(scheme) && !w_zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "w_zeros must be non-NULL for W4A16");
+  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || (a_scales && !aligned16(a_scales)))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "operands and scales must be 16-byte aligned");
+  if ((st = check_device()) != PQL_OK) return st;
+  return launched(do_qgemm(scheme, a, a_scales, w_codes, w_scales, w_zeros, M, N, K, c, ldc,
+                           static_cast<hipStream_t>(stream)),
+                  "qgemm launch");
+}
+
+pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* w_codes,
+                       const void* w_scales, const void* w_zeros, int64_t N, void* c, int64_t ldc, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
+  pql_status st = check_gemm_shape(scheme, M, N, K);
+  if (st != PQL_OK) return st;
+  if (ldc < N) return fail(PQL_ERR_INVALID_ARGUMENT, "ldc must be >= N (got %lld)", (long long)ldc);
+  if (is_w4a16(scheme) ? lda != K : (lda < K || lda % 8))
+    return fail(PQL_ERR_INVALID_ARGUMENT, is_w4a16(scheme) ? "W4A16 needs lda == K" : "lda must be >= K and a multiple of 8");
+  if (M == 0) return ok();
+  if (!a || !w_codes || !w_scales || !c) return fail(PQL_ERR_INVALID_ARGUMENT, "a, w_codes, w_scales and c must be non-NULL");
+  if (is_w4a16(scheme) && !w_zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "w_zeros must be non-NULL for W4A16");
+  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "operands and scales must be 16-byte aligned");
+  size_t need = 0;
+  if (!is_w4a16(scheme)) {
+    const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
+    need = round256(s.codes) + round256(s.scales) + (scheme == PQL_FP8_TENSOR ? kTensorWs : 0);
+    if (!workspace || workspace_bytes < need)
+      return fail(PQL_ERR_WORKSPACE, "qlinear needs a %zu-byte workspace (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PQL_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+  if ((st = check_device()) != PQL_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (is_w4a16(scheme))
+    return launched(do_qgemm(scheme, a, nullptr, w_codes, w_scales, w_zeros, M, N, K, c, ldc, hs), "qlinear launch");
+  const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void* a_codes = ws;
+  void* a_scales = ws + round256(s.codes);
+  void* partials = ws + round256(s.codes) + round256(s.scales);
+  hipError_t e = do_quantize(scheme, PQL_ACTIVATION, a, M, K, lda, a_codes, a_scales, nullptr, partials, hs);
+  if (e != hipSuccess) return launched(e, "qlinear activation quantize");
+  return launched(do_qgemm(scheme, a_codes, a_scales, w_codes, w_scales, w_zeros, M, N, K, c, ldc, hs),
+                  "qlinear gemm");
+}
+
+const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, int64_t K) {
+  if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM) return "";
+  switch (op) {
+    case PQL_OP_QUANTIZE:
+      if (is_w4a16(scheme) && role == PQL_ACTIVATION) return "";
+      switch (scheme) {
+        case PQL_FP8_TENSOR: return "k_amax_partial+k_fp8_tensor";
+        case PQL_FP8_ROW: return "k_fp8_row";
+        case PQL_FP8_BLOCK128: return role == PQL_ACTIVATION ? "k_fp8_block_act" : "k_fp8_block_wt";
+        case PQL_MXFP8: return "k_mx<e4m3>";
+        case PQL_MXFP4: return "k_mx<e2m1>";
+        default: return scheme == PQL_W4A16_SYM ? "k_int4<sym>" : "k_int4<asym>";
+      }
+    case PQL_OP_DEQUANTIZE: return "k_dequant";
+    case PQL_OP_QGEMM:
+    case PQL_OP_QLINEAR:
+      if (is_w4a16(scheme)) return pql::gemm_w4a16_kernel_name(M, N, K);
+      return pql::gemm_kernel_name(scheme == PQL_FP8_BLOCK128 ? pql::GEMM_FP8_BLOCK
+                                   : scheme == PQL_MXFP8      ? pql::GEMM_MXFP8
+                                   : scheme == PQL_MXFP4      ? pql::GEMM_MXFP4
+                                                              : pql::GEMM_FP8_ROWSCALE,
+                                   M, N, K);
+  }
+  return "";
+}
+
+}  // extern "C"

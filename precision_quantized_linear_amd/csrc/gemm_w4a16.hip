@@ -1,0 +1,278 @@
+// W4A16 GEMM on gfx950: C[M, N] = A (bf16) * W_hat^T, W_hat = bf16((q - z) * s).
+//
+// The weight is int4 with a bf16 scale and a 4-bit zero-point per 128-element
+// K-group ("vLLM-Omni accelerates inference with AutoRound quantization",
+// section "Usage": bits 4, group size 128).  Each weight element is expanded
+// to bf16((q - z) * s) -- the product is exact in fp32, so this equals the
+// library's own dequantize -- and multiplied on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16: lane l feeds row l % 16 with K-elements
+// 8 * (l / 16) .. +7; accumulator lane l holds C[4 * (l / 16) + r][l % 16]).
+//
+// Two kernels:
+//   * M > 64: compute-bound.  256 x 256 output tile per 256-thread workgroup,
+//     K steps of 64.  Per step the workgroup stages A (bf16, 32 KB) and the
+//     expanded W tile (bf16, 32 KB) in double-buffered LDS; each thread
+//     expands one W row-slice of 64 codes.  LDS layout and bank swizzle are
+//     the same as the fp8 kernel's (128-byte rows, chunk c at c ^ (row & 7)).
+//   * M <= 64: weight-bandwidth-bound.  A workgroup owns 32 output columns;
+//     its 4 waves split the K-groups, each wave streams 16-byte code chunks
+//     straight into registers (no LDS staging), and the partial sums of the
+//     4 waves are added in LDS.
+#include <algorithm>
+
+#include "pql_device.hpp"
+#include "pql_internal.hpp"
+
+namespace pql {
+
+namespace {
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return bf16_bits(lo) | (bf16_bits(hi) << 16); }
+
+// 8 int4 codes (element j at bits 4j) -> 8 bf16 of (q - z) * s, packed in pairs.
+__device__ __forceinline__ uint4 expand8(uint32_t w, float s, float zs) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf((float)((w >> (4 * j)) & 0xF), s, zs);
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
+}
+
+__device__ __forceinline__ v8bf as_v8bf(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+
+constexpr int BM = 256, BN = 256, BKB = 128;    // BKB bytes = 64 bf16 per row per step
+constexpr int kStageBytes = BM * BKB + BN * BKB;
+constexpr int kGroupM = 4;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BKB + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ void tile_of_block(int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int b = blockIdx.x;
+  const int xcd = b & 7, idx = b >> 3;
+  const int per = T >> 3, rem = T & 7;
+  const int L = xcd * per + min(xcd, rem) + idx;
+  const int in_group = kGroupM * tiles_n;
+  const int group = L / in_group;
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int l = L - group * in_group;
+  tm = first_m + l % gm;
+  tn = l / gm;
+}
+
+// ---------------------------------------------------------------- large M
+__global__ __launch_bounds__(256, 1) void k_w4a16_tile(const uint16_t* __restrict__ a,
+                                                      const uint32_t* __restrict__ wq,
+                                                      const uint16_t* __restrict__ w_scales,
+                                                      const uint8_t* __restrict__ w_zeros, int64_t M,
+                                                      int64_t N, int64_t K, uint16_t* __restrict__ c,
+                                                      int64_t ldc) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  int tm, tn;
+  tile_of_block(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t Ab = K * 2;                 // A bytes per row
+  const int64_t Wb = K / 2;                 // code bytes per row
+  const int nsteps = (int)(K / 64);
+  const int64_t ngroups = K / 128;
+
+  const int ld_c = t & 7, ld_r = t >> 3;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a + m0 * K), (short)0, (int)(std::min<int64_t>(BM, M - m0) * Ab), 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const uint8_t*>(wq) + n0 * Wb), (short)0,
+      (int)(std::min<int64_t>(BN, N - n0) * Wb), 0x00020000);
+  const int64_t wrow = std::min<int64_t>(n0 + t, N - 1);   // the W row this thread expands
+
+  uint4 ra[8];
+  uint4 rw[2];
+  float s_reg = 0.f, zs_reg = 0.f;
+  auto load_step = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v4i v = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, (ld_r + 32 * i) * (int)Ab + s * BKB + ld_c * 16, 0, 0);
+      ra[i] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v4i v = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, t * (int)Wb + s * 32 + h * 16, 0, 0);
+      rw[h] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+    const int64_t gi = wrow * ngroups + (s >> 1);
+    s_reg = __uint_as_float((uint32_t)w_scales[gi] << 16);
+    zs_reg = -(float)w_zeros[gi] * s_reg;      // exact: z * s fits in fp32
+  };
+  auto store_step = [&](int stage) {
+    uint8_t* A = smem + stage * kStageBytes;
+    uint8_t* W = A + BM * BKB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(A + swz(ld_r + 32 * i, ld_c)) = ra[i];
+    const uint32_t words[8] = {rw[0].x, rw[0].y, rw[0].z, rw[0].w, rw[1].x, rw[1].y, rw[1].z, rw[1].w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) *reinterpret_cast<uint4*>(W + swz(t, q)) = expand8(words[q], s_reg, zs_reg);
+  };
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  const int fr = lane & 15, fk = lane >> 4;
+  for (int s = 0; s < nsteps; ++s) {
+    const int stage = s & 1;
+    if (s + 1 < nsteps) load_step(s + 1);
+    const uint8_t* A = smem + stage * kStageBytes;
+    const uint8_t* W = A + BM * BKB;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      v8bf af[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        af[i] = as_v8bf(*reinterpret_cast<const uint4*>(A + swz(wm * 128 + i * 16 + fr, 4 * kk + fk)));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const v8bf bf = as_v8bf(*reinterpret_cast<const uint4*>(W + swz(wn * 128 + j * 16 + fr, 4 * kk + fk)));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][j], 0, 0, 0);
+      }
+    }
+    if (s + 1 < nsteps) store_step(stage ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t col = n0 + wn * 128 + j * 16 + fr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wm * 128 + i * 16 + 4 * fk + r;
+        if (row < M) c[row * ldc + col] = (uint16_t)bf16_bits(acc[i][j][r]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- small M
+// Workgroup: 32 columns (two 16-column MFMA blocks), 4 waves splitting the
+// K-groups round-robin.  Within a 128-group, lane slot g = l / 16 owns the 32
+// consecutive K-elements 32 g .. 32 g + 31 (one 16-byte code load), and MFMA
+// step t consumes elements 32 g + 8 t .. + 7 from every slot; A is read with
+// the same assignment, so the contraction still covers each k exactly once.
+template <int MB>   // row blocks of 16
+__global__ __launch_bounds__(256) void k_w4a16_small(const uint16_t* __restrict__ a,
+                                                    const uint32_t* __restrict__ wq,
+                                                    const uint16_t* __restrict__ w_scales,
+                                                    const uint8_t* __restrict__ w_zeros, int64_t M,
+                                                    int64_t N, int64_t K, uint16_t* __restrict__ c,
+                                                    int64_t ldc) {
+  __shared__ float part[4][MB * 16][33];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int fr = lane & 15, g4 = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 32;
+  const int64_t ngroups = K / 128;
+  const int64_t wpr = K / 8;                        // code words per row
+
+  v4f acc[MB][2];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i][0] = acc[i][1] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  int64_t wrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wrow[j] = std::min<int64_t>(n0 + j * 16 + fr, N - 1);
+
+  for (int64_t gidx = wave; gidx < ngroups; gidx += 4) {
+    uint4 code[2];
+    float s[2], zs[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      code[j] = ldg16_nt(wq + wrow[j] * wpr + gidx * 16 + g4 * 4);
+      const int64_t gi = wrow[j] * ngroups + gidx;
+      s[j] = __uint_as_float((uint32_t)w_scales[gi] << 16);
+      zs[j] = -(float)w_zeros[gi] * s[j];
+    }
+    const uint32_t cw[2][4] = {{code[0].x, code[0].y, code[0].z, code[0].w},
+                               {code[1].x, code[1].y, code[1].z, code[1].w}};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      v8bf bf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bf[j] = as_v8bf(expand8(cw[j][st], s[j], zs[j]));
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int64_t row = (int64_t)i * 16 + fr;
+        uint4 av = make_uint4(0, 0, 0, 0);
+        if (row < M) av = ldg16(a + row * K + gidx * 128 + g4 * 32 + st * 8);
+        const v8bf af = as_v8bf(av);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[wave][i * 16 + 4 * g4 + r][j * 16 + fr] = acc[i][j][r];
+  __syncthreads();
+  for (int e = t; e < MB * 16 * 32; e += 256) {
+    const int row = e >> 5, col = e & 31;
+    const int64_t gc = n0 + col;
+    if (row < M && gc < N) {
+      const float v = part[0][row][col] + part[1][row][col] + part[2][row][col] + part[3][row][col];
+      c[(int64_t)row * ldc + gc] = (uint16_t)bf16_bits(v);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales,
+                             const uint8_t* w_zeros, int64_t M, int64_t N, int64_t K, uint16_t* c,
+                             int64_t ldc, hipStream_t st) {
+  if (M <= 64) {
+    const dim3 grid((unsigned)((N + 31) / 32)), block(256);
+    if (M <= 16) hipLaunchKernelGGL(k_w4a16_small<1>, grid, block, 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+    else if (M <= 32) hipLaunchKernelGGL(k_w4a16_small<2>, grid, block, 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+    else hipLaunchKernelGGL(k_w4a16_small<4>, grid, block, 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+    return hipGetLastError();
+  }
+  const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+  const size_t lds = 2 * kStageBytes;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static bool configured[64] = {};
+  if (dev < 64 && !configured[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_w4a16_tile),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    configured[dev] = true;
+  }
+  hipLaunchKernelGGL(k_w4a16_tile, dim3(tiles), dim3(256), lds, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+  return hipGetLastError();
+}
+
+const char* gemm_w4a16_kernel_name(int64_t M, int64_t, int64_t) {
+  if (M <= 16) return "k_w4a16_small<16>";
+  if (M <= 32) return "k_w4a16_small<32>";
+  if (M <= 64) return "k_w4a16_small<64>";
+  return "k_w4a16_tile_256x256x64";
+}
+
+}  // namespace pql

@@ -1,0 +1,59 @@
+// Host-side interface between the C ABI (abi.cpp) and the kernel launchers.
+// Launchers assume their arguments were validated by the ABI layer and return
+// the HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pql {
+
+// Number of per-block partial maxima the per-tensor amax pass writes.
+constexpr int kTensorAmaxBlocks = 1024;
+
+// ---------------------------------------------------------------- quantize
+hipError_t launch_quant_fp8_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   uint8_t* codes, float* scale, float* ws_partials, hipStream_t st);
+hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_fp8_block_act(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                      uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_fp8_block_wt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                     uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_mx(bool fp4, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                           uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_quant_int4(bool sym, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                             uint32_t* codes, uint16_t* scales, uint8_t* zeros, hipStream_t st);
+
+// ---------------------------------------------------------------- dequantize
+// kind: 0 fp8 tensor, 1 fp8 row, 2 fp8 block act, 3 fp8 block weight, 4 mxfp8,
+//       5 mxfp4, 6 int4
+hipError_t launch_dequant(int kind, const void* codes, const void* scales, const uint8_t* zeros,
+                          int64_t rows, int64_t cols, uint16_t* y, int64_t ldy, hipStream_t st);
+
+// ---------------------------------------------------------------- GEMM
+enum GemmKind { GEMM_FP8_ROWSCALE = 0, GEMM_FP8_BLOCK = 1, GEMM_MXFP8 = 2, GEMM_MXFP4 = 3 };
+
+struct GemmArgs {
+  const uint8_t* a;        // A codes [M, K] (fp4: [M, K/2])
+  const uint8_t* w;        // W codes [N, K] (fp4: [N, K/2])
+  const void* a_scales;    // fp32 or e8m0, per kind
+  const void* w_scales;
+  int64_t a_scale_stride;  // fp8 row-scale kind: 0 = one scale for all rows, 1 = per row
+  int64_t w_scale_stride;
+  int64_t M, N, K;
+  uint16_t* c;             // bf16 [M, ldc]
+  int64_t ldc;
+};
+
+hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st);
+const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);
+
+// W4A16: C = A (bf16) * dequant(Wq)^T
+hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales,
+                             const uint8_t* w_zeros, int64_t M, int64_t N, int64_t K,
+                             uint16_t* c, int64_t ldc, hipStream_t st);
+const char* gemm_w4a16_kernel_name(int64_t M, int64_t N, int64_t K);
+
+}  // namespace pql

@@ -1,0 +1,176 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function that
+include/pql.h declares, answers size queries, and rejects bad arguments before
+touching a device.  No compute is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import precision_quantized_linear_amd as pql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pql.h")
+
+S = pql.SCHEMES
+A, W = pql.ROLES["activation"], pql.ROLES["weight"]
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pql_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = pql.lib()
+    names = header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in pql.h but not exported"
+    assert L.pql_version() == 1
+
+
+def _sizes(scheme, role, rows, cols):
+    return pql.quantized_sizes(scheme, role, rows, cols)
+
+
+def test_quantized_sizes():
+    assert _sizes("fp8_tensor", "activation", 256, 512) == (256 * 512, 4, 0)
+    assert _sizes("fp8_row", "weight", 12288, 3072) == (12288 * 3072, 4 * 12288, 0)
+    assert _sizes("fp8_block128", "activation", 8192, 5120) == (8192 * 5120, 4 * 8192 * 40, 0)
+    assert _sizes("fp8_block128", "weight", 13824, 5120) == (13824 * 5120, 4 * 108 * 40, 0)
+    assert _sizes("mxfp8", "activation", 20280, 5120) == (20280 * 5120, 20280 * 160, 0)
+    assert _sizes("mxfp4", "weight", 5120, 5120) == (5120 * 2560, 5120 * 160, 0)
+    assert _sizes("w4a16_asym", "weight", 12288, 3072) == (12288 * 1536, 2 * 12288 * 24, 12288 * 24)
+
+
+@pytest.mark.parametrize("scheme,role,rows,cols", [
+    ("fp8_row", "activation", 4, 48),         # K not a multiple of 32
+    ("mxfp8", "activation", 4, 16),
+    ("fp8_block128", "activation", 4, 96),    # K not a multiple of 128
+    ("fp8_block128", "weight", 64, 128),      # weight rows not a multiple of 128
+    ("w4a16_asym", "weight", 4, 64),
+    ("fp8_row", "activation", -1, 64),
+    ("fp8_row", "activation", 4, 0),
+])
+def test_invalid_shapes_rejected(scheme, role, rows, cols):
+    with pytest.raises(ValueError):
+        _sizes(scheme, role, rows, cols)
+
+
+def test_unsupported_combinations():
+    with pytest.raises(NotImplementedError):
+        _sizes("w4a16_asym", "activation", 4, 128)
+    with pytest.raises(NotImplementedError):
+        _sizes(7, "activation", 4, 128)
+    with pytest.raises(NotImplementedError):
+        _sizes("fp8_row", 2, 4, 128)
+
+
+def test_workspace_sizes():
+    assert pql.workspace_size("quantize", "fp8_tensor") == 4096
+    assert pql.workspace_size("quantize", "mxfp8") == 0
+    ws = pql.workspace_size("qlinear", "mxfp8", "activation", 20280, 5120, 5120)
+    assert ws == 20280 * 5120 + ((20280 * 160 + 255) // 256) * 256
+    assert pql.workspace_size("qlinear", "w4a16_asym", "activation", 16, 12288, 3072) == 0
+    with pytest.raises(ValueError):
+        pql.workspace_size("qlinear", "fp8_row", "activation", 16, 128, 100)
+
+
+def test_kernel_names_distinct_per_scheme():
+    names = {s: pql.kernel_name("qgemm", s, "activation", 4096, 4096, 4096) for s in S}
+    assert all(names.values())
+    fp = [names[s] for s in ("fp8_row", "fp8_block128", "mxfp8", "mxfp4")]
+    assert len(set(fp)) == 4
+    assert pql.kernel_name("quantize", "w4a16_asym", "activation") == ""
+    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 1, 12288, 3072).startswith("k_w4a16_small")
+    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 4096, 12288, 3072).startswith("k_w4a16_tile")
+
+
+# ----------------------------------------------------------------- validation before launch
+# Host buffers stand in for device pointers: every call below must fail in
+# validation, before any device is touched.
+_buf = (ctypes.c_uint8 * 4096 * 64)()
+_base = (ctypes.addressof(_buf) + 255) & ~255
+
+
+def _p(off=0):
+    return _base + off
+
+
+def _quantize(scheme=S["fp8_row"], role=A, x=None, rows=16, cols=128, ldx=128, codes=None, scales=None,
+              zeros=None, ws=None, wsb=0):
+    L = pql.lib()
+    return L.pql_quantize(scheme, role, _p() if x is None else x, rows, cols, ldx,
+                          _p(4096) if codes is None else codes, _p(8192) if scales is None else scales,
+                          zeros, ws, wsb, None)
+
+
+def test_quantize_validation():
+    assert _quantize(x=0) == pql.PQL_ERR_INVALID_ARGUMENT                  # NULL x
+    assert _quantize(ldx=120) == pql.PQL_ERR_INVALID_ARGUMENT              # ldx < cols
+    assert _quantize(ldx=132) == pql.PQL_ERR_INVALID_ARGUMENT              # ldx not a multiple of 8
+    assert _quantize(x=_p(4)) == pql.PQL_ERR_INVALID_ARGUMENT              # misaligned
+    assert _quantize(cols=100) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert _quantize(scheme=S["w4a16_asym"], role=A) == pql.PQL_ERR_UNSUPPORTED
+    assert _quantize(scheme=S["w4a16_asym"], role=W, zeros=None) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert _quantize(scheme=S["fp8_tensor"], ws=None) == pql.PQL_ERR_WORKSPACE
+    assert _quantize(scheme=S["fp8_tensor"], ws=_p(16384), wsb=64) == pql.PQL_ERR_WORKSPACE
+    assert _quantize(scheme=9) == pql.PQL_ERR_UNSUPPORTED
+    assert _quantize(rows=0) == pql.PQL_OK                                 # empty: no-op
+    assert "ldx" in _last_error_after(lambda: _quantize(ldx=120))
+
+
+def _last_error_after(fn):
+    fn()
+    return pql.lib().pql_last_error().decode()
+
+
+def test_qgemm_validation():
+    L = pql.lib()
+    g = lambda scheme=S["fp8_row"], a=_p(), sa=_p(1024), wc=_p(2048), ws=_p(3072), wz=None, M=16, N=256, K=256, \
+        c=_p(8192), ldc=256: L.pql_qgemm(scheme, a, sa, wc, ws, wz, M, N, K, c, ldc, None)
+    assert g(K=200) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(N=0) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(ldc=100) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(sa=None) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(scheme=S["w4a16_asym"], wz=None) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(scheme=S["fp8_block128"], N=200, ldc=200) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(a=_p(8)) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(scheme=11) == pql.PQL_ERR_UNSUPPORTED
+    assert g(M=0) == pql.PQL_OK
+
+
+def test_qlinear_validation():
+    L = pql.lib()
+    q = lambda scheme=S["mxfp8"], M=16, K=256, lda=256, N=256, ws=_p(16384), wsb=64: L.pql_qlinear(
+        scheme, _p(), M, K, lda, _p(2048), _p(3072), None, N, _p(8192), N, ws, wsb, None)
+    assert q(wsb=64) == pql.PQL_ERR_WORKSPACE
+    assert q(ws=None, wsb=0) == pql.PQL_ERR_WORKSPACE
+    assert q(lda=250) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert q(K=96, lda=96) == pql.PQL_ERR_INVALID_ARGUMENT
+
+
+def test_dequantize_validation():
+    L = pql.lib()
+    d = lambda scheme=S["mxfp4"], role=A, codes=_p(), rows=16, cols=128, ldy=128: L.pql_dequantize(
+        scheme, role, codes, _p(4096), None, rows, cols, _p(8192), ldy, None)
+    assert d(codes=None) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert d(ldy=64) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert d(scheme=S["w4a16_sym"], role=W) == pql.PQL_ERR_INVALID_ARGUMENT     # zeros NULL
+    assert d(scheme=S["w4a16_sym"], role=A) == pql.PQL_ERR_UNSUPPORTED
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="checks the no-device path")
+def test_valid_call_without_device_reports_hip_error():
+    assert _quantize() == pql.PQL_ERR_HIP
+    assert "HIP" in pql.lib().pql_last_error().decode() or "device" in pql.lib().pql_last_error().decode()
+
+
+def test_python_api_errors_map_to_exceptions():
+    with pytest.raises(ValueError):
+        pql.quantize(torch.zeros(4, 128, dtype=torch.float32), "mxfp8")
+    with pytest.raises(ValueError):
+        pql.quantize(torch.zeros(4, 128, dtype=torch.bfloat16), "nvfp4")

@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+* Quantized codes, scales and zero-points must match the oracle bit for bit.
+* Dequantized bf16 must match bit for bit.
+* GEMM outputs, given identical quantized inputs, must satisfy
+  ||C_gpu - C_oracle||_F / ||C_oracle||_F <= 1e-2 (the tolerance the
+  quantized-linear target states); the oracle is the exact float64 product.
+Small cases span several 256x256 tiles with ragged M / N tails; the full-size
+workloads (the shapes the benchmark times) are checked on sampled rows and
+sampled output entries, which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import precision_quantized_linear_amd as pql
+import workloads as wl
+from oracle import formats as F
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TOL = 1e-2
+FP_SCHEMES = ("fp8_tensor", "fp8_row", "fp8_block128", "mxfp8", "mxfp4")
+
+
+def up(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def down_bf16(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_q_equal(gpu: dict, ref: dict, what=""):
+    assert np.array_equal(gpu["codes"], ref["codes"]), f"codes differ {what}: " + _first_diff(gpu["codes"], ref["codes"])
+    gs, rs = np.asarray(gpu["scales"]), np.asarray(ref["scales"])
+    if gs.dtype == np.float32:
+        gs, rs = gs.view(np.uint32), rs.astype(np.float32).view(np.uint32)
+    assert np.array_equal(gs.reshape(rs.shape), rs), f"scales differ {what}: " + _first_diff(gs.reshape(rs.shape), rs)
+    if ref["zeros"] is not None:
+        assert np.array_equal(gpu["zeros"], ref["zeros"]), f"zeros differ {what}"
+
+
+def _first_diff(a, b):
+    idx = np.argwhere(a != b)
+    if len(idx) == 0:
+        return "shapes " + str(a.shape) + " vs " + str(b.shape)
+    i = tuple(idx[0])
+    return f"{len(idx)} entries, first at {i}: gpu {a[i]!r} oracle {b[i]!r}"
+
+
+def hard_input(seed, rows, cols, std=1.0):
+    """Normal data plus the cases the casts must get right: zero rows / groups, exact
+    ties after scaling, tiny and subnormal values, negative zeros, one huge outlier."""
+    x = wl.bf16_bits_to_f32(wl.small_case(seed, rows, cols, std)).copy()
+    rng = np.random.default_rng(seed + 1)
+    if rows > 2:
+        x[1, :] = 0.0
+    x[0, : min(cols, 128)] = np.float32(0.0)
+    x[0, 0] = 448.0 * std
+    x[0, 1] = 0.53125 * std
+    x[0, 2] = 0.59375 * std
+    if rows > 3:
+        x[2, 32:64] = np.float32(1e-39)          # bf16 subnormal range
+        x[3, 5] = np.float32(3.0e38)
+    idx = rng.integers(0, rows * cols, 50)
+    x.reshape(-1)[idx] *= np.float32(7.5)
+    bits = wl.f32_to_bf16_bits(x)
+    bits.reshape(-1)[rng.integers(0, rows * cols, 20)] = 0x8000   # -0
+    return bits
+
+
+# ----------------------------------------------------------------- quantize
+QUANT_CASES = []
+for scheme in FP_SCHEMES + ("w4a16_asym", "w4a16_sym"):
+    for role in ("activation", "weight"):
+        if scheme.startswith("w4a16") and role == "activation":
+            continue
+        for rows, cols in ((1, 128), (37, 384), (300, 1152), (384, 640)):
+            if scheme == "fp8_block128" and role == "weight" and rows % 128:
+                continue
+            QUANT_CASES.append((scheme, role, rows, cols))
+
+
+@pytest.mark.parametrize("scheme,role,rows,cols", QUANT_CASES)
+def test_quantize_bit_exact(scheme, role, rows, cols):
+    x = hard_input(rows * 7 + cols, rows, cols, 0.02 if role == "weight" else 1.0)
+    ref = oracle.quantize(x, scheme, role)
+    got = pql.to_numpy(pql.quantize(up(x), scheme, role))
+    assert_q_equal(got, ref, f"{scheme}/{role} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("scheme", FP_SCHEMES + ("w4a16_asym",))
+def test_quantize_strided_rows(scheme):
+    role = "weight" if scheme == "w4a16_asym" else "activation"
+    wide = hard_input(99, 256, 768)
+    x = up(wide)[:, 128:128 + 512]
+    ref = oracle.quantize(np.ascontiguousarray(wide[:, 128:128 + 512]), scheme, role)
+    assert_q_equal(pql.to_numpy(pql.quantize(x, scheme, role)), ref, "strided")
+
+
+def test_quantize_row_longer_than_register_tile():
+    # per-row FP8 keeps up to 8192 elements per row in registers; longer rows take the two-pass path
+    x = hard_input(5, 9, 12288)
+    assert_q_equal(pql.to_numpy(pql.quantize(up(x), "fp8_row")), oracle.quantize(x, "fp8_row"), "long rows")
+
+
+@pytest.mark.parametrize("scheme", FP_SCHEMES)
+def test_quantize_all_zero(scheme):
+    x = np.zeros((128, 256), np.uint16)
+    assert_q_equal(pql.to_numpy(pql.quantize(up(x), scheme, "weight")), oracle.quantize(x, scheme, "weight"))
+
+
+# ----------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("scheme,role", [(s, r) for s in FP_SCHEMES for r in ("activation", "weight")]
+                         + [("w4a16_asym", "weight"), ("w4a16_sym", "weight")])
+def test_dequantize_bit_exact(scheme, role):
+    x = hard_input(17, 256, 640, 0.02 if role == "weight" else 1.0)
+    ref_q = oracle.quantize(x, scheme, role)
+    y = pql.dequantize(pql.from_numpy(ref_q, DEV))
+    assert np.array_equal(down_bf16(y), oracle.dequantize(ref_q))
+
+
+# ----------------------------------------------------------------- GEMM, small shapes
+GEMM_SHAPES = [(1, 256, 128), (77, 384, 256), (256, 256, 640), (300, 640, 1152), (513, 128, 384)]
+
+
+@pytest.mark.parametrize("scheme", FP_SCHEMES)
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_qgemm_matches_oracle(scheme, M, N, K):
+    a = wl.small_case(1000 + M, M, K, 1.0)
+    w = wl.small_case(2000 + N, N, K, 0.02)
+    aq, wq = oracle.quantize(a, scheme, "activation"), oracle.quantize(w, scheme, "weight")
+    c = pql.qgemm(pql.from_numpy(aq, DEV), pql.from_numpy(wq, DEV))
+    c_gpu = F.bf16_to_f32(down_bf16(c)).astype(np.float64)
+    err = oracle.rel_fro_error(c_gpu, oracle.gemm_ref(aq, wq))
+    assert err <= TOL, f"{scheme} {M}x{N}x{K}: rel err {err:.3e}"
+    assert err <= 5e-3   # expected ~2^-9 from the bf16 output rounding; flags a drift early
+
+
+@pytest.mark.parametrize("M", [1, 5, 16, 33, 64, 65, 300])
+@pytest.mark.parametrize("sym", [False, True])
+def test_w4a16_gemm_matches_oracle(M, sym):
+    N, K = 384, 1152
+    a = wl.small_case(3000 + M, M, K, 1.0)
+    w = wl.small_case(4000, N, K, 0.02)
+    wq = oracle.quantize(w, "w4a16_sym" if sym else "w4a16_asym", "weight")
+    c = pql.qgemm(up(a), pql.from_numpy(wq, DEV))
+    err = oracle.rel_fro_error(F.bf16_to_f32(down_bf16(c)), oracle.gemm_ref(a, wq))
+    assert err <= TOL, f"M={M}: rel err {err:.3e}"
+
+
+@pytest.mark.parametrize("scheme", FP_SCHEMES + ("w4a16_asym",))
+def test_qlinear_equals_quantize_then_qgemm(scheme):
+    M, N, K = 300, 384, 640
+    a = up(wl.small_case(5, M, K))
+    wq = pql.quantize(up(wl.small_case(6, N, K, 0.02)), scheme, "weight")
+    y = pql.qlinear(a.reshape(3, 100, K), wq)
+    assert y.shape == (3, 100, N)
+    if scheme.startswith("w4a16"):
+        ref = pql.qgemm(a, wq)
+    else:
+        ref = pql.qgemm(pql.quantize(a, scheme, "activation"), wq)
+    assert torch.equal(y.reshape(M, N).view(torch.int16), ref.view(torch.int16))
+
+
+def test_schemes_give_different_outputs():
+    """The pages' no-silent-fallback check: each scheme is a real, different computation."""
+    M, N, K = 256, 256, 512
+    a = up(wl.small_case(7, M, K))
+    w = up(wl.small_case(8, N, K, 0.02))
+    outs = {s: pql.qlinear(a, pql.quantize(w, s, "weight")) for s in FP_SCHEMES + ("w4a16_asym",)}
+    keys = list(outs)
+    for i in range(len(keys)):
+        for j in range(i + 1, len(keys)):
+            assert not torch.equal(outs[keys[i]], outs[keys[j]]), (keys[i], keys[j])
+
+
+# ----------------------------------------------------------------- full-size workloads
+def _sample_rows(n, k, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(n, min(k, n), replace=False).tolist()) | {0, n - 1} | set(extra)
+    return np.array(sorted(r for r in rows if 0 <= r < n))
+
+
+def _take(q_np: dict, rows: np.ndarray, role: str) -> dict:
+    """Rows of a downloaded GPU quantization (canonical layout) as an oracle-style dict."""
+    out = dict(q_np)
+    out["codes"] = q_np["codes"][rows]
+    if q_np["scheme"] == "fp8_tensor":
+        out["scales"] = q_np["scales"]
+    elif q_np["scheme"] == "fp8_block128" and role == "weight":
+        out["scales"] = q_np["scales"][rows // 128]
+    else:
+        out["scales"] = q_np["scales"][rows]
+    if q_np["zeros"] is not None:
+        out["zeros"] = q_np["zeros"][rows]
+    out["rows"] = len(rows)
+    return out
+
+
+def _expand_block_rows(q: dict) -> dict:
+    """A row subset of a 128x128-block weight as a dict the oracle can dequantize:
+    repeat the block scale per row and relabel it as a per-(row, group) scale."""
+    q = dict(q)
+    q["role"] = "activation"
+    return q
+
+
+def _check_rows(xbits, q_gpu_np, scheme, role, rows):
+    if scheme == "fp8_block128" and role == "weight":
+        blocks = np.unique(rows // 128)
+        for b in blocks:
+            r = np.arange(b * 128, b * 128 + 128)
+            ref = oracle.quantize(np.ascontiguousarray(xbits[r]), scheme, role)
+            got = dict(_take(q_gpu_np, r, role))
+            got["scales"] = q_gpu_np["scales"][b:b + 1]
+            assert_q_equal(got, ref, f"block {b}")
+        return
+    ref = oracle.quantize(np.ascontiguousarray(xbits[rows]), scheme, role)
+    assert_q_equal(_take(q_gpu_np, rows, role), ref, "sampled rows")
+
+
+def _gemm_sample_ref(aq_rows: dict, wq_rows: dict, scheme):
+    if scheme == "fp8_block128":
+        # expand the weight's block scales to per-(row, group) so the sampled rows stand alone
+        w = dict(wq_rows)
+        w["scales"] = np.asarray(wq_rows["scales"], np.float32)
+        w["role"] = "activation"
+        return oracle.gemm_ref(aq_rows, w)
+    return oracle.gemm_ref(aq_rows, wq_rows)
+
+
+@pytest.mark.parametrize("name,scheme", [("fp8_tensor_small", "fp8_tensor"), ("fp8_row_dit", "fp8_row"),
+                                         ("fp8_block_dit", "fp8_block128"), ("mx_video_dit", "mxfp8"),
+                                         ("mx_video_dit", "mxfp4")])
+def test_full_size_workload(name, scheme):
+    w_ = wl.WORKLOADS[name]
+    a_bits, w_bits = wl.activation(w_), wl.weight(w_)
+    a_t, w_t = up(a_bits), up(w_bits)
+    wq = pql.quantize(w_t, scheme, "weight")
+    aq = pql.quantize(a_t, scheme, "activation")
+    y = pql.qlinear(a_t, wq)
+    c = pql.qgemm(aq, wq)
+    assert torch.equal(y.view(torch.int16), c.view(torch.int16)), "qlinear != quantize + qgemm"
+    aq_np, wq_np = pql.to_numpy(aq), pql.to_numpy(wq)
+    if scheme == "fp8_tensor":
+        assert_q_equal(aq_np, oracle.quantize(a_bits, scheme, "activation"), "A")
+        assert_q_equal(wq_np, oracle.quantize(w_bits, scheme, "weight"), "W")
+        err = oracle.rel_fro_error(F.bf16_to_f32(down_bf16(c)), oracle.gemm_ref(aq_np, wq_np))
+        assert err <= TOL
+        return
+    ra = _sample_rows(w_.M, 96, 11, extra=range(w_.M - 40, w_.M))    # includes the ragged tail
+    rw = _sample_rows(w_.N, 96, 12, extra=range(w_.N - 8, w_.N))
+    _check_rows(a_bits, aq_np, scheme, "activation", ra)
+    _check_rows(w_bits, wq_np, scheme, "weight", rw)
+    a_rows = _take(aq_np, ra, "activation")
+    w_rows = _take(wq_np, rw, "weight")
+    if scheme == "fp8_block128":
+        w_rows["scales"] = np.repeat(wq_np["scales"][rw // 128][:, None, :], 1, axis=1).reshape(len(rw), -1)
+    ref = _gemm_sample_ref(a_rows, w_rows, scheme)
+    got = F.bf16_to_f32(down_bf16(c)[np.ix_(ra, rw)])
+    err = oracle.rel_fro_error(got, ref)
+    assert err <= TOL, f"{name}/{scheme}: rel err {err:.3e}"
+
+
+@pytest.mark.parametrize("M", [1, 16, 256, 4096])
+def test_full_size_w4a16(M):
+    w_ = wl.WORKLOADS["w4a16_dit"]
+    codes, zeros, scales = wl.int4_weight_parts(w_)
+    wq_np = {"scheme": "w4a16_asym", "role": "weight", "rows": w_.N, "cols": w_.K,
+             "codes": F.pack_int4(codes), "scales": scales, "zeros": zeros}
+    wq = pql.from_numpy(wq_np, DEV)
+    a_bits = wl.activation(w_, M)
+    c = pql.qlinear(up(a_bits), wq)
+    ra = _sample_rows(M, 48, 13)
+    rw = _sample_rows(w_.N, 128, 14, extra=range(w_.N - 4, w_.N))
+    w_rows = {k: (v[rw] if isinstance(v, np.ndarray) else v) for k, v in wq_np.items()}
+    w_rows["rows"] = len(rw)
+    ref = oracle.gemm_ref(np.ascontiguousarray(a_bits[ra]), w_rows)
+    got = F.bf16_to_f32(down_bf16(c)[np.ix_(ra, rw)])
+    err = oracle.rel_fro_error(got, ref)
+    assert err <= TOL, f"M={M}: rel err {err:.3e}"
+
+
+def test_full_size_int4_weight_quantizer():
+    w_ = wl.WORKLOADS["w4a16_dit"]
+    w_bits = wl.weight(w_)
+    q = pql.to_numpy(pql.quantize(up(w_bits), "w4a16_asym", "weight"))
+    rw = _sample_rows(w_.N, 128, 15)
+    _check_rows(w_bits, q, "w4a16_asym", "weight", rw)

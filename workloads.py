@@ -118,6 +118,16 @@ def int4_weight_parts(w: Workload):
     return codes, zeros, scales
 
 
+def pack_int4_codes(codes: np.ndarray) -> np.ndarray:
+    """Store generated int4 codes [R, K] in the canonical u32 layout [R, K/8]
+    (element k at bits 4*(k mod 8)), as a checkpoint loader would hand them over."""
+    c = np.asarray(codes, dtype=np.uint32).reshape(codes.shape[0], -1, 8)
+    out = np.zeros(c.shape[:2], dtype=np.uint32)
+    for j in range(8):
+        out |= (c[:, :, j] & 0xF) << np.uint32(4 * j)
+    return out
+
+
 def small_case(seed: int, rows: int, cols: int, std: float = 1.0) -> np.ndarray:
     """A small seeded bf16 tensor for parity cases that span several tiles."""
     return normal_bf16(seed, rows, cols, std)
