@@ -1,10 +1,13 @@
 // Block-scaled GEMM on gfx950 matrix cores: C[M, N] = A_hat * W_hat^T, bf16 out.
 //
-// A and W arrive as K-contiguous codes (e4m3fn bytes, or e2m1 pairs), which
-// is the operand order of v_mfma_scale_f32_16x16x128_f8f6f4: lane l feeds row
-// (l % 16) with the 32 consecutive K-elements starting at 32 * (l / 16), and
-// its scale byte is that row's e8m0 exponent for the same 32 elements.  The
-// accumulator lane l holds C[4 * (l / 16) + r][l % 16], r = 0..3.
+// A and W arrive as K-contiguous codes (e4m3fn bytes, or e2m1 pairs).  In
+// v_mfma_scale_f32_16x16x128_f8f6f4 lane l feeds row (l % 16); with g = l / 16
+// its operand holds, for fp4, the 32 K-elements 32 g .. 32 g + 31 (16 bytes),
+// and for fp8 the 16 K-elements 16 g .. 16 g + 15 in bytes 0-15 and
+// 64 + 16 g .. 64 + 16 g + 15 in bytes 16-31.  In both cases lane l's scale
+// byte is row (l % 16)'s e8m0 exponent for K-elements 32 g .. 32 g + 31.  (The
+// fp8 split was pinned with one-hot probes on the device.)  The accumulator
+// lane l holds C[4 * (l / 16) + r][l % 16], r = 0..3.
 //
 // Scale handling per scheme ("[vLLM] Other quantization: FP8, ModelOpt, INC,
 // TorchAO, Quark", section "FP8"; "vLLM-Omni Online Quantization complete
@@ -100,7 +103,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
 
   auto load_step = [&](int s) {
     const int kb0 = s * BKB;
-    const bool inside = kb0 + ld_c * 16 < Kb;             // false only in a half-filled last step
+    // only an fp4 operand with K % 256 == 128 has a half-filled last step
+    const bool inside = !T::kFp4 || kb0 + ld_c * 16 < Kb;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int off = ld_off + 32 * i * (int)Kb + kb0;
@@ -161,7 +165,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
   const int fr = lane & 15, fk = lane >> 4;   // fragment row and 32-element K slot
   for (int s = 0; s < nsteps; ++s) {
     const int stage = s & 1;
+    // Order of one step: issue the next step's global loads, run this step's
+    // MFMAs, then write the loaded tile to the other LDS buffer.  The
+    // scheduling barriers keep the compiler from hoisting those LDS writes
+    // (and their wait on the loads) above the MFMAs.
     if (s + 1 < nsteps) load_step(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
 
     const uint8_t* A = smem + stage * kStageBytes;
     const uint8_t* W = A + BM * BKB;
@@ -177,8 +186,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
           uint4 lo = *reinterpret_cast<const uint4*>(A + swz(r, 4 * h + fk));
           af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
         } else {
-          uint4 lo = *reinterpret_cast<const uint4*>(A + swz(r, 2 * fk));
-          uint4 hi = *reinterpret_cast<const uint4*>(A + swz(r, 2 * fk + 1));
+          uint4 lo = *reinterpret_cast<const uint4*>(A + swz(r, fk));
+          uint4 hi = *reinterpret_cast<const uint4*>(A + swz(r, 4 + fk));
           af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
       }
@@ -205,8 +214,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
           uint4 lo = *reinterpret_cast<const uint4*>(W + swz(c, 4 * h + fk));
           bf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
         } else {
-          uint4 lo = *reinterpret_cast<const uint4*>(W + swz(c, 2 * fk));
-          uint4 hi = *reinterpret_cast<const uint4*>(W + swz(c, 2 * fk + 1));
+          uint4 lo = *reinterpret_cast<const uint4*>(W + swz(c, fk));
+          uint4 hi = *reinterpret_cast<const uint4*>(W + swz(c, 4 + fk));
           bf = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         }
         int bsc = 127;
@@ -230,6 +239,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < nsteps) store_step(stage ^ 1);
     __syncthreads();
   }

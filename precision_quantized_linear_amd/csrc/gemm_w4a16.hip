@@ -132,6 +132,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_tile(const uint16_t* __restric
   for (int s = 0; s < nsteps; ++s) {
     const int stage = s & 1;
     if (s + 1 < nsteps) load_step(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* A = smem + stage * kStageBytes;
     const uint8_t* W = A + BM * BKB;
 #pragma unroll
@@ -147,6 +148,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_tile(const uint16_t* __restric
         for (int i = 0; i < 8; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf, acc[i][j], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (s + 1 < nsteps) store_step(stage ^ 1);
     __syncthreads();
   }

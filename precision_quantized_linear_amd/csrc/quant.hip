@@ -36,8 +36,9 @@ struct Fp8Div {
     rcp = __fdiv_rn(1.0f, s_);
     fast = s_ >= kSmallestFastScale;
   }
+  // The correction step turns -0 / s into +0; the quotient's sign is x's (s > 0).
   __device__ __forceinline__ float operator()(float x) const {
-    return fast ? div_rn_markstein(x, s, rcp) : __fdiv_rn(x, s);
+    return fast ? __builtin_copysignf(div_rn_markstein(x, s, rcp), x) : __fdiv_rn(x, s);
   }
 };
 
