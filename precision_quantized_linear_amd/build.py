@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpql.so")
-SOURCES = ("abi.cpp", "quant.hip", "gemm.hip", "gemm_w4a16.hip")
+SOURCES = ("abi.cpp", "quant.hip", "gemm.hip", "gemm32.hip", "gemm_w4a16.hip")
 ARCH = "gfx950"
 
 
@@ -33,7 +33,7 @@ def hipcc() -> str:
 def compile_flags():
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument",
+            "-Wno-unused-command-line-argument", "-Wno-inline-asm",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

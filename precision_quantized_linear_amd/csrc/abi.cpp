@@ -167,6 +167,7 @@ hipError_t do_qgemm(int scheme, const void* a, const void* a_scales, const void*
   g.K = K;
   g.c = static_cast<uint16_t*>(c);
   g.ldc = ldc;
+  g.vec_store = aligned16(c) && ldc % 8 == 0;
   pql::GemmKind kind = scheme == PQL_FP8_BLOCK128 ? pql::GEMM_FP8_BLOCK
                        : scheme == PQL_MXFP8      ? pql::GEMM_MXFP8
                        : scheme == PQL_MXFP4      ? pql::GEMM_MXFP4

@@ -297,7 +297,7 @@ hipError_t launch_kind(const GemmArgs& g, hipStream_t st) {
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st) {
   switch (kind) {
-    case GEMM_FP8_ROWSCALE: return launch_kind<GEMM_FP8_ROWSCALE>(g, st);
+    case GEMM_FP8_ROWSCALE: return launch_gemm32_fp8(g, st);
     case GEMM_FP8_BLOCK: return launch_kind<GEMM_FP8_BLOCK>(g, st);
     case GEMM_MXFP8: return launch_kind<GEMM_MXFP8>(g, st);
     case GEMM_MXFP4: return launch_kind<GEMM_MXFP4>(g, st);
@@ -307,7 +307,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st) {
 
 const char* gemm_kernel_name(GemmKind kind, int64_t, int64_t, int64_t) {
   switch (kind) {
-    case GEMM_FP8_ROWSCALE: return "k_gemm<fp8_rowscale>_256x256x128";
+    case GEMM_FP8_ROWSCALE: return "k_gemm32_fp8";
     case GEMM_FP8_BLOCK: return "k_gemm<fp8_block128>_256x256x128";
     case GEMM_MXFP8: return "k_gemm<mxfp8>_256x256x128";
     case GEMM_MXFP4: return "k_gemm<mxfp4>_256x256x256";

@@ -75,6 +75,8 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_tile(const uint16_t* __restric
   const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
   int tm, tn;
   tile_of_block(tiles_m, tiles_n, tm, tn);
+  tm = __builtin_amdgcn_readfirstlane(tm);   // computed with VALU division; keep it scalar so
+  tn = __builtin_amdgcn_readfirstlane(tn);   // the buffer descriptors live in SGPRs
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;

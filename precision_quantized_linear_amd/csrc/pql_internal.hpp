@@ -45,9 +45,12 @@ struct GemmArgs {
   int64_t M, N, K;
   uint16_t* c;             // bf16 [M, ldc]
   int64_t ldc;
+  int vec_store;           // 1 if c and ldc allow 16-byte row stores
 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st);
+// FP8 tensor / row scales on the four-stage 32x32x64 kernel
+hipError_t launch_gemm32_fp8(const GemmArgs& g, hipStream_t st);
 const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);
 
 // W4A16: C = A (bf16) * dequant(Wq)^T
