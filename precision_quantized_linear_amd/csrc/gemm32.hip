@@ -1,4 +1,4 @@
-// Deep-pipelined FP8 GEMM for the per-tensor / per-row scale schemes, gfx950.
+// Persistent FP8 GEMM for the per-tensor / per-row scale schemes, gfx950.
 //
 // C[M, N] = s_a[m] * s_w[n] * sum_k e4m3(a[m, k]) * e4m3(w[n, k]), bf16 out
 // ("[vLLM] Other quantization: FP8, ModelOpt, INC, TorchAO, Quark", section
@@ -6,36 +6,38 @@
 // scale is the token-wise rule applied to W's rows).
 //
 // Matrix core: v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales.  Lane l
-// feeds row (l % 32); with g = l / 32 its 32 operand bytes are K-elements
-// 16 g .. 16 g + 15 (bytes 0-15) and 32 + 16 g .. 32 + 16 g + 15 (bytes
-// 16-31) of a 64-element K block -- the same split as the 16x16x128 form,
-// pinned with one-hot probes on the device.  Accumulator register r of lane l
-// holds C[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+// feeds row (l % 32) of its operand; with g = l / 32 its 32 operand bytes are
+// K-elements 16 g .. 16 g + 15 (bytes 0-15) and 32 + 16 g .. 32 + 16 g + 15
+// (bytes 16-31) of a 64-element K slice -- pinned with one-hot probes on the
+// device.  The W fragment is the first operand and the A fragment the second,
+// so accumulator register r of lane l holds C[m = l % 32][n = 8 (r / 4) +
+// 4 (l / 32) + r % 4]: four consecutive output columns per register quad.
 //
-// Shape: one 256 x 256 output tile per workgroup of 4 waves (one per SIMD);
-// each wave owns a 128 x 128 quarter as 4 x 4 MFMA blocks (256 accumulators
-// per lane).  Large wave tiles keep LDS read traffic at 64 bytes per clock
-// per CU at the matrix-core peak (each wave reads 16 KB of operands per
-// 64-wide K step for 16 MFMAs).
+// Shape: one 256 x 256 output tile at a time per workgroup of 4 waves (one per
+// SIMD); each wave owns a 128 x 128 quarter as 4 x 4 MFMA blocks (256
+// accumulators per lane).  The grid is persistent (one workgroup per CU) and
+// each workgroup walks its tiles as one continuous stream of K slices.
 //
-// Pipeline: K advances 64 bytes per step; a stage (A and W tiles) is 32 KB
-// and four stages rotate through one 128 KB LDS array.  At step
-// s a wave
-//   1. waits for its own loads of stage s + 1 and for its LDS reads, then
-//      meets the other waves at s_barrier (after which stage s + 1 is
-//      complete and stage s, read during step s - 1, is free);
-//   2. refills stage s with step s + 4 (global -> LDS, buffer_load ... lds);
-//   3. issues the 16 MFMAs of step s on fragments already in registers,
-//      interleaved one-to-one with the 16 LDS reads that fetch step s + 1's
-//      fragments into the other register set.
-// Loads therefore run three steps ahead of their use, and LDS latency hides
-// behind the matrix core.  The direct-to-LDS loads are inline asm so that
-// the compiler does not order the LDS reads behind them (its alias tracking
-// cannot tell the stages of one LDS array apart); all waits on them are the
-// explicit vmcnt values below.  LDS rows are 64 bytes (four 16-byte chunks); chunk c of row
-// r sits at position c ^ ((r >> 1) & 3), which keeps each 8-lane group of a
-// fragment read on distinct banks.  Tiles are assigned XCD by XCD in 4 x 8
-// patches so that concurrent workgroups share A and W rows in L2.
+// Operands move global -> LDS with direct-to-LDS buffer loads, one full
+// 128-byte line per row and instruction (8 rows x 128 bytes per wave-wide
+// load): half-line loads cost about 40 % more L2 bandwidth, the limit of this
+// kernel.  A line holds two 64-byte K slices, so LDS holds operands in two
+// 64 KB regions, each with both slices of a K pair for all 256 A and 256 W
+// rows.  With slices numbered t over the whole stream and pair j = slices
+// (2 j, 2 j + 1) in region j % 2:
+//   * fragments of slice t are read from LDS while slice t - 1 computes, into
+//     the other of two register sets;
+//   * before odd slice 2 j + 1 the waves meet at a barrier, having waited for
+//     all their loads: pair j + 1 is then complete and region j % 2 (read up
+//     to slice 2 j) is free;
+//   * slice 2 j + 1 interleaves its 16 MFMAs with the 16 LDS reads of slice
+//     2 j + 2 and with the 16 loads of pair j + 2 into region j % 2.
+// Loads therefore have one to two slices to land.  The loads are inline asm:
+// the compiler's alias tracking cannot tell the regions of one LDS array
+// apart and would order every LDS read behind them; all waits on them are the
+// explicit counts below.  Rows are 128 bytes (eight 16-byte chunks); chunk c
+// of row r sits at position c ^ (r % 8), which keeps each 8-lane group of a
+// fragment read on distinct banks.
 #include <algorithm>
 
 #include "pql_device.hpp"
@@ -46,21 +48,23 @@ namespace pql {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BM = 256, BN = 256, BKB = 64;      // tile rows, cols, K bytes per step
-constexpr int kOpBytes = BM * BKB;               // one operand's tile per stage (16 KB)
-constexpr int kStageBytes = 2 * kOpBytes;        // A then W
+constexpr int BM = 256, BN = 256;
+constexpr int kSlice = 64;                       // K bytes per MFMA slice
+constexpr int kRow = 128;                        // K bytes per LDS row: one pair of slices
+constexpr int kOpBytes = BM * kRow;              // one operand's rows in a region (32 KB)
+constexpr int kRegionBytes = 2 * kOpBytes;       // A then W
+constexpr int kScaleBytes = 1024;                // per wave: 128 row scales, then 128 column scales
 constexpr int kGroupM = 4;
-constexpr int kLoadsPerStep = 8;                 // direct-to-LDS instructions per wave per step
-constexpr int kEpiBytes = 32 * 128 * 2;          // per wave: 32 output rows x 128 bf16
 constexpr int kPersistentCap = 256;              // one workgroup per CU
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt 6:4
 // left at its maximum, lgkmcnt in bits 11:8.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-__device__ __forceinline__ int swz64(int row, int chunk) { return row * BKB + ((chunk ^ ((row >> 1) & 3)) << 4); }
+__device__ __forceinline__ int swz128(int row, int chunk) { return row * kRow + ((chunk ^ (row & 7)) << 4); }
 
 // Persistent schedule.  Workgroup b runs on XCD b % 8 (dispatch is round-robin
 // over the XCDs).  Each XCD owns a contiguous range of the tile order, and its
@@ -103,7 +107,16 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, int nbytes) {
 // One direct-to-LDS load: 16 bytes per lane from rsrc + voff into LDS at lds + 16 * lane.
 __device__ __forceinline__ void lds_load16(v4i rsrc, const uint8_t* lds, int voff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff), "s"(rsrc)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff),
+               "s"(rsrc)
+               : "memory", "m0");
+}
+
+// One direct-to-LDS load of 4 bytes per lane: rsrc + voff into LDS at lds + 4 * lane.
+__device__ __forceinline__ void lds_load4(v4i rsrc, const uint8_t* lds, int voff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff),
+               "s"(rsrc)
                : "memory", "m0");
 }
 
@@ -113,8 +126,13 @@ __device__ __forceinline__ v8i cat(uint4 lo, uint4 hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * kStageBytes + 4 * kEpiBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kRegionBytes + 4 * kScaleBytes];
 
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   Sched sched;
@@ -126,22 +144,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int Kb = (int)g.K;
-  const int nsteps = Kb / BKB;
+  const int nsteps = Kb / kSlice;               // slices per tile (even: K % 128 == 0)
 
-  // ---- load stream.  Wave w moves A rows and W rows 64 w .. 64 w + 63 of a tile,
-  // 16 rows (1 KB) per instruction; lane i fetches chunk (i % 4) ^ f(row) of row
-  // i / 4 of the group, which lands at LDS offset 16 i.  Descriptors cover only
-  // the tile's valid rows, so rows past M / N (and offsets past the end) read 0.
-  // Loads run four steps ahead; the steps past a tile's end come from the next
-  // tile, whose descriptors are kept beside the current ones so the choice is a
-  // scalar select rather than a branch.  Past this workgroup's last tile the
-  // stream refetches its last tile into stages that are never read.
-  const int dl_row = wave * 64 + (lane >> 2);
-  const int dl_off = dl_row * Kb + (((lane & 3) ^ ((dl_row >> 1) & 3)) << 4);   // rows + 16 q keep f(row)
-  // A tile operand as a scalar (base, byte count) pair.  Each load gets a
-  // descriptor whose base is moved forward by the row group and K offset (and
-  // whose byte count shrinks by as much), so the per-lane offset is the one
-  // loop-invariant register dl_off and the loop writes no VGPR for its loads.
+  // ---- load stream.  Wave w moves A rows and W rows 64 w .. 64 w + 63 of a tile
+  // for one K pair, 8 rows per instruction: lane i fetches chunk (i % 8) ^ (i / 8)
+  // of row i / 8 of the group, which lands at LDS offset 16 i, the swizzled
+  // position.  Each load's descriptor starts at its row group and K pair and
+  // covers only the tile's valid rows (rows past M / N read 0), so the per-lane
+  // offset is the one loop-invariant register `voff`.  Pairs past a tile's end
+  // come from the next tile, whose (base, bytes) pairs are kept beside the
+  // current ones; past this workgroup's last tile the stream refetches its last
+  // tile into a region that is never read.
+  const int voff = (lane >> 3) * Kb + (((lane & 7) ^ (lane >> 3)) << 4);
   struct Span {
     uint64_t base;
     int bytes;
@@ -161,24 +175,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
   Span a_cur, w_cur, a_nxt, w_nxt;
   tile_spans(0, a_cur, w_cur);
   tile_spans(1, a_nxt, w_nxt);
-  // Load step `ls` (counted from the current tile's start) into stage `slot`.
-  auto issue = [&](int ls, int slot) {
+  // Load part `part` (0..15: row group part / 2 of A for even parts, of W for odd
+  // ones) of the pair starting at local slice `ls` (even; counted from the
+  // current tile's start) into region `region`.
+  auto issue_part = [&](int ls, int region, int part) {
     const bool here = ls < nsteps;
-    const Span as = here ? a_cur : a_nxt, ws = here ? w_cur : w_nxt;
-    const int koff = (here ? ls : ls - nsteps) * BKB + wave * 64 * Kb;
-    const uint8_t* stage = smem + (slot & 3) * kStageBytes + wave * 64 * BKB;
-    const int voff = dl_off - wave * 64 * Kb;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      lds_load16(rsrc_at(as, koff + 16 * q * Kb), stage + 16 * q * BKB, voff);
-      lds_load16(rsrc_at(ws, koff + 16 * q * Kb), stage + kOpBytes + 16 * q * BKB, voff);
-    }
+    const Span sp = (part & 1) ? (here ? w_cur : w_nxt) : (here ? a_cur : a_nxt);
+    const int rows = wave * 64 + 8 * (part >> 1);
+    const int off = (here ? ls : ls - nsteps) * kSlice + rows * Kb;
+    const uint8_t* dst = smem + (region & 1) * kRegionBytes + (part & 1) * kOpBytes + rows * kRow;
+    lds_load16(rsrc_at(sp, off), dst, voff);
   };
 
-  // Fragment offsets within a stage (blocks of 32 rows; rows + 32 i keep f(row)).
+  // Fragment offsets within a region: slice half h of the pair uses chunks
+  // 4 h + g and 4 h + 2 + g (g = lane / 32); rows + 32 i keep the swizzle.
   const int fr = lane & 31, fk = lane >> 5;
-  const int a_lo = swz64(wm * 128 + fr, fk), a_hi = swz64(wm * 128 + fr, 2 + fk);
-  const int w_lo = kOpBytes + swz64(wn * 128 + fr, fk), w_hi = kOpBytes + swz64(wn * 128 + fr, 2 + fk);
+  int a_off[2][2], w_off[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      a_off[h][q] = swz128(wm * 128 + fr, 4 * h + 2 * q + fk);
+      w_off[h][q] = kOpBytes + swz128(wn * 128 + fr, 4 * h + 2 * q + fk);
+    }
 
   v16f acc[4][4];
   auto zero_acc = [&]() {
@@ -192,111 +211,137 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
   zero_acc();
 
   uint4 fa0[4][2], fw0[4][2], fa1[4][2], fw1[4][2];   // two register sets of fragment halves
-  auto read_frags = [&](uint4 (&fa)[4][2], uint4 (&fw)[4][2], int slot) {
-    const uint8_t* stage = smem + (slot & 3) * kStageBytes;
+  auto read_frags = [&](uint4 (&fa)[4][2], uint4 (&fw)[4][2], const uint8_t* region, int h) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i][0] = lds16(stage + a_lo + i * 32 * BKB);
-      fa[i][1] = lds16(stage + a_hi + i * 32 * BKB);
-      fw[i][0] = lds16(stage + w_lo + i * 32 * BKB);
-      fw[i][1] = lds16(stage + w_hi + i * 32 * BKB);
-    }
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        fa[i][q] = lds16(region + a_off[h][q] + i * 32 * kRow);
+        fw[i][q] = lds16(region + w_off[h][q] + i * 32 * kRow);
+      }
   };
-  // The step's 16 MFMAs, each followed by one of the 16 LDS reads that fetch the
-  // next step's fragments (scheduling barriers pin this order).
-  auto mfmas_and_reads = [&](const uint4 (&fa)[4][2], const uint4 (&fw)[4][2], uint4 (&na)[4][2],
-                             uint4 (&nw)[4][2], const uint8_t* next_stage) {
+  // One slice: its 16 MFMAs, each followed by one of the 16 LDS reads that fetch
+  // the next slice's fragments (half h of `next_region`) and, for the first
+  // slice of a pair, by one of the 16 loads of the pair starting at local slice
+  // `ls` into `load_region` (scheduling barriers pin this order).
+  auto slice = [&](const uint4 (&fa)[4][2], const uint4 (&fw)[4][2], uint4 (&na)[4][2], uint4 (&nw)[4][2],
+                   const uint8_t* next_region, int h, bool loads, int ls, int load_region) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(fa[i][0], fa[i][1]), cat(fw[j][0], fw[j][1]),
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(fw[j][0], fw[j][1]), cat(fa[i][0], fa[i][1]),
                                                                     acc[i][j], 0, 0, 0, 127, 0, 127);
         __builtin_amdgcn_sched_barrier(0);
         const int k = j * 4 + i;
-        const int blk = (k >> 1) & 3, half = k & 1;
-        if (k < 8) na[blk][half] = lds16(next_stage + (half ? a_hi : a_lo) + blk * 32 * BKB);
-        else nw[blk][half] = lds16(next_stage + (half ? w_hi : w_lo) + blk * 32 * BKB);
+        const int blk = (k >> 1) & 3, q = k & 1;
+        if (k < 8) na[blk][q] = lds16(next_region + a_off[h][q] + blk * 32 * kRow);
+        else nw[blk][q] = lds16(next_region + w_off[h][q] + blk * 32 * kRow);
+        if (loads) issue_part(ls, load_region, k);
         __builtin_amdgcn_sched_barrier(0);
       }
   };
+  auto region_of = [&](int G) { return smem + ((G >> 1) & 1) * kRegionBytes; };   // slice G's pair region
+  auto barrier_all_loads = [&]() {
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  // ---- epilogue of tile k: scales, bf16, 16-byte row stores.  Each wave stages 32
-  // output rows at a time in its own 8 KB region (not part of the stage ring, which
-  // already holds the next tile's first steps).
-  uint16_t* ep = reinterpret_cast<uint16_t*>(smem + 4 * kStageBytes + wave * kEpiBytes);
-  const float* sa = static_cast<const float*>(g.a_scales);
-  const float* sw = static_cast<const float*>(g.w_scales);
+  // ---- scales.  Each wave keeps its 128 row and 128 column scales in its own
+  // 1 KB of LDS, fetched by direct-to-LDS loads right after the previous tile's
+  // epilogue; the next barrier's wait retires them.  Per-tensor scales have
+  // stride 0: every lane then reads the one scale.
+  uint8_t* scr = smem + 2 * kRegionBytes + wave * kScaleBytes;
+  const float* sc_rows = reinterpret_cast<const float*>(scr);
+  const float* sc_cols = sc_rows + 128;
+  auto prefetch_scales = [&](int k) {
+    int tm, tn;
+    sched.coords(std::min(k, my_tiles - 1), tm, tn);
+    const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane(tm) * BM + wm * 128;
+    const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(tn) * BN + wn * 128;
+    const int64_t sa_first = g.a_scale_stride ? m0 : 0, sw_first = g.w_scale_stride ? n0 : 0;
+    const int64_t sa_rows = g.a_scale_stride ? std::max<int64_t>(0, std::min<int64_t>(128, g.M - m0)) : 1;
+    const int64_t sw_rows = g.w_scale_stride ? std::max<int64_t>(0, std::min<int64_t>(128, g.N - n0)) : 1;
+    const v4i ra = make_rsrc(static_cast<const float*>(g.a_scales) + sa_first, (int)(sa_rows * 4));
+    const v4i rw = make_rsrc(static_cast<const float*>(g.w_scales) + sw_first, (int)(sw_rows * 4));
+    const int va = (int)g.a_scale_stride * lane * 4, vw = (int)g.w_scale_stride * lane * 4;
+    lds_load4(ra, scr, va);
+    lds_load4(ra, scr + 256, va + (int)g.a_scale_stride * 256);
+    lds_load4(rw, scr + 512, vw);
+    lds_load4(rw, scr + 768, vw + (int)g.w_scale_stride * 256);
+  };
+
+  // ---- epilogue of tile k: each lane owns output row m = 32 i + l % 32 of block
+  // i and, per accumulator quad, four consecutive columns: scale, round to bf16,
+  // store 8 bytes (the two lane halves of a row fill 16 contiguous bytes).
   auto epilogue = [&](int k) {
     int tm, tn;
     sched.coords(k, tm, tn);
     const int64_t m0 = (int64_t)tm * BM + wm * 128, n0 = (int64_t)tn * BN + wn * 128;
-    float cs[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cs[j] = sw[std::min<int64_t>(n0 + j * 32 + fr, g.N - 1) * g.w_scale_stride];
-    const int64_t col0 = n0 + (lane & 15) * 8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int64_t row = m0 + i * 32 + fr;
+      const float rs = sc_rows[i * 32 + fr];
+      uint16_t* dst_row = g.c + row * g.ldc;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = 8 * (r >> 2) + 4 * fk + (r & 3);
-        const float rs = sa[std::min<int64_t>(m0 + i * 32 + lr, g.M - 1) * g.a_scale_stride];
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ep[lr * 128 + j * 32 + fr] = (uint16_t)f32_to_bf16_rne(acc[i][j][r] * rs * cs[j]);
-      }
+        for (int rq = 0; rq < 4; ++rq) {
+          const int cl = j * 32 + rq * 8 + fk * 4;
+          const float4 cs = *reinterpret_cast<const float4*>(sc_cols + cl);
+          const uint32_t lo = pack_bf16x2(acc[i][j][4 * rq + 0] * rs * cs.x, acc[i][j][4 * rq + 1] * rs * cs.y);
+          const uint32_t hi = pack_bf16x2(acc[i][j][4 * rq + 2] * rs * cs.z, acc[i][j][4 * rq + 3] * rs * cs.w);
+          const int64_t col = n0 + cl;
+          if (row < g.M) {
+            if (g.vec_store && col + 4 <= g.N) {
+              *reinterpret_cast<uint2*>(dst_row + col) = uint2{lo, hi};
+            } else {
+              const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int lr = q * 4 + (lane >> 4);
-        const int64_t row = m0 + i * 32 + lr;
-        const uint4 v = *reinterpret_cast<const uint4*>(ep + lr * 128 + (lane & 15) * 8);
-        if (row >= g.M) continue;
-        uint16_t* dst = g.c + row * g.ldc + col0;
-        if (g.vec_store && col0 + 8 <= g.N) {
-          *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-          const uint16_t e[8] = {(uint16_t)v.x, (uint16_t)(v.x >> 16), (uint16_t)v.y, (uint16_t)(v.y >> 16),
-                                 (uint16_t)v.z, (uint16_t)(v.z >> 16), (uint16_t)v.w, (uint16_t)(v.w >> 16)};
-#pragma unroll
-          for (int e8 = 0; e8 < 8; ++e8)
-            if (col0 + e8 < g.N) dst[e8] = e[e8];
+              for (int c = 0; c < 4; ++c)
+                if (col + c < g.N) dst_row[col + c] = e[c];
+            }
+          }
         }
-      }
     }
     zero_acc();
   };
 
-  // ---- prologue: steps 0..3 in flight; wait for stage 0 and read step 0's fragments.
+  // ---- prologue: pairs 0 and 1 in flight, then slice 0's fragments.
 #pragma unroll
-  for (int s = 0; s < 4; ++s) issue(s, s);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsPerStep, 0));
+  for (int part = 0; part < 16; ++part) issue_part(0, 0, part);
+#pragma unroll
+  for (int part = 0; part < 16; ++part) issue_part(2, 1, part);
+  prefetch_scales(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(16 + 4, 0));   // pair 0 landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_frags(fa0, fw0, 0);
+  read_frags(fa0, fw0, smem, 0);
 
-  // ---- step s of the current tile (G counts steps over all tiles): fragments of
-  // the step are in (fa, fw); stage G % 4 was read at step G - 1 and is refilled
-  // with the load four steps ahead.  The look-ahead reads of the very last step
-  // fetch a stage whose values are never used.  nsteps is even (K % 128 == 0), so
-  // tiles end after the second step of a pair.
-  auto step = [&](int s, int G, const uint4 (&fa)[4][2], const uint4 (&fw)[4][2], uint4 (&na)[4][2],
-                  uint4 (&nw)[4][2]) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerStep, 0));   // stage G + 1 complete
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue(s + 4, G);
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas_and_reads(fa, fw, na, nw, smem + ((G + 1) & 3) * kStageBytes);
-  };
+  // ---- the stream.  G counts slices over all tiles; nsteps is even, so a
+  // tile's slice s has the parity of G, even slices use register set 0 and odd
+  // slices set 1, and a tile ends with the first slice of a pair.
   int G = 0;
   for (int k = 0; k < my_tiles; ++k) {
-    for (int s = 0; s < nsteps; s += 2, G += 2) {
-      step(s, G, fa0, fw0, fa1, fw1);
-      step(s + 1, G + 1, fa1, fw1, fa0, fw0);
+    slice(fa0, fw0, fa1, fw1, region_of(G), 1, false, 0, 0);                 // s = 0
+    int s = 1;
+    for (; s < nsteps - 1; s += 2) {
+      barrier_all_loads();
+      slice(fa1, fw1, fa0, fw0, region_of(G + s + 1), 0, true, s + 3, (G + s) >> 1);
+      slice(fa0, fw0, fa1, fw1, region_of(G + s + 1), 1, false, 0, 0);
     }
+    barrier_all_loads();
+    slice(fa1, fw1, fa0, fw0, region_of(G + s + 1), 0, true, s + 3, (G + s) >> 1);   // s = nsteps - 1
+    G += nsteps;
     epilogue(k);
     a_cur = a_nxt;
     w_cur = w_nxt;
     tile_spans(k + 2, a_nxt, w_nxt);
+    // The epilogue's LDS reads of the scales are done before the next tile's
+    // scales may overwrite them.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    prefetch_scales(k + 1);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
@@ -305,10 +350,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
 
 hipError_t launch_gemm32_fp8(const GemmArgs& g, hipStream_t st) {
   const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
-  // The load stream runs four K steps ahead, which stays within the next tile
-  // only when a tile has at least four steps; shorter K gets one tile per
-  // workgroup (its look-ahead loads then land in stages that are never read).
-  const int grid = (g.K / BKB >= 4) ? std::min(tiles, kPersistentCap) : tiles;
+  // The load stream runs one pair (two slices) ahead into the next tile, which
+  // is the next tile's own first pair only when a tile has at least two pairs;
+  // K = 128 gets one tile per workgroup (its look-ahead loads then land in a
+  // region that is never read).
+  const int grid = (g.K / kRow >= 2) ? std::min(tiles, kPersistentCap) : tiles;
   hipLaunchKernelGGL(k_gemm32_fp8, dim3(grid), dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
