@@ -54,6 +54,9 @@ constexpr int kRow = 128;                        // K bytes per LDS row: one pai
 constexpr int kOpBytes = BM * kRow;              // one operand's rows in a region (32 KB)
 constexpr int kRegionBytes = 2 * kOpBytes;       // A then W
 constexpr int kScaleBytes = 1024;                // per wave: 128 row scales, then 128 column scales
+constexpr int kEpiRow = 136;                     // staged output row: 64 bf16 + 8 bytes of padding
+constexpr int kEpiBytes = 32 * kEpiRow;          // per wave: 32 output rows staged for row stores
+constexpr int kWaveBytes = kScaleBytes + kEpiBytes;
 constexpr int kGroupM = 4;
 constexpr int kPersistentCap = 256;              // one workgroup per CU
 
@@ -132,7 +135,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kRegionBytes + 4 * kScaleBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kRegionBytes + 4 * kWaveBytes];
 
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   Sched sched;
@@ -199,16 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
       w_off[h][q] = kOpBytes + swz128(wn * 128 + fr, 4 * h + 2 * q + fk);
     }
 
-  v16f acc[4][4];
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  };
-  zero_acc();
+  v16f acc[4][4];   // each tile's first slice starts the sums from zero
 
   uint4 fa0[4][2], fw0[4][2], fa1[4][2], fw1[4][2];   // two register sets of fragment halves
   auto read_frags = [&](uint4 (&fa)[4][2], uint4 (&fw)[4][2], const uint8_t* region, int h) {
@@ -225,18 +219,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
   // slice of a pair, by one of the 16 loads of the pair starting at local slice
   // `ls` into `load_region` (scheduling barriers pin this order).
   auto slice = [&](const uint4 (&fa)[4][2], const uint4 (&fw)[4][2], uint4 (&na)[4][2], uint4 (&nw)[4][2],
-                   const uint8_t* next_region, int h, bool loads, int ls, int load_region) {
+                   const uint8_t* next_region, int h, bool loads, int ls, int load_region, bool reads = true,
+                   bool first = false) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(fw[j][0], fw[j][1]), cat(fa[i][0], fa[i][1]),
-                                                                    acc[i][j], 0, 0, 0, 127, 0, 127);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            cat(fw[j][0], fw[j][1]), cat(fa[i][0], fa[i][1]), first ? v16f{} : acc[i][j], 0, 0, 0, 127, 0, 127);
         __builtin_amdgcn_sched_barrier(0);
         const int k = j * 4 + i;
         const int blk = (k >> 1) & 3, q = k & 1;
-        if (k < 8) na[blk][q] = lds16(next_region + a_off[h][q] + blk * 32 * kRow);
-        else nw[blk][q] = lds16(next_region + w_off[h][q] + blk * 32 * kRow);
+        if (reads) {
+          if (k < 8) na[blk][q] = lds16(next_region + a_off[h][q] + blk * 32 * kRow);
+          else nw[blk][q] = lds16(next_region + w_off[h][q] + blk * 32 * kRow);
+        }
         if (loads) issue_part(ls, load_region, k);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -252,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
   // 1 KB of LDS, fetched by direct-to-LDS loads right after the previous tile's
   // epilogue; the next barrier's wait retires them.  Per-tensor scales have
   // stride 0: every lane then reads the one scale.
-  uint8_t* scr = smem + 2 * kRegionBytes + wave * kScaleBytes;
+  uint8_t* scr = smem + 2 * kRegionBytes + wave * kWaveBytes;
   const float* sc_rows = reinterpret_cast<const float*>(scr);
   const float* sc_cols = sc_rows + 128;
   auto prefetch_scales = [&](int k) {
@@ -279,6 +276,51 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
     int tm, tn;
     sched.coords(k, tm, tn);
     const int64_t m0 = (int64_t)tm * BM + wm * 128, n0 = (int64_t)tn * BN + wn * 128;
+    const bool interior = g.vec_store && m0 + 128 <= g.M && n0 + 128 <= g.N;   // wave-uniform
+    if (interior) {
+      // The wave's 128 x 128 quarter is inside C.  Rows go out through LDS so
+      // that each store writes whole 128-byte lines: per 32-row block i and
+      // 64-column half p, lanes write their scaled bf16 quads (8 bytes) into a
+      // 32-row staging block, then read it back as 16-byte row pieces (8 lanes
+      // per row, 8 rows per instruction).  Staged rows are padded to 136 bytes,
+      // which keeps both the quad writes and the row reads on distinct banks
+      // with constant offsets from one per-lane address.
+      uint8_t* stg = scr + kScaleBytes;
+      const float4* cs4 = static_cast<const float4*>(__builtin_assume_aligned(sc_cols, 16));
+      const int rr = lane >> 3, rc = lane & 7;             // read-back: row rr + 8 q, 16-byte piece rc
+      uint8_t* wr = stg + fr * kEpiRow + fk * 8;
+      const uint8_t* rd = stg + rr * kEpiRow + rc * 16;
+      const uint32_t voff = (uint32_t)(rr * g.ldc * 2 + rc * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float rs = sc_rows[i * 32 + fr];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * p + jj;
+            float4 cs[4];
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) cs[rq] = cs4[j * 8 + rq * 2 + fk];
+            const v16f a = acc[i][j];
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq)
+              *reinterpret_cast<uint2*>(wr + (jj * 8 + rq * 2) * 8) =
+                  uint2{pack_bf16x2(a[4 * rq + 0] * rs * cs[rq].x, a[4 * rq + 1] * rs * cs[rq].y),
+                        pack_bf16x2(a[4 * rq + 2] * rs * cs[rq].z, a[4 * rq + 3] * rs * cs[rq].w)};
+            __builtin_amdgcn_sched_barrier(0);   // one accumulator block at a time
+          }
+#pragma unroll
+          for (int qr = 0; qr < 4; ++qr) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow + 8);
+            char* base = reinterpret_cast<char*>(g.c + (m0 + i * 32 + 8 * qr) * g.ldc + n0 + p * 64);
+            *reinterpret_cast<uint4*>(base + voff) = uint4{lo.x, lo.y, hi.x, hi.y};
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = m0 + i * 32 + fr;
@@ -305,7 +347,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
           }
         }
     }
-    zero_acc();
   };
 
   // ---- prologue: pairs 0 and 1 in flight, then slice 0's fragments.
@@ -324,17 +365,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
   // slices set 1, and a tile ends with the first slice of a pair.
   int G = 0;
   for (int k = 0; k < my_tiles; ++k) {
-    slice(fa0, fw0, fa1, fw1, region_of(G), 1, false, 0, 0);                 // s = 0
+    slice(fa0, fw0, fa1, fw1, region_of(G), 1, false, 0, 0, true, true);     // s = 0 starts the sums
     int s = 1;
     for (; s < nsteps - 1; s += 2) {
       barrier_all_loads();
       slice(fa1, fw1, fa0, fw0, region_of(G + s + 1), 0, true, s + 3, (G + s) >> 1);
       slice(fa0, fw0, fa1, fw1, region_of(G + s + 1), 1, false, 0, 0);
     }
+    // s = nsteps - 1: the next tile's first fragments are read after the
+    // epilogue, which keeps their registers free while it runs.
     barrier_all_loads();
-    slice(fa1, fw1, fa0, fw0, region_of(G + s + 1), 0, true, s + 3, (G + s) >> 1);   // s = nsteps - 1
+    slice(fa1, fw1, fa0, fw0, region_of(G + s + 1), 0, true, s + 3, (G + s) >> 1, false);
     G += nsteps;
     epilogue(k);
+    read_frags(fa0, fw0, region_of(G), 0);
     a_cur = a_nxt;
     w_cur = w_nxt;
     tile_spans(k + 2, a_nxt, w_nxt);
