@@ -23,56 +23,95 @@ namespace {
 
 constexpr float kSmallestFastScale = 0x1p-80f;
 
+// ---------------------------------------------------------------- geometry
+// Chunk-parallel kernels use row segments: a workgroup is 4 waves, wave w works
+// on row 4 * blockIdx.x + w and lane l on chunks (8 bf16 = 16 bytes)
+// 64 U blockIdx.y + 64 u + l, u < U, of that row.  No index division, and
+// every wave-wide load is 1 KB of one row.  Scale groups (4, 16 or 64 lanes)
+// never straddle a 64-chunk slice because K is a multiple of the group.
+constexpr int kSegU = 2;
+struct Seg {
+  int64_t row;
+  int lane;
+  int64_t c0;   // first chunk of this lane (add 64 u)
+  __device__ __forceinline__ Seg() {
+    lane = threadIdx.x & 63;
+    row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    c0 = (int64_t)blockIdx.y * 64 * kSegU + lane;
+  }
+};
+inline dim3 seg_grid(int64_t rows, int64_t cols) {
+  const int64_t cpr = cols >> 3;
+  return dim3((unsigned)((rows + 3) / 4), (unsigned)((cpr + 64 * kSegU - 1) / (64 * kSegU)));
+}
+
+// ---------------------------------------------------------------- FP8 casts
 // fp32 scale of the FP8 schemes: s = fp32(amax / 448), 1 if that is 0.
 __device__ __forceinline__ float fp8_scale(float amax) {
   float s = __fdiv_rn(amax, 448.0f);
   return s == 0.0f ? 1.0f : s;
 }
 
-struct Fp8Div {
-  float s, rcp;
-  bool fast;
-  __device__ __forceinline__ explicit Fp8Div(float s_) : s(s_) {
-    rcp = __fdiv_rn(1.0f, s_);
-    fast = s_ >= kSmallestFastScale;
-  }
-  // The correction step turns -0 / s into +0; the quotient's sign is x's (s > 0).
-  __device__ __forceinline__ float operator()(float x) const {
-    return fast ? __builtin_copysignf(div_rn_markstein(x, s, rcp), x) : __fdiv_rn(x, s);
-  }
-};
+// fp32(x / s), correctly rounded.  FAST (s >= 2^-80): one reciprocal per
+// scale and a Markstein correction per element; the correction turns -0 / s
+// into +0, so the sign is taken from x (s > 0).
+template <bool FAST>
+__device__ __forceinline__ float quot(float x, float s, float rcp) {
+  if constexpr (FAST) return __builtin_copysignf(div_rn_markstein(x, s, rcp), x);
+  else return __fdiv_rn(x, s);
+}
+
+// Four fp32 values -> four e4m3fn codes (byte j = value j) with the hardware
+// convert, which rounds to nearest even and keeps the sign of zero.  It agrees
+// with the saturating definition for every |v| < 464 (checked on the device for
+// all fp32 values) and returns NaN above: FP8 quotients are at most
+// 448 (1 + 2^-24) by construction, MX callers clamp to +-448 first.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
 
 // 8 bf16 -> 8 e4m3fn codes of fp32(x / s).
-__device__ __forceinline__ uint2 fp8_chunk(uint4 c, const Fp8Div& d) {
+template <bool FAST>
+__device__ __forceinline__ uint2 fp8_chunk(uint4 c, float s, float rcp) {
   float f[8];
   chunk_to_f32(c, f);
-  uint32_t b[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) b[j] = e4m3_encode(d(f[j]));
-  return make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                    b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24));
+  for (int j = 0; j < 8; ++j) f[j] = quot<FAST>(f[j], s, rcp);
+  return make_uint2(fp8x4(f[0], f[1], f[2], f[3]), fp8x4(f[4], f[5], f[6], f[7]));
 }
 
 // ---------------------------------------------------------------- per tensor
-// Pass 1: partial[b] = max |x| over the chunks block b visits.
+// Pass 1: partial[b] = max |x| over the row segments workgroup b visits.
 __global__ __launch_bounds__(256) void k_amax_partial(const uint16_t* __restrict__ x, int64_t rows,
                                                       int64_t cols, int64_t ldx,
                                                       float* __restrict__ partial) {
   const int64_t cpr = cols >> 3;
-  const int64_t total = rows * cpr;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t segs = (cpr + 63) >> 6;
+  const int64_t units = rows * segs;         // (row, 64-chunk segment) pairs
   float m = 0.0f;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    int64_t r = i / cpr, c = i - r * cpr;
-    m = fmaxf(m, chunk_absmax(ldg16(x + r * ldx + c * 8)));
+  for (int64_t u = (int64_t)blockIdx.x * 4 + wave; u < units; u += (int64_t)gridDim.x * 4) {
+    const int64_t r = u / segs, c = (u - r * segs) * 64 + lane;
+    if (c < cpr) m = fmaxf(m, chunk_absmax(ldg16(x + r * ldx + c * 8)));
   }
   m = wave_max(m);
   __shared__ float red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  if (lane == 0) red[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// Pass 2: every block folds the partials into amax, then quantizes its chunks.
+// Pass 2: every workgroup folds the partials into amax, then quantizes its segment.
+template <bool FAST>
+__device__ __forceinline__ void fp8_tensor_seg(const Seg& g, const uint16_t* xr, uint8_t* cr, int64_t cpr,
+                                               float s, float rcp) {
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    if (c < cpr) stg8(cr + c * 8, fp8_chunk<FAST>(ldg16(xr + c * 8), s, rcp));
+  }
+}
 __global__ __launch_bounds__(256) void k_fp8_tensor(const uint16_t* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t ldx,
                                                     const float* __restrict__ partial, int npartial,
@@ -84,21 +123,34 @@ __global__ __launch_bounds__(256) void k_fp8_tensor(const uint16_t* __restrict__
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const Fp8Div d(fp8_scale(amax));
-  if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = d.s;
+  const float s = fp8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) scale[0] = s;
+  const Seg g;
+  if (g.row >= rows) return;
   const int64_t cpr = cols >> 3;
-  const int64_t total = rows * cpr;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    int64_t r = i / cpr, c = i - r * cpr;
-    stg8(codes + r * cols + c * 8, fp8_chunk(ldg16(x + r * ldx + c * 8), d));
-  }
+  const uint16_t* xr = x + g.row * ldx;
+  uint8_t* cr = codes + g.row * cols;
+  if (s >= kSmallestFastScale) fp8_tensor_seg<true>(g, xr, cr, cpr, s, __fdiv_rn(1.0f, s));
+  else fp8_tensor_seg<false>(g, xr, cr, cpr, s, 0.0f);
 }
 
 // ---------------------------------------------------------------- per row
 // One wave per row.  CH > 0: the row (at most 64*CH chunks) stays in
 // registers between the max and the cast.  CH == 0: rows too long for that
 // are read twice.
+template <int CH, bool FAST>
+__device__ __forceinline__ void fp8_row_cast(const uint4 (&c)[CH > 0 ? CH : 1], const uint16_t* xr, uint8_t* cr,
+                                             int nch, int lane, float s, float rcp) {
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int ch = i * 64 + lane;
+      if (ch < nch) stg8(cr + ch * 8, fp8_chunk<FAST>(c[i], s, rcp));
+    }
+  } else {
+    for (int ch = lane; ch < nch; ch += 64) stg8(cr + ch * 8, fp8_chunk<FAST>(ldg16(xr + ch * 8), s, rcp));
+  }
+}
 template <int CH>
 __global__ __launch_bounds__(256) void k_fp8_row(const uint16_t* __restrict__ x, int64_t rows,
                                                  int64_t cols, int64_t ldx,
@@ -110,52 +162,61 @@ __global__ __launch_bounds__(256) void k_fp8_row(const uint16_t* __restrict__ x,
   const uint16_t* xr = x + row * ldx;
   uint8_t* cr = codes + row * cols;
   const int nch = (int)(cols >> 3);
+  uint4 c[CH > 0 ? CH : 1];
+  float m = 0.0f;
   if constexpr (CH > 0) {
-    uint4 c[CH];
-    float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int ch = i * 64 + lane;
-      if (ch < nch) {
-        c[i] = ldg16(xr + ch * 8);
-        m = fmaxf(m, chunk_absmax(c[i]));
-      }
-    }
-    const Fp8Div d(fp8_scale(wave_max(m)));
-    if (lane == 0) scales[row] = d.s;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int ch = i * 64 + lane;
-      if (ch < nch) stg8(cr + ch * 8, fp8_chunk(c[i], d));
+      c[i] = ch < nch ? ldg16(xr + ch * 8) : make_uint4(0, 0, 0, 0);
+      m = fmaxf(m, chunk_absmax(c[i]));
     }
   } else {
-    float m = 0.0f;
     for (int ch = lane; ch < nch; ch += 64) m = fmaxf(m, chunk_absmax(ldg16(xr + ch * 8)));
-    const Fp8Div d(fp8_scale(wave_max(m)));
-    if (lane == 0) scales[row] = d.s;
-    for (int ch = lane; ch < nch; ch += 64) stg8(cr + ch * 8, fp8_chunk(ldg16(xr + ch * 8), d));
   }
+  const float s = fp8_scale(wave_max(m));
+  if (lane == 0) scales[row] = s;
+  if (s >= kSmallestFastScale) fp8_row_cast<CH, true>(c, xr, cr, nch, lane, s, __fdiv_rn(1.0f, s));
+  else fp8_row_cast<CH, false>(c, xr, cr, nch, lane, s, 0.0f);
 }
 
 // ---------------------------------------------------------------- 1x128 groups
-// One chunk per thread; the 16 chunks of a group sit in one 16-lane DPP row.
+// Row segments; the 16 chunks of a group sit in one 16-lane DPP row.
 __global__ __launch_bounds__(256) void k_fp8_block_act(const uint16_t* __restrict__ x, int64_t rows,
                                                        int64_t cols, int64_t ldx,
                                                        uint8_t* __restrict__ codes,
                                                        float* __restrict__ scales) {
+  const Seg g;
+  if (g.row >= rows) return;
   const int64_t cpr = cols >> 3;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = i < rows * cpr;      // whole groups are valid or invalid together
-  const int64_t r = valid ? i / cpr : 0, c = valid ? i - r * cpr : 0;
-  uint4 v = valid ? ldg16(x + r * ldx + c * 8) : make_uint4(0, 0, 0, 0);
-  const Fp8Div d(fp8_scale(group16_max(chunk_absmax(v))));
-  if (!valid) return;
-  if ((c & 15) == 0) scales[r * (cols >> 7) + (c >> 4)] = d.s;
-  stg8(codes + r * cols + c * 8, fp8_chunk(v, d));
+  const uint16_t* xr = x + g.row * ldx;
+  uint4 v[kSegU];
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    v[u] = c < cpr ? ldg16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    const float s = fp8_scale(group16_max(chunk_absmax(v[u])));   // whole groups are in or out of range
+    if (c >= cpr) continue;
+    if ((c & 15) == 0) scales[g.row * (cols >> 7) + (c >> 4)] = s;
+    uint2 q;
+    if (s >= kSmallestFastScale) q = fp8_chunk<true>(v[u], s, __fdiv_rn(1.0f, s));
+    else q = fp8_chunk<false>(v[u], s, 0.0f);
+    stg8(codes + g.row * cols + c * 8, q);
+  }
 }
 
 // ---------------------------------------------------------------- 128x128 blocks
 // One workgroup per block: thread t owns chunk (t % 16) of rows t/16 + 16 j.
+template <bool FAST>
+__device__ __forceinline__ void fp8_block_wt_cast(const uint4 (&v)[8], uint8_t* cb, int64_t cols, int r0, float s,
+                                                  float rcp) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) stg8(cb + (int64_t)(r0 + 16 * j) * cols, fp8_chunk<FAST>(v[j], s, rcp));
+}
 __global__ __launch_bounds__(256) void k_fp8_block_wt(const uint16_t* __restrict__ x, int64_t cols,
                                                       int64_t ldx, uint8_t* __restrict__ codes,
                                                       float* __restrict__ scales) {
@@ -174,90 +235,119 @@ __global__ __launch_bounds__(256) void k_fp8_block_wt(const uint16_t* __restrict
   __shared__ float red[4];
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
-  const Fp8Div d(fp8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
-  if (t == 0) scales[blockIdx.x] = d.s;
+  const float s = fp8_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  if (t == 0) scales[blockIdx.x] = s;
   uint8_t* cb = codes + (rb * 128) * cols + kb * 128 + cc * 8;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) stg8(cb + (int64_t)(r0 + 16 * j) * cols, fp8_chunk(v[j], d));
+  if (s >= kSmallestFastScale) fp8_block_wt_cast<true>(v, cb, cols, r0, s, __fdiv_rn(1.0f, s));
+  else fp8_block_wt_cast<false>(v, cb, cols, r0, s, 0.0f);
 }
 
 // ---------------------------------------------------------------- MX
-// One chunk per thread; the 4 chunks of a 32-element block share a DPP quad.
+// Row segments; the 4 chunks of a 32-element block share a DPP quad.  The
+// scaling x * 2^-X is exact; e4m3 values in (448, 512) saturate (clamped before
+// the hardware convert), e2m1 values above 6 saturate in the convert itself
+// (which agrees with the definition for every fp32 value at unit scale).
 template <bool FP4>
 __global__ __launch_bounds__(256) void k_mx(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                             int64_t ldx, uint8_t* __restrict__ codes,
                                             uint8_t* __restrict__ scales) {
+  const Seg g;
+  if (g.row >= rows) return;
   const int64_t cpr = cols >> 3;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = i < rows * cpr;
-  const int64_t r = valid ? i / cpr : 0, c = valid ? i - r * cpr : 0;
-  uint4 v = valid ? ldg16(x + r * ldx + c * 8) : make_uint4(0, 0, 0, 0);
-  const int X = mx_shared_exponent(group4_max(chunk_absmax(v)), FP4 ? 2 : 8);
-  if (!valid) return;
-  if ((c & 3) == 0) scales[r * (cols >> 5) + (c >> 2)] = (uint8_t)(X + 127);
-  const float inv = exp2i(-X);             // exact scaling: x * 2^-X
-  float f[8];
-  chunk_to_f32(v, f);
-  if constexpr (FP4) {
-    uint32_t w = 0;
+  const uint16_t* xr = x + g.row * ldx;
+  uint4 v[kSegU];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) w |= e2m1_encode(f[j] * inv) << (4 * j);
-    *reinterpret_cast<uint32_t*>(codes + r * (cols >> 1) + c * 4) = w;
-  } else {
-    uint32_t b[8];
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    v[u] = c < cpr ? ldg16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+  }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = e4m3_encode(f[j] * inv);
-    stg8(codes + r * cols + c * 8, make_uint2(b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                                              b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)));
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    const int X = mx_shared_exponent(group4_max(chunk_absmax(v[u])), FP4 ? 2 : 8);
+    if (c >= cpr) continue;
+    if ((c & 3) == 0) scales[g.row * (cols >> 5) + (c >> 2)] = (uint8_t)(X + 127);
+    const float inv = exp2i(-X);
+    float f[8];
+    chunk_to_f32(v[u], f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] *= inv;
+    if constexpr (FP4) {
+      uint32_t w = 0;
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0], f[1], 1.0f, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], 1.0f, 1);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], 1.0f, 2);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], 1.0f, 3);
+      *reinterpret_cast<uint32_t*>(codes + g.row * (cols >> 1) + c * 4) = w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = __builtin_amdgcn_fmed3f(f[j], -448.0f, 448.0f);
+      stg8(codes + g.row * cols + c * 8, make_uint2(fp8x4(f[0], f[1], f[2], f[3]), fp8x4(f[4], f[5], f[6], f[7])));
+    }
   }
 }
 
 // ---------------------------------------------------------------- int4 round-to-nearest
-// One chunk (= one u32 of codes) per thread; a 128-group is a 16-lane DPP row.
+// Row segments; a 128-group is a 16-lane DPP row.  One chunk = one u32 of codes.
 template <bool SYM>
 __global__ __launch_bounds__(256) void k_int4(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
                                               int64_t ldx, uint32_t* __restrict__ codes,
                                               uint16_t* __restrict__ scales,
                                               uint8_t* __restrict__ zeros) {
+  const Seg g;
+  if (g.row >= rows) return;
   const int64_t cpr = cols >> 3;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool valid = i < rows * cpr;
-  const int64_t r = valid ? i / cpr : 0, c = valid ? i - r * cpr : 0;
-  uint4 v = valid ? ldg16(x + r * ldx + c * 8) : make_uint4(0, 0, 0, 0);
-  float f[8];
-  chunk_to_f32(v, f);
-  float s, z;
-  if constexpr (SYM) {
-    const float amax = group16_max(chunk_absmax(v));
-    s = __uint_as_float(f32_to_bf16_rne(__fdiv_rn(amax, 7.0f)) << 16);
-    z = 8.0f;
-    if (s == 0.0f) s = 1.0f;
-  } else {
-    float lo = 0.0f, hi = 0.0f;
+  const uint16_t* xr = x + g.row * ldx;
+  uint4 v[kSegU];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { lo = fminf(lo, f[j]); hi = fmaxf(hi, f[j]); }
-    lo = group16_min(lo);
-    hi = group16_max(hi);
-    s = __uint_as_float(f32_to_bf16_rne(__fdiv_rn(hi - lo, 15.0f)) << 16);
-    if (s == 0.0f) {
-      s = 1.0f;
-      z = 0.0f;
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    v[u] = c < cpr ? ldg16(xr + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    float f[8];
+    chunk_to_f32(v[u], f);
+    float s, z;
+    if constexpr (SYM) {
+      const float amax = group16_max(chunk_absmax(v[u]));
+      s = __uint_as_float(f32_to_bf16_rne(__fdiv_rn(amax, 7.0f)) << 16);
+      z = 8.0f;
+      if (s == 0.0f) s = 1.0f;
     } else {
-      z = fminf(fmaxf(__builtin_rintf(__fdiv_rn(-lo, s)), 0.0f), 15.0f);
-    }
-  }
-  if (!valid) return;
-  uint32_t w = 0;
+      float lo = 0.0f, hi = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float q = fminf(fmaxf(__builtin_rintf(__fdiv_rn(f[j], s)) + z, 0.0f), 15.0f);
-    w |= (uint32_t)q << (4 * j);
-  }
-  codes[r * cpr + c] = w;
-  if ((c & 15) == 0) {
-    const int64_t g = r * (cols >> 7) + (c >> 4);
-    scales[g] = (uint16_t)(__float_as_uint(s) >> 16);
-    zeros[g] = (uint8_t)z;
+      for (int j = 0; j < 8; ++j) { lo = fminf(lo, f[j]); hi = fmaxf(hi, f[j]); }
+      lo = group16_min(lo);
+      hi = group16_max(hi);
+      s = __uint_as_float(f32_to_bf16_rne(__fdiv_rn(hi - lo, 15.0f)) << 16);
+      if (s == 0.0f) {
+        s = 1.0f;
+        z = 0.0f;
+      } else {
+        z = fminf(fmaxf(__builtin_rintf(__fdiv_rn(-lo, s)), 0.0f), 15.0f);
+      }
+    }
+    if (c >= cpr) continue;
+    float q[8];
+    if (s >= kSmallestFastScale) {
+      const float rcp = __fdiv_rn(1.0f, s);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = quot<true>(f[j], s, rcp);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) q[j] = quot<false>(f[j], s, 0.0f);
+    }
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w |= (uint32_t)fminf(fmaxf(__builtin_rintf(q[j]) + z, 0.0f), 15.0f) << (4 * j);
+    codes[g.row * cpr + c] = w;
+    if ((c & 15) == 0) {
+      const int64_t gi = g.row * (cols >> 7) + (c >> 4);
+      scales[gi] = (uint16_t)(__float_as_uint(s) >> 16);
+      zeros[gi] = (uint8_t)z;
+    }
   }
 }
 
@@ -282,65 +372,68 @@ __device__ __forceinline__ float e8m0_value(uint32_t code) {
   return __uint_as_float(code << 23);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __global__ __launch_bounds__(256) void k_dequant(int kind, const uint8_t* __restrict__ codes,
                                                  const void* __restrict__ scales,
                                                  const uint8_t* __restrict__ zeros, int64_t rows,
                                                  int64_t cols, uint16_t* __restrict__ y, int64_t ldy) {
-  const int64_t cpr = cols >> 3;
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * cpr) return;
-  const int64_t r = i / cpr, c = i - r * cpr;
-  float v[8];
-  if (kind <= 5) {
-    if (kind == 5) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (cols >> 1) + c * 4);
-      const float sc = e8m0_value(static_cast<const uint8_t*>(scales)[r * (cols >> 5) + (c >> 2)]);
+  const Seg g;
+  if (g.row >= rows) return;
+  const int64_t cpr = cols >> 3, r = g.row;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((w >> (4 * j)) & 0xF) * sc;
-    } else {
-      const uint2 w = *reinterpret_cast<const uint2*>(codes + r * cols + c * 8);
-      float sc;
-      const float* sf = static_cast<const float*>(scales);
-      switch (kind) {
-        case 0: sc = sf[0]; break;
-        case 1: sc = sf[r]; break;
-        case 2: sc = sf[r * (cols >> 7) + (c >> 4)]; break;
-        case 3: sc = sf[(r >> 7) * (cols >> 7) + (c >> 4)]; break;
-        default: sc = e8m0_value(static_cast<const uint8_t*>(scales)[r * (cols >> 5) + (c >> 2)]);
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    if (c >= cpr) continue;
+    float v[8];
+    if (kind <= 5) {
+      if (kind == 5) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (cols >> 1) + c * 4);
+        const float sc = e8m0_value(static_cast<const uint8_t*>(scales)[r * (cols >> 5) + (c >> 2)]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((w >> (4 * j)) & 0xF) * sc;
+      } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(codes + r * cols + c * 8);
+        float sc;
+        const float* sf = static_cast<const float*>(scales);
+        switch (kind) {
+          case 0: sc = sf[0]; break;
+          case 1: sc = sf[r]; break;
+          case 2: sc = sf[r * (cols >> 7) + (c >> 4)]; break;
+          case 3: sc = sf[(r >> 7) * (cols >> 7) + (c >> 4)]; break;
+          default: sc = e8m0_value(static_cast<const uint8_t*>(scales)[r * (cols >> 5) + (c >> 2)]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = e4m3_decode((w.x >> (8 * j)) & 0xFF) * sc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 + j] = e4m3_decode((w.y >> (8 * j)) & 0xFF) * sc;
       }
+    } else {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[r * cpr + c];
+      const int64_t gi = r * (cols >> 7) + (c >> 4);
+      const float s = __uint_as_float((uint32_t)static_cast<const uint16_t*>(scales)[gi] << 16);
+      const float z = (float)zeros[gi];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = e4m3_decode((w.x >> (8 * j)) & 0xFF) * sc;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[4 + j] = e4m3_decode((w.y >> (8 * j)) & 0xFF) * sc;
+      for (int j = 0; j < 8; ++j) v[j] = ((float)((w >> (4 * j)) & 0xF) - z) * s;
     }
-  } else {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[r * cpr + c];
-    const int64_t g = r * (cols >> 7) + (c >> 4);
-    const float s = __uint_as_float((uint32_t)static_cast<const uint16_t*>(scales)[g] << 16);
-    const float z = (float)zeros[g];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = ((float)((w >> (4 * j)) & 0xF) - z) * s;
+    stg16(y + r * ldy + c * 8,
+          make_uint4(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]), bf16x2_rne(v[4], v[5]), bf16x2_rne(v[6], v[7])));
   }
-  uint4 o;
-  o.x = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-  o.y = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-  o.z = f32_to_bf16_rne(v[4]) | (f32_to_bf16_rne(v[5]) << 16);
-  o.w = f32_to_bf16_rne(v[6]) | (f32_to_bf16_rne(v[7]) << 16);
-  stg16(y + r * ldy + c * 8, o);
 }
-
-inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_quant_fp8_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                    uint8_t* codes, float* scale, float* ws_partials, hipStream_t st) {
-  const int64_t chunks = rows * (cols >> 3);
-  int np = (int)std::min<int64_t>(kTensorAmaxBlocks, std::max<int64_t>(1, blocks_for(chunks)));
+  const int64_t units = rows * (((cols >> 3) + 63) >> 6);
+  const int np = (int)std::min<int64_t>(kTensorAmaxBlocks, std::max<int64_t>(1, (units + 3) / 4));
   hipLaunchKernelGGL(k_amax_partial, dim3(np), dim3(256), 0, st, x, rows, cols, ldx, ws_partials);
-  unsigned nb = (unsigned)std::min<int64_t>(8192, std::max<int64_t>(1, blocks_for(chunks)));
-  hipLaunchKernelGGL(k_fp8_tensor, dim3(nb), dim3(256), 0, st, x, rows, cols, ldx, ws_partials, np,
+  hipLaunchKernelGGL(k_fp8_tensor, seg_grid(rows, cols), dim3(256), 0, st, x, rows, cols, ldx, ws_partials, np,
                      codes, scale);
   return hipGetLastError();
 }
@@ -352,6 +445,7 @@ hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t rows, int64_t cols, i
   if (nch <= 64) hipLaunchKernelGGL(k_fp8_row<1>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
   else if (nch <= 128) hipLaunchKernelGGL(k_fp8_row<2>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
   else if (nch <= 256) hipLaunchKernelGGL(k_fp8_row<4>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  else if (nch <= 384) hipLaunchKernelGGL(k_fp8_row<6>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
   else if (nch <= 512) hipLaunchKernelGGL(k_fp8_row<8>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
   else if (nch <= 1024) hipLaunchKernelGGL(k_fp8_row<16>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
   else hipLaunchKernelGGL(k_fp8_row<0>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
@@ -360,8 +454,7 @@ hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t rows, int64_t cols, i
 
 hipError_t launch_quant_fp8_block_act(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                       uint8_t* codes, float* scales, hipStream_t st) {
-  hipLaunchKernelGGL(k_fp8_block_act, dim3(blocks_for(rows * (cols >> 3))), dim3(256), 0, st, x, rows,
-                     cols, ldx, codes, scales);
+  hipLaunchKernelGGL(k_fp8_block_act, seg_grid(rows, cols), dim3(256), 0, st, x, rows, cols, ldx, codes, scales);
   return hipGetLastError();
 }
 
@@ -374,7 +467,7 @@ hipError_t launch_quant_fp8_block_wt(const uint16_t* x, int64_t rows, int64_t co
 
 hipError_t launch_quant_mx(bool fp4, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                            uint8_t* codes, uint8_t* scales, hipStream_t st) {
-  const dim3 grid(blocks_for(rows * (cols >> 3))), block(256);
+  const dim3 grid = seg_grid(rows, cols), block(256);
   if (fp4) hipLaunchKernelGGL(k_mx<true>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
   else hipLaunchKernelGGL(k_mx<false>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
   return hipGetLastError();
@@ -382,7 +475,7 @@ hipError_t launch_quant_mx(bool fp4, const uint16_t* x, int64_t rows, int64_t co
 
 hipError_t launch_quant_int4(bool sym, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint32_t* codes, uint16_t* scales, uint8_t* zeros, hipStream_t st) {
-  const dim3 grid(blocks_for(rows * (cols >> 3))), block(256);
+  const dim3 grid = seg_grid(rows, cols), block(256);
   if (sym) hipLaunchKernelGGL(k_int4<true>, grid, block, 0, st, x, rows, cols, ldx, codes, scales, zeros);
   else hipLaunchKernelGGL(k_int4<false>, grid, block, 0, st, x, rows, cols, ldx, codes, scales, zeros);
   return hipGetLastError();
@@ -390,8 +483,8 @@ hipError_t launch_quant_int4(bool sym, const uint16_t* x, int64_t rows, int64_t 
 
 hipError_t launch_dequant(int kind, const void* codes, const void* scales, const uint8_t* zeros,
                           int64_t rows, int64_t cols, uint16_t* y, int64_t ldy, hipStream_t st) {
-  hipLaunchKernelGGL(k_dequant, dim3(blocks_for(rows * (cols >> 3))), dim3(256), 0, st, kind,
-                     static_cast<const uint8_t*>(codes), scales, zeros, rows, cols, y, ldy);
+  hipLaunchKernelGGL(k_dequant, seg_grid(rows, cols), dim3(256), 0, st, kind, static_cast<const uint8_t*>(codes),
+                     scales, zeros, rows, cols, y, ldy);
   return hipGetLastError();
 }
 
