@@ -39,6 +39,8 @@
 // of row r sits at position c ^ (r % 8), which keeps each 8-lane group of a
 // fragment read on distinct banks.
 #include <algorithm>
+#include <tuple>
+#include <type_traits>
 
 #include "pql_device.hpp"
 #include "pql_internal.hpp"
@@ -134,8 +136,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kRegionBytes + 4 * kWaveBytes];
+template <int KIND>
+struct Kind {
+  static constexpr bool kMx = KIND == GEMM_MXFP8 || KIND == GEMM_MXFP4;
+  static constexpr bool kFp4 = KIND == GEMM_MXFP4;
+  static constexpr int kSpr = kFp4 ? 4 : 2;                // MFMA slices per 128-byte row of a region
+  static constexpr int kLogSpr = kFp4 ? 2 : 1;
+  static constexpr int kQ = kFp4 ? 1 : 2;                  // 16-byte fragment reads per block and slice
+  static constexpr int kFmt = kFp4 ? 4 : 0;                // MFMA operand format: e2m1 or e4m3
+  static constexpr int kSB = kFp4 ? 8 : 4;                 // e8m0 bytes per row and region
+  static constexpr int kMxRegionBytes = kMx ? 2 * BM * kSB : 0;
+  static constexpr int kWaveBytes = kEpiBytes + (kMx ? 0 : kScaleBytes);
+  static constexpr int kLdsBytes = 2 * kRegionBytes + 2 * kMxRegionBytes + 4 * kWaveBytes;
+};
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
+  using T = Kind<KIND>;
+  constexpr int kSpr = T::kSpr, kQ = T::kQ;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[T::kLdsBytes];
 
   const int tiles_m = (int)((g.M + BM - 1) / BM), tiles_n = (int)((g.N + BN - 1) / BN);
   Sched sched;
@@ -146,133 +165,225 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int Kb = (int)g.K;
-  const int nsteps = Kb / kSlice;               // slices per tile (even: K % 128 == 0)
+  const int Kb = (int)(T::kFp4 ? g.K / 2 : g.K);   // bytes per operand row
+  const int nreg = Kb / kRow;                      // regions (128-byte K spans) per tile
+  const int sb_row = (int)(g.K / 32);              // e8m0 bytes per row (MX)
 
   // ---- load stream.  Wave w moves A rows and W rows 64 w .. 64 w + 63 of a tile
-  // for one K pair, 8 rows per instruction: lane i fetches chunk (i % 8) ^ (i / 8)
-  // of row i / 8 of the group, which lands at LDS offset 16 i, the swizzled
-  // position.  Each load's descriptor starts at its row group and K pair and
-  // covers only the tile's valid rows (rows past M / N read 0), so the per-lane
-  // offset is the one loop-invariant register `voff`.  Pairs past a tile's end
-  // come from the next tile, whose (base, bytes) pairs are kept beside the
-  // current ones; past this workgroup's last tile the stream refetches its last
-  // tile into a region that is never read.
+  // for one K region, 8 rows per instruction: lane i fetches chunk
+  // (i % 8) ^ (i / 8) of row i / 8 of the group, which lands at LDS offset 16 i,
+  // the swizzled position.  Each load's descriptor starts at its row group and
+  // K region and covers only the tile's valid rows (rows past M / N read 0), so
+  // the per-lane offset is the one loop-invariant register `voff`.  Regions
+  // past a tile's end come from the next tile, whose (base, bytes) pairs are
+  // kept beside the current ones; past this workgroup's last tile the stream
+  // refetches its last tile into a region that is never read.  MX scales ride
+  // the same stream: per region, each row's kSB exponent bytes.
   const int voff = (lane >> 3) * Kb + (((lane & 7) ^ (lane >> 3)) << 4);
+  const int voff_sc = (lane / (T::kSB / 4)) * sb_row + (lane % (T::kSB / 4)) * 4;
   struct Span {
     uint64_t base;
     int bytes;
   };
-  auto tile_spans = [&](int k, Span& as, Span& ws) {
+  struct TileSpans {
+    Span a, w, sa, sw;
+  };
+  auto tile_spans = [&](int k, TileSpans& ts) __attribute__((always_inline)) {
     int tm, tn;
     sched.coords(std::min(k, my_tiles - 1), tm, tn);
     tm = __builtin_amdgcn_readfirstlane(tm);
     tn = __builtin_amdgcn_readfirstlane(tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-    as = Span{reinterpret_cast<uint64_t>(g.a + m0 * Kb), (int)(std::min<int64_t>(BM, g.M - m0) * Kb)};
-    ws = Span{reinterpret_cast<uint64_t>(g.w + n0 * Kb), (int)(std::min<int64_t>(BN, g.N - n0) * Kb)};
+    const int mr = (int)std::min<int64_t>(BM, g.M - m0), nr = (int)std::min<int64_t>(BN, g.N - n0);
+    ts.a = Span{reinterpret_cast<uint64_t>(g.a + m0 * Kb), mr * Kb};
+    ts.w = Span{reinterpret_cast<uint64_t>(g.w + n0 * Kb), nr * Kb};
+    if constexpr (T::kMx) {
+      ts.sa = Span{reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(g.a_scales) + m0 * sb_row), mr * sb_row};
+      ts.sw = Span{reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(g.w_scales) + n0 * sb_row), nr * sb_row};
+    }
   };
-  auto rsrc_at = [](const Span& sp, int off) {
+  auto rsrc_at = [](const Span& sp, int off) __attribute__((always_inline)) {
     return make_rsrc(reinterpret_cast<const void*>(sp.base + (uint64_t)off), std::max(sp.bytes - off, 0));
   };
-  Span a_cur, w_cur, a_nxt, w_nxt;
-  tile_spans(0, a_cur, w_cur);
-  tile_spans(1, a_nxt, w_nxt);
-  // Load part `part` (0..15: row group part / 2 of A for even parts, of W for odd
-  // ones) of the pair starting at local slice `ls` (even; counted from the
-  // current tile's start) into region `region`.
-  auto issue_part = [&](int ls, int region, int part) {
-    const bool here = ls < nsteps;
-    const Span sp = (part & 1) ? (here ? w_cur : w_nxt) : (here ? a_cur : a_nxt);
-    const int rows = wave * 64 + 8 * (part >> 1);
-    const int off = (here ? ls : ls - nsteps) * kSlice + rows * Kb;
-    const uint8_t* dst = smem + (region & 1) * kRegionBytes + (part & 1) * kOpBytes + rows * kRow;
-    lds_load16(rsrc_at(sp, off), dst, voff);
-  };
-
-  // Fragment offsets within a region: slice half h of the pair uses chunks
-  // 4 h + g and 4 h + 2 + g (g = lane / 32); rows + 32 i keep the swizzle.
-  const int fr = lane & 31, fk = lane >> 5;
-  int a_off[2][2], w_off[2][2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      a_off[h][q] = swz128(wm * 128 + fr, 4 * h + 2 * q + fk);
-      w_off[h][q] = kOpBytes + swz128(wn * 128 + fr, 4 * h + 2 * q + fk);
+  TileSpans cur, nxt;
+  tile_spans(0, cur);
+  tile_spans(1, nxt);
+  uint8_t* const mx_sc = smem + 2 * kRegionBytes;   // two slots of MX scales
+  // Load part `part` of local region `lr` (counted from the current tile's
+  // start; past nreg it is the next tile's) into LDS slot `slot`.  Parts 0..15
+  // are code rows (row group part / 2 of A for even parts, of W for odd ones);
+  // MX parts 16.. are the exponent rows (A, then W; 64 / (4 / kSB)... rows each).
+  auto issue_part = [&](int lr, int slot, int part) __attribute__((always_inline)) {
+    const bool here = lr < nreg;
+    const int rg = here ? lr : lr - nreg;
+    if (part < 16) {
+      const Span& sp = (part & 1) ? (here ? cur.w : nxt.w) : (here ? cur.a : nxt.a);
+      const int rows = wave * 64 + 8 * (part >> 1);
+      const uint8_t* dst = smem + (slot & 1) * kRegionBytes + (part & 1) * kOpBytes + rows * kRow;
+      lds_load16(rsrc_at(sp, rg * kRow + rows * Kb), dst, voff);
+    } else if constexpr (T::kMx) {
+      constexpr int kRowsPer = 256 / T::kSB;                     // exponent rows per instruction
+      const int q = part - 16, per_op = 64 / kRowsPer;
+      const bool wop = q >= per_op;
+      const Span& sp = wop ? (here ? cur.sw : nxt.sw) : (here ? cur.sa : nxt.sa);
+      const int rows = wave * 64 + kRowsPer * (wop ? q - per_op : q);
+      const uint8_t* dst = mx_sc + (slot & 1) * T::kMxRegionBytes + (wop ? BM * T::kSB : 0) + rows * T::kSB;
+      lds_load4(rsrc_at(sp, rg * T::kSB + rows * sb_row), dst, voff_sc);
     }
+  };
+  constexpr int kParts = 16 + (T::kMx ? 2 * (64 * T::kSB / 256) : 0);   // loads per wave and region
+
+  // Fragment offsets within a region for slice h: fp8 uses chunks 4 h + g and
+  // 4 h + 2 + g (g = lane / 32), fp4 chunk 2 h + g; rows + 32 i keep the swizzle.
+  const int fr = lane & 31, fk = lane >> 5;
+  int a_off[kSpr][kQ], w_off[kSpr][kQ];
+#pragma unroll
+  for (int h = 0; h < kSpr; ++h)
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int chunk = T::kFp4 ? 2 * h + fk : 4 * h + 2 * q + fk;
+      a_off[h][q] = swz128(wm * 128 + fr, chunk);
+      w_off[h][q] = kOpBytes + swz128(wn * 128 + fr, chunk);
+    }
+  // MX exponents of a region: lane l holds, for each of its 4 A (and W) row
+  // blocks, the kSB bytes of row 32 i + l % 32, shifted down by l / 32 bytes so
+  // that byte 2 h' of dword d is the exponent of the K-block this lane's
+  // operand covers in slice 4 d + h' (the slice's two 32-blocks go to the two
+  // lane halves).
+  const int sa_off = (wm * 128 + fr) * T::kSB, sw_off = BM * T::kSB + (wn * 128 + fr) * T::kSB;
+  constexpr int kSD = T::kSB / 4;   // exponent dwords per row and region
 
   v16f acc[4][4];   // each tile's first slice starts the sums from zero
 
-  uint4 fa0[4][2], fw0[4][2], fa1[4][2], fw1[4][2];   // two register sets of fragment halves
-  auto read_frags = [&](uint4 (&fa)[4][2], uint4 (&fw)[4][2], const uint8_t* region, int h) {
+  uint4 fa0[4][kQ], fw0[4][kQ], fa1[4][kQ], fw1[4][kQ];   // two register sets of fragments
+  int eca[4][kSD], ecw[4][kSD], ena[4][kSD], enw[4][kSD];  // MX exponents: current and next region
+  auto read_frags = [&](uint4 (&fa)[4][kQ], uint4 (&fw)[4][kQ], const uint8_t* region, auto hc) __attribute__((always_inline)) {
+    constexpr int h = decltype(hc)::value;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < kQ; ++q) {
         fa[i][q] = lds16(region + a_off[h][q] + i * 32 * kRow);
         fw[i][q] = lds16(region + w_off[h][q] + i * 32 * kRow);
       }
   };
-  // One slice: its 16 MFMAs, each followed by one of the 16 LDS reads that fetch
-  // the next slice's fragments (half h of `next_region`) and, for the first
-  // slice of a pair, by one of the 16 loads of the pair starting at local slice
-  // `ls` into `load_region` (scheduling barriers pin this order).
-  auto slice = [&](const uint4 (&fa)[4][2], const uint4 (&fw)[4][2], uint4 (&na)[4][2], uint4 (&nw)[4][2],
-                   const uint8_t* next_region, int h, bool loads, int ls, int load_region, bool reads = true,
-                   bool first = false) {
+  auto read_exps = [&](int (&ea)[4][kSD], int (&ew)[4][kSD], int slot) __attribute__((always_inline)) {
+    if constexpr (T::kMx) {
+      const uint8_t* base = mx_sc + (slot & 1) * T::kMxRegionBytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int d = 0; d < kSD; ++d) {
+          ea[i][d] = *reinterpret_cast<const int*>(base + sa_off + i * 32 * T::kSB + 4 * d);
+          ew[i][d] = *reinterpret_cast<const int*>(base + sw_off + i * 32 * T::kSB + 4 * d);
+        }
+    }
+  };
+  auto shift_exps = [&](int (&ea)[4][kSD], int (&ew)[4][kSD]) __attribute__((always_inline)) {
+    if constexpr (T::kMx) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int d = 0; d < kSD; ++d) {
+          ea[i][d] = (int)((uint32_t)ea[i][d] >> (8 * fk));
+          ew[i][d] = (int)((uint32_t)ew[i][d] >> (8 * fk));
+        }
+    }
+  };
+  auto operand = [](const uint4 (&f)[kQ]) __attribute__((always_inline)) {
+    if constexpr (kQ == 2) return cat(f[0], f[kQ - 1]);
+    else return cat(f[0], uint4{0, 0, 0, 0});
+  };
+  // One slice (slice h of its region): its 16 MFMAs, interleaved with the LDS
+  // reads of the next slice's fragments (slice hn of `next_region`), with the
+  // next region's exponents when the next slice starts a region, and, for the
+  // last slice of a region, with the loads of local region `load_lr` into LDS
+  // slot `load_slot` (scheduling barriers pin this order).
+  auto slice = [&](auto hc, auto flags, const uint4 (&fa)[4][kQ], const uint4 (&fw)[4][kQ], uint4 (&na)[4][kQ],
+                   uint4 (&nw)[4][kQ], const uint8_t* next_region, int next_slot, int load_lr, int load_slot) __attribute__((always_inline)) {
+    constexpr int h = decltype(hc)::value;
+    constexpr int fl = decltype(flags)::value;
+    constexpr bool reads = fl & 1, loads = fl & 2, first = fl & 4;
+    constexpr int hn = (h + 1) & (kSpr - 1);
+    constexpr bool region_end = h == kSpr - 1;
+    constexpr int d = T::kFp4 ? (h >> 1) : 0;
+    constexpr int opsel = T::kFp4 ? 2 * (h & 1) : 2 * h;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            cat(fw[j][0], fw[j][1]), cat(fa[i][0], fa[i][1]), first ? v16f{} : acc[i][j], 0, 0, 0, 127, 0, 127);
+        const v16f c = first ? v16f{} : acc[i][j];   // compile-time choice
+        if constexpr (T::kMx)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(operand(fw[j]), operand(fa[i]), c, T::kFmt,
+                                                                      T::kFmt, opsel, ecw[j][d], opsel, eca[i][d]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(operand(fw[j]), operand(fa[i]), c, 0, 0, 0,
+                                                                      127, 0, 127);
         __builtin_amdgcn_sched_barrier(0);
         const int k = j * 4 + i;
-        const int blk = (k >> 1) & 3, q = k & 1;
-        if (reads) {
-          if (k < 8) na[blk][q] = lds16(next_region + a_off[h][q] + blk * 32 * kRow);
-          else nw[blk][q] = lds16(next_region + w_off[h][q] + blk * 32 * kRow);
+        if constexpr (reads) {
+          if constexpr (kQ == 2) {
+            const int blk = (k >> 1) & 3, q = k & 1;
+            if (k < 8) na[blk][q] = lds16(next_region + a_off[hn][q] + blk * 32 * kRow);
+            else nw[blk][q] = lds16(next_region + w_off[hn][q] + blk * 32 * kRow);
+          } else if ((k & 1) == 0) {
+            const int idx = k >> 1;
+            if (idx < 4) na[idx][0] = lds16(next_region + a_off[hn][0] + idx * 32 * kRow);
+            else nw[idx - 4][0] = lds16(next_region + w_off[hn][0] + (idx - 4) * 32 * kRow);
+          }
+          if constexpr (T::kMx && region_end) {
+            if (k == 15) read_exps(ena, enw, next_slot);
+          }
         }
-        if (loads) issue_part(ls, load_region, k);
+        if constexpr (loads) {
+          issue_part(load_lr, load_slot, k);
+          if (k < kParts - 16) issue_part(load_lr, load_slot, 16 + k);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
   };
-  auto region_of = [&](int G) { return smem + ((G >> 1) & 1) * kRegionBytes; };   // slice G's pair region
-  auto barrier_all_loads = [&]() {
+  auto region_ptr = [&](int R) __attribute__((always_inline)) { return smem + (R & 1) * kRegionBytes; };
+  auto barrier_all_loads = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- scales.  Each wave keeps its 128 row and 128 column scales in its own
-  // 1 KB of LDS, fetched by direct-to-LDS loads right after the previous tile's
-  // epilogue; the next barrier's wait retires them.  Per-tensor scales have
-  // stride 0: every lane then reads the one scale.
-  uint8_t* scr = smem + 2 * kRegionBytes + wave * kWaveBytes;
-  const float* sc_rows = reinterpret_cast<const float*>(scr);
+  // ---- FP8 row / column scales.  Each wave keeps its 128 row and 128 column
+  // scales in its own 1 KB of LDS, fetched by direct-to-LDS loads right after
+  // the previous tile's epilogue; the next barrier's wait retires them.
+  // Per-tensor scales have stride 0: every lane then reads the one scale.
+  uint8_t* wave_lds = smem + 2 * kRegionBytes + 2 * T::kMxRegionBytes + wave * T::kWaveBytes;
+  const float* sc_rows = reinterpret_cast<const float*>(wave_lds + kEpiBytes);
   const float* sc_cols = sc_rows + 128;
-  auto prefetch_scales = [&](int k) {
-    int tm, tn;
-    sched.coords(std::min(k, my_tiles - 1), tm, tn);
-    const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane(tm) * BM + wm * 128;
-    const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(tn) * BN + wn * 128;
-    const int64_t sa_first = g.a_scale_stride ? m0 : 0, sw_first = g.w_scale_stride ? n0 : 0;
-    const int64_t sa_rows = g.a_scale_stride ? std::max<int64_t>(0, std::min<int64_t>(128, g.M - m0)) : 1;
-    const int64_t sw_rows = g.w_scale_stride ? std::max<int64_t>(0, std::min<int64_t>(128, g.N - n0)) : 1;
-    const v4i ra = make_rsrc(static_cast<const float*>(g.a_scales) + sa_first, (int)(sa_rows * 4));
-    const v4i rw = make_rsrc(static_cast<const float*>(g.w_scales) + sw_first, (int)(sw_rows * 4));
-    const int va = (int)g.a_scale_stride * lane * 4, vw = (int)g.w_scale_stride * lane * 4;
-    lds_load4(ra, scr, va);
-    lds_load4(ra, scr + 256, va + (int)g.a_scale_stride * 256);
-    lds_load4(rw, scr + 512, vw);
-    lds_load4(rw, scr + 768, vw + (int)g.w_scale_stride * 256);
+  auto prefetch_scales = [&](int k) __attribute__((always_inline)) {
+    if constexpr (!T::kMx) {
+      int tm, tn;
+      sched.coords(std::min(k, my_tiles - 1), tm, tn);
+      const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane(tm) * BM + wm * 128;
+      const int64_t n0 = (int64_t)__builtin_amdgcn_readfirstlane(tn) * BN + wn * 128;
+      const int64_t sa_first = g.a_scale_stride ? m0 : 0, sw_first = g.w_scale_stride ? n0 : 0;
+      const int64_t sa_rows = g.a_scale_stride ? std::max<int64_t>(0, std::min<int64_t>(128, g.M - m0)) : 1;
+      const int64_t sw_rows = g.w_scale_stride ? std::max<int64_t>(0, std::min<int64_t>(128, g.N - n0)) : 1;
+      const v4i ra = make_rsrc(static_cast<const float*>(g.a_scales) + sa_first, (int)(sa_rows * 4));
+      const v4i rw = make_rsrc(static_cast<const float*>(g.w_scales) + sw_first, (int)(sw_rows * 4));
+      const int va = (int)g.a_scale_stride * lane * 4, vw = (int)g.w_scale_stride * lane * 4;
+      uint8_t* scr = wave_lds + kEpiBytes;
+      lds_load4(ra, scr, va);
+      lds_load4(ra, scr + 256, va + (int)g.a_scale_stride * 256);
+      lds_load4(rw, scr + 512, vw);
+      lds_load4(rw, scr + 768, vw + (int)g.w_scale_stride * 256);
+    }
+  };
+  // Value of accumulator element (i, j, r) as written to C.
+  auto out_val = [&](float a, float rs, float cs) __attribute__((always_inline)) {
+    if constexpr (T::kMx) return a;
+    else return a * rs * cs;
   };
 
   // ---- epilogue of tile k: each lane owns output row m = 32 i + l % 32 of block
-  // i and, per accumulator quad, four consecutive columns: scale, round to bf16,
-  // store 8 bytes (the two lane halves of a row fill 16 contiguous bytes).
-  auto epilogue = [&](int k) {
+  // i and, per accumulator quad, four consecutive columns.
+  auto epilogue = [&](int k) __attribute__((always_inline)) {
     int tm, tn;
     sched.coords(k, tm, tn);
     const int64_t m0 = (int64_t)tm * BM + wm * 128, n0 = (int64_t)tn * BN + wn * 128;
@@ -280,20 +391,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
     if (interior) {
       // The wave's 128 x 128 quarter is inside C.  Rows go out through LDS so
       // that each store writes whole 128-byte lines: per 32-row block i and
-      // 64-column half p, lanes write their scaled bf16 quads (8 bytes) into a
-      // 32-row staging block, then read it back as 16-byte row pieces (8 lanes
-      // per row, 8 rows per instruction).  Staged rows are padded to 136 bytes,
+      // 64-column half p, lanes write their bf16 quads (8 bytes) into a 32-row
+      // staging block, then read it back as 16-byte row pieces (8 lanes per
+      // row, 8 rows per instruction).  Staged rows are padded to 136 bytes,
       // which keeps both the quad writes and the row reads on distinct banks
       // with constant offsets from one per-lane address.
-      uint8_t* stg = scr + kScaleBytes;
+      uint8_t* stg = wave_lds;
       const float4* cs4 = static_cast<const float4*>(__builtin_assume_aligned(sc_cols, 16));
       const int rr = lane >> 3, rc = lane & 7;             // read-back: row rr + 8 q, 16-byte piece rc
       uint8_t* wr = stg + fr * kEpiRow + fk * 8;
       const uint8_t* rd = stg + rr * kEpiRow + rc * 16;
-      const uint32_t voff = (uint32_t)(rr * g.ldc * 2 + rc * 16);
+      const uint32_t voff_c = (uint32_t)(rr * g.ldc * 2 + rc * 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float rs = sc_rows[i * 32 + fr];
+        const float rs = T::kMx ? 1.0f : sc_rows[i * 32 + fr];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
 #pragma unroll
@@ -301,13 +412,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
             const int j = 2 * p + jj;
             float4 cs[4];
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) cs[rq] = cs4[j * 8 + rq * 2 + fk];
+            for (int rq = 0; rq < 4; ++rq) cs[rq] = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : cs4[j * 8 + rq * 2 + fk];
             const v16f a = acc[i][j];
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq)
               *reinterpret_cast<uint2*>(wr + (jj * 8 + rq * 2) * 8) =
-                  uint2{pack_bf16x2(a[4 * rq + 0] * rs * cs[rq].x, a[4 * rq + 1] * rs * cs[rq].y),
-                        pack_bf16x2(a[4 * rq + 2] * rs * cs[rq].z, a[4 * rq + 3] * rs * cs[rq].w)};
+                  uint2{pack_bf16x2(out_val(a[4 * rq + 0], rs, cs[rq].x), out_val(a[4 * rq + 1], rs, cs[rq].y)),
+                        pack_bf16x2(out_val(a[4 * rq + 2], rs, cs[rq].z), out_val(a[4 * rq + 3], rs, cs[rq].w))};
             __builtin_amdgcn_sched_barrier(0);   // one accumulator block at a time
           }
 #pragma unroll
@@ -315,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
             const uint2 lo = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow);
             const uint2 hi = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow + 8);
             char* base = reinterpret_cast<char*>(g.c + (m0 + i * 32 + 8 * qr) * g.ldc + n0 + p * 64);
-            *reinterpret_cast<uint4*>(base + voff) = uint4{lo.x, lo.y, hi.x, hi.y};
+            *reinterpret_cast<uint4*>(base + voff_c) = uint4{lo.x, lo.y, hi.x, hi.y};
           }
         }
       }
@@ -324,16 +435,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t row = m0 + i * 32 + fr;
-      const float rs = sc_rows[i * 32 + fr];
+      const float rs = T::kMx ? 1.0f : sc_rows[i * 32 + fr];
       uint16_t* dst_row = g.c + row * g.ldc;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
           const int cl = j * 32 + rq * 8 + fk * 4;
-          const float4 cs = *reinterpret_cast<const float4*>(sc_cols + cl);
-          const uint32_t lo = pack_bf16x2(acc[i][j][4 * rq + 0] * rs * cs.x, acc[i][j][4 * rq + 1] * rs * cs.y);
-          const uint32_t hi = pack_bf16x2(acc[i][j][4 * rq + 2] * rs * cs.z, acc[i][j][4 * rq + 3] * rs * cs.w);
+          const float4 cs = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const float4*>(sc_cols + cl);
+          const uint32_t lo = pack_bf16x2(out_val(acc[i][j][4 * rq + 0], rs, cs.x), out_val(acc[i][j][4 * rq + 1], rs, cs.y));
+          const uint32_t hi = pack_bf16x2(out_val(acc[i][j][4 * rq + 2], rs, cs.z), out_val(acc[i][j][4 * rq + 3], rs, cs.w));
           const int64_t col = n0 + cl;
           if (row < g.M) {
             if (g.vec_store && col + 4 <= g.N) {
@@ -349,58 +460,101 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32_fp8(GemmArgs g) {
     }
   };
 
-  // ---- prologue: pairs 0 and 1 in flight, then slice 0's fragments.
+  using H0 = std::integral_constant<int, 0>;
+  // ---- prologue: regions 0 and 1 in flight, then slice 0's fragments.
 #pragma unroll
-  for (int part = 0; part < 16; ++part) issue_part(0, 0, part);
+  for (int part = 0; part < kParts; ++part) issue_part(0, 0, part);
 #pragma unroll
-  for (int part = 0; part < 16; ++part) issue_part(2, 1, part);
+  for (int part = 0; part < kParts; ++part) issue_part(1, 1, part);
   prefetch_scales(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(16 + 4, 0));   // pair 0 landed
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kParts + (T::kMx ? 0 : 4), 0));   // region 0 landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  read_frags(fa0, fw0, smem, 0);
+  read_frags(fa0, fw0, smem, H0{});
+  read_exps(eca, ecw, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  shift_exps(eca, ecw);
 
-  // ---- the stream.  G counts slices over all tiles; nsteps is even, so a
-  // tile's slice s has the parity of G, even slices use register set 0 and odd
-  // slices set 1, and a tile ends with the first slice of a pair.
-  int G = 0;
-  for (int k = 0; k < my_tiles; ++k) {
-    slice(fa0, fw0, fa1, fw1, region_of(G), 1, false, 0, 0, true, true);     // s = 0 starts the sums
-    int s = 1;
-    for (; s < nsteps - 1; s += 2) {
-      barrier_all_loads();
-      slice(fa1, fw1, fa0, fw0, region_of(G + s + 1), 0, true, s + 3, (G + s) >> 1);
-      slice(fa0, fw0, fa1, fw1, region_of(G + s + 1), 1, false, 0, 0);
+  // ---- the stream.  R counts regions over all tiles.  Within a region the
+  // slices alternate register sets 0 / 1 (kSpr is even, so a region and a tile
+  // always start with set 0); the last slice of a region waits for all loads
+  // and meets the other waves first, then refills the region two ahead and
+  // reads the next region's exponents, which become current after it.
+  // Flags: 1 = read the next slice's fragments, 2 = issue loads, 4 = first
+  // slice of a tile (its sums start from zero).
+  using F_FIRST = std::integral_constant<int, 5>;
+  using F_MID = std::integral_constant<int, 1>;
+  using F_LOAD = std::integral_constant<int, 3>;
+  using F_END = std::integral_constant<int, 2>;
+  auto adopt_exps = [&]() __attribute__((always_inline)) {
+    if constexpr (T::kMx) {
+      shift_exps(ena, enw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int dd = 0; dd < kSD; ++dd) {
+          eca[i][dd] = ena[i][dd];
+          ecw[i][dd] = enw[i][dd];
+        }
     }
-    // s = nsteps - 1: the next tile's first fragments are read after the
-    // epilogue, which keeps their registers free while it runs.
+  };
+  // Slices 1 .. kSpr - 2 of region R (fp4 only), all in the region.
+  auto inner_slices = [&](int R) __attribute__((always_inline)) {
+    if constexpr (kSpr == 4) {
+      slice(std::integral_constant<int, 1>{}, F_MID{}, fa1, fw1, fa0, fw0, region_ptr(R), R + 1, 0, 0);
+      slice(std::integral_constant<int, 2>{}, F_MID{}, fa0, fw0, fa1, fw1, region_ptr(R), R + 1, 0, 0);
+    }
+  };
+  int R = 0;   // regions over all tiles
+  for (int k = 0; k < my_tiles; ++k) {
+    slice(H0{}, F_FIRST{}, fa0, fw0, fa1, fw1, region_ptr(R), R + 1, 0, 0);
+    inner_slices(R);
+    for (int r = 0; r + 1 < nreg; ++r, ++R) {
+      barrier_all_loads();
+      slice(std::integral_constant<int, kSpr - 1>{}, F_LOAD{}, fa1, fw1, fa0, fw0, region_ptr(R + 1), R + 1, r + 2,
+            R);
+      adopt_exps();
+      slice(H0{}, F_MID{}, fa0, fw0, fa1, fw1, region_ptr(R + 1), R + 2, 0, 0);
+      inner_slices(R + 1);
+    }
+    // The tile's last slice: the next tile's first fragments are read after
+    // the epilogue, which keeps their registers free while it runs.
     barrier_all_loads();
-    slice(fa1, fw1, fa0, fw0, region_of(G + s + 1), 0, true, s + 3, (G + s) >> 1, false);
-    G += nsteps;
+    slice(std::integral_constant<int, kSpr - 1>{}, F_END{}, fa1, fw1, fa0, fw0, region_ptr(R + 1), R + 1, nreg + 1,
+          R);
+    ++R;
     epilogue(k);
-    read_frags(fa0, fw0, region_of(G), 0);
-    a_cur = a_nxt;
-    w_cur = w_nxt;
-    tile_spans(k + 2, a_nxt, w_nxt);
+    read_frags(fa0, fw0, region_ptr(R), H0{});
+    read_exps(eca, ecw, R);
+    cur = nxt;
+    tile_spans(k + 2, nxt);
     // The epilogue's LDS reads of the scales are done before the next tile's
     // scales may overwrite them.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    shift_exps(eca, ecw);
     prefetch_scales(k + 1);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+template <int KIND>
+hipError_t launch_kind32(const GemmArgs& g, hipStream_t st) {
+  const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
+  const int64_t row_bytes = Kind<KIND>::kFp4 ? g.K / 2 : g.K;
+  // The load stream runs two regions ahead, into the next tile, which is the
+  // next tile's own first regions only when a tile has at least two regions;
+  // shorter K gets one tile per workgroup (its look-ahead loads then land in a
+  // region that is never read).
+  const int grid = (row_bytes / kRow >= 2) ? std::min(tiles, kPersistentCap) : tiles;
+  hipLaunchKernelGGL(k_gemm32<KIND>, dim3(grid), dim3(kThreads), 0, st, g);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_gemm32_fp8(const GemmArgs& g, hipStream_t st) {
-  const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
-  // The load stream runs one pair (two slices) ahead into the next tile, which
-  // is the next tile's own first pair only when a tile has at least two pairs;
-  // K = 128 gets one tile per workgroup (its look-ahead loads then land in a
-  // region that is never read).
-  const int grid = (g.K / kRow >= 2) ? std::min(tiles, kPersistentCap) : tiles;
-  hipLaunchKernelGGL(k_gemm32_fp8, dim3(grid), dim3(kThreads), 0, st, g);
-  return hipGetLastError();
+hipError_t launch_gemm32_fp8(const GemmArgs& g, hipStream_t st) { return launch_kind32<GEMM_FP8_ROWSCALE>(g, st); }
+hipError_t launch_gemm32_mx(bool fp4, const GemmArgs& g, hipStream_t st) {
+  return fp4 ? launch_kind32<GEMM_MXFP4>(g, st) : launch_kind32<GEMM_MXFP8>(g, st);
 }
 
 }  // namespace pql

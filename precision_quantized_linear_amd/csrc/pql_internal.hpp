@@ -49,8 +49,10 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st);
-// FP8 tensor / row scales on the four-stage 32x32x64 kernel
+// Persistent 32x32x64 kernels: FP8 tensor / row scales, and MXFP8 / MXFP4
+// (MXFP4 needs K % 256 == 0, MXFP8 K % 128 == 0).
 hipError_t launch_gemm32_fp8(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm32_mx(bool fp4, const GemmArgs& g, hipStream_t st);
 const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);
 
 // W4A16: C = A (bf16) * dequant(Wq)^T
