@@ -298,7 +298,7 @@ hipError_t launch_kind(const GemmArgs& g, hipStream_t st) {
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st) {
   switch (kind) {
     case GEMM_FP8_ROWSCALE: return launch_gemm32_fp8(g, st);
-    case GEMM_FP8_BLOCK: return launch_kind<GEMM_FP8_BLOCK>(g, st);
+    case GEMM_FP8_BLOCK: return launch_gemm_block(g, st);
     case GEMM_MXFP8: return launch_gemm32_mx(false, g, st);
     case GEMM_MXFP4: return g.K % 256 == 0 ? launch_gemm32_mx(true, g, st) : launch_kind<GEMM_MXFP4>(g, st);
   }
@@ -308,7 +308,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st) {
 const char* gemm_kernel_name(GemmKind kind, int64_t, int64_t, int64_t K) {
   switch (kind) {
     case GEMM_FP8_ROWSCALE: return "k_gemm32_fp8";
-    case GEMM_FP8_BLOCK: return "k_gemm<fp8_block128>_256x256x128";
+    case GEMM_FP8_BLOCK: return "k_gemm_block";
     case GEMM_MXFP8: return "k_gemm32<mxfp8>";
     case GEMM_MXFP4: return K % 256 == 0 ? "k_gemm32<mxfp4>" : "k_gemm<mxfp4>_256x256x256";
   }

@@ -42,12 +42,15 @@
 #include <tuple>
 #include <type_traits>
 
+#include "gemm_common.hpp"
 #include "pql_device.hpp"
 #include "pql_internal.hpp"
 
 namespace pql {
 
 namespace {
+
+using namespace gemm;
 
 constexpr int kThreads = 256;
 constexpr int BM = 256, BN = 256;
@@ -59,82 +62,10 @@ constexpr int kScaleBytes = 1024;                // per wave: 128 row scales, th
 constexpr int kEpiRow = 136;                     // staged output row: 64 bf16 + 8 bytes of padding
 constexpr int kEpiBytes = 32 * kEpiRow;          // per wave: 32 output rows staged for row stores
 constexpr int kWaveBytes = kScaleBytes + kEpiBytes;
-constexpr int kGroupM = 4;
 constexpr int kPersistentCap = 256;              // one workgroup per CU
 
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt 6:4
-// left at its maximum, lgkmcnt in bits 11:8.
-constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
-
-__device__ __forceinline__ int swz128(int row, int chunk) { return row * kRow + ((chunk ^ (row & 7)) << 4); }
-
-// Persistent schedule.  Workgroup b runs on XCD b % 8 (dispatch is round-robin
-// over the XCDs).  Each XCD owns a contiguous range of the tile order, and its
-// workgroups take consecutive tiles of that range round by round, so the
-// tiles in flight on one XCD form 4 x 8 patches that share A and W rows in
-// its L2.  The tile order walks 4-tile-tall groups column by column.
-struct Sched {
-  int tiles_m, tiles_n, first, stride, count;   // this workgroup's tiles: first + k * stride, k < count
-  __device__ void init(int T, int tm_, int tn_) {
-    tiles_m = tm_;
-    tiles_n = tn_;
-    const int G = gridDim.x, b = blockIdx.x;
-    const int xcd = b & 7, slot = b >> 3;
-    const int nslots = (G - xcd + 7) >> 3;                       // workgroups on this XCD
-    const int per = T >> 3, rem = T & 7;
-    const int start = xcd * per + min(xcd, rem), len = per + (xcd < rem ? 1 : 0);
-    first = start + slot;
-    stride = nslots;
-    count = slot < len ? (len - slot + nslots - 1) / nslots : 0;
-  }
-  __device__ void coords(int k, int& tm, int& tn) const {
-    const int L = first + k * stride;
-    const int in_group = kGroupM * tiles_n;
-    const int group = L / in_group;
-    const int first_m = group * kGroupM;
-    const int gm = min(tiles_m - first_m, kGroupM);
-    const int l = L - group * in_group;
-    tm = first_m + l % gm;
-    tn = l / gm;
-  }
-};
-
-// Buffer descriptor for bytes [base, base + nbytes); loads beyond nbytes read 0.
-__device__ __forceinline__ v4i make_rsrc(const void* base, int nbytes) {
-  const uint64_t p = reinterpret_cast<uint64_t>(base);
-  return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)p), __builtin_amdgcn_readfirstlane((int)(p >> 32) & 0xffff),
-             __builtin_amdgcn_readfirstlane(nbytes), 0x00020000};
-}
-
-// One direct-to-LDS load: 16 bytes per lane from rsrc + voff into LDS at lds + 16 * lane.
-__device__ __forceinline__ void lds_load16(v4i rsrc, const uint8_t* lds, int voff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0), "v"(voff),
-               "s"(rsrc)
-               : "memory", "m0");
-}
-
-// One direct-to-LDS load of 4 bytes per lane: rsrc + voff into LDS at lds + 4 * lane.
-__device__ __forceinline__ void lds_load4(v4i rsrc, const uint8_t* lds, int voff) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds" ::"s"(m0), "v"(voff),
-               "s"(rsrc)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-__device__ __forceinline__ v8i cat(uint4 lo, uint4 hi) {
-  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const bf16x2 v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 template <int KIND>
 struct Kind {

@@ -53,6 +53,8 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st);
 // (MXFP4 needs K % 256 == 0, MXFP8 K % 128 == 0).
 hipError_t launch_gemm32_fp8(const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm32_mx(bool fp4, const GemmArgs& g, hipStream_t st);
+// Persistent FP8 block-128 kernel (16x16x128 MFMA per K-group, FMA promotion; N % 128 == 0).
+hipError_t launch_gemm_block(const GemmArgs& g, hipStream_t st);
 const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);
 
 // W4A16: C = A (bf16) * dequant(Wq)^T
