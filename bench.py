@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--all", action="store_true", help="also time every workload and kernel")
+    p.add_argument("--workload", default=None, help="with --all: only this workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true",
@@ -92,14 +93,18 @@ class EventTimer:
 
 
 def time_loop(torch, fn, steps, warmup):
+    """Mean duration of one launch: `steps` launches back to back between two HIP events
+    on the launching stream, so the host's launch latency overlaps the GPU's work."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    timer = EventTimer(torch)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
     for i in range(steps):
-        timer(lambda: fn(i))
+        fn(i)
+    e.record()
     torch.cuda.synchronize()
-    return timer.mean_ms()
+    return s.elapsed_time(e) / steps
 
 
 # ----------------------------------------------------------------------------- headline step
@@ -147,12 +152,14 @@ def headline(torch, pql, steps, warmup):
 
 
 # ----------------------------------------------------------------------------- every workload
-def all_workloads(torch, pql, steps, warmup):
+def all_workloads(torch, pql, steps, warmup, only=None):
     import workloads as wl
     lines = []
     for name, scheme in (("fp8_tensor_small", "fp8_tensor"), ("fp8_row_dit", "fp8_row"),
                          ("fp8_block_dit", "fp8_block128"), ("mx_video_dit", "mxfp8"),
                          ("mx_video_dit", "mxfp4")):
+        if only and name != only:
+            continue
         w = wl.WORKLOADS[name]
         a0, w0 = up(torch, wl.activation(w)), up(torch, wl.weight(w))
         Ra, Rw = rotation(a0.numel() * 2), rotation(w0.numel() * 2)
@@ -184,6 +191,8 @@ def all_workloads(torch, pql, steps, warmup):
                       "qlinear_us": tl * 1e3, "qlinear_tflops": flops / (tl * 1e-3) / 1e12})
         del acts, wts, aq, wq, out, ws
         torch.cuda.empty_cache()
+    if only and only != "w4a16_dit":
+        return lines
     w = wl.WORKLOADS["w4a16_dit"]
     codes, zeros, scales = wl.int4_weight_parts(w)
     wq = pql.QTensor("w4a16_asym", "weight", w.N, w.K,
@@ -273,7 +282,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.all:
-        for line in all_workloads(torch, pql, args.steps, args.warmup):
+        for line in all_workloads(torch, pql, args.steps, args.warmup, args.workload):
             print(json.dumps(line), flush=True)
     h = headline(torch, pql, args.steps, args.warmup)
     peak = PEAK_TFLOPS["fp8"]

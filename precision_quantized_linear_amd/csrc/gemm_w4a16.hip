@@ -244,11 +244,183 @@ __global__ __launch_bounds__(256) void k_w4a16_small(const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- M <= 16
+// Weight-bandwidth-bound GEMV-like path.  Codes stay integers: each 16-byte
+// chunk (32 codes of one row) is spread into bf16 pairs 128 + q with two
+// bit operations per pair (bf16 represents 128..143 exactly), and the
+// zero-point is removed per group after the matrix core:
+//   sum_k a_k (q_k - z) = sum_k a_k (128 + q_k) - (128 + z) sum_k a_k,
+// with sum_k a_k from a second MFMA against a bf16 ones operand, so the
+// dequantized weight is never rounded.  Each K-group's sums are promoted with
+// the group's scale: acc += s (P - (128 + z) Q).
+//
+// A workgroup owns 16 output columns; its 4 waves split the K-groups.  Lane
+// (n = l % 16, g = l / 16) streams chunk 4 G + g of weight row n for its
+// wave's groups G (the 4 lanes of a row read 64 contiguous bytes per group),
+// all loads of a batch of 8 groups issued before any is used.  Because the
+// nibbles of a code word come out as pairs (k, k + 4), the A operand of a
+// lane holds a[m, k0 + {0, 4, 1, 5, 2, 6, 3, 7}] (one v_perm per pair); the
+// matrix core's sum over K does not care about the order.
+__device__ __forceinline__ uint4 spread_codes(uint32_t w) {
+  // nibble j of w -> bf16 128 + q_j; dword i holds elements (i, i + 4)
+  const uint32_t base = 0x43004300u;
+  return make_uint4(__builtin_amdgcn_ubfe(w, 0, 4) | (__builtin_amdgcn_ubfe(w, 16, 4) << 16) | base,
+                    __builtin_amdgcn_ubfe(w, 4, 4) | (__builtin_amdgcn_ubfe(w, 20, 4) << 16) | base,
+                    __builtin_amdgcn_ubfe(w, 8, 4) | (__builtin_amdgcn_ubfe(w, 24, 4) << 16) | base,
+                    __builtin_amdgcn_ubfe(w, 12, 4) | (__builtin_amdgcn_ubfe(w, 28, 4) << 16) | base);
+}
+// 8 bf16 a0..a7 (pairs per dword) -> pairs (a0, a4), (a1, a5), (a2, a6), (a3, a7).
+__device__ __forceinline__ uint4 pair_k_k4(uint4 a) {
+  return make_uint4(__builtin_amdgcn_perm(a.z, a.x, 0x05040100u), __builtin_amdgcn_perm(a.z, a.x, 0x07060302u),
+                    __builtin_amdgcn_perm(a.w, a.y, 0x05040100u), __builtin_amdgcn_perm(a.w, a.y, 0x07060302u));
+}
+
+constexpr int kGemvBatch = 4;   // K-groups whose code loads are in flight together, per wave
+constexpr int kGemvWaves = 8;   // waves per workgroup, splitting the K-groups
+constexpr int kGemvStageMax = 128 * 1024;  // LDS bytes for the staged activation rows
+
+// NB column blocks of 16 per workgroup: every A fragment feeds NB weight row
+// blocks.  The activation rows (M <= 16) are staged once per workgroup in LDS
+// (rows padded by 16 bytes, which spreads the 16 rows of a fragment read over
+// the banks); the code loads of the first batch are in flight meanwhile.
+template <int NB>
+__global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* __restrict__ a,
+                                                               const uint32_t* __restrict__ wq,
+                                                               const uint16_t* __restrict__ w_scales,
+                                                               const uint8_t* __restrict__ w_zeros, int64_t M,
+                                                               int64_t N, int64_t K, uint16_t* __restrict__ c,
+                                                               int64_t ldc) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t gemv_lds[];
+  float (*part)[16][16 * NB + 1] = reinterpret_cast<float (*)[16][16 * NB + 1]>(gemv_lds);
+  uint8_t* a_lds = gemv_lds + sizeof(float) * kGemvWaves * 16 * (16 * NB + 1);
+  const int64_t a_row_bytes = K * 2 + 16;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
+  const int ng = (int)(K / 128);
+  const int per = (ng + kGemvWaves - 1) / kGemvWaves;
+  const int gbeg = std::min(ng, wave * per), gend = std::min(ng, gbeg + per);
+  const uint32_t* wrow[NB];
+  int64_t nrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    nrow[nb] = std::min<int64_t>(n0 + nb * 16 + n16, N - 1);   // weight row of this lane (clamped)
+    wrow[nb] = wq + nrow[nb] * (K / 8);
+  }
+  const bool a_valid = n16 < M;
+  const uint8_t* arow = a_lds + n16 * a_row_bytes;             // A row m = l % 16 of the A operand
+  const v8bf ones = as_v8bf(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+
+  uint4 code[kGemvBatch][NB];
+  float s[kGemvBatch][NB], z[kGemvBatch][NB];
+  auto fetch = [&](int b0) {
+#pragma unroll
+    for (int u = 0; u < kGemvBatch; ++u) {
+      const int G = b0 + u;
+      if (G < gend) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          code[u][nb] = ldg16_nt(wrow[nb] + (int64_t)G * 16 + g * 4);
+          const int64_t gi = nrow[nb] * ng + G;
+          s[u][nb] = __uint_as_float((uint32_t)w_scales[gi] << 16);
+          z[u][nb] = 128.0f + (float)w_zeros[gi];
+        }
+      }
+    }
+  };
+  fetch(gbeg);
+  // Stage A: M rows of K bf16, 16-byte pieces.
+  const int64_t pieces = M * (K / 8);
+  for (int64_t e = t; e < pieces; e += 64 * kGemvWaves) {
+    const int64_t m = e / (K / 8), q = e - m * (K / 8);
+    *reinterpret_cast<uint4*>(a_lds + m * a_row_bytes + q * 16) = ldg16(a + m * K + q * 8);
+  }
+  __syncthreads();
+
+  v4f acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int b0 = gbeg; b0 < gend; b0 += kGemvBatch) {
+    if (b0 != gbeg) fetch(b0);
+#pragma unroll
+    for (int u = 0; u < kGemvBatch; ++u) {
+      const int G = b0 + u;
+      if (G >= gend) break;
+      v4f P[NB], Q = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) P[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint4 av = make_uint4(0, 0, 0, 0);
+        if (a_valid) av = *reinterpret_cast<const uint4*>(arow + (int64_t)G * 256 + g * 64 + d * 16);
+        const v8bf af = as_v8bf(pair_k_k4(av));
+        Q = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, Q, 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t cw = d == 0 ? code[u][nb].x : d == 1 ? code[u][nb].y : d == 2 ? code[u][nb].z : code[u][nb].w;
+          P[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_v8bf(spread_codes(cw)), P[nb], 0, 0, 0);
+        }
+      }
+      // lane (n = l % 16, g) holds rows m = 4 g + r of column n
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[nb][r] = __builtin_fmaf(s[u][nb], __builtin_fmaf(-z[u][nb], Q[r], P[nb][r]), acc[nb][r]);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[wave][4 * g + r][nb * 16 + n16] = acc[nb][r];
+  __syncthreads();
+  for (int e = t; e < 16 * 16 * NB; e += 64 * kGemvWaves) {
+    const int m = e / (16 * NB), nn = e - m * (16 * NB);
+    const int64_t col = n0 + nn;
+    if (m < M && col < N) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGemvWaves; ++w) v += part[w][m][nn];
+      c[(int64_t)m * ldc + col] = (uint16_t)bf16_bits(v);
+    }
+  }
+}
+
+template <int NB>
+size_t gemv_lds_bytes(int64_t M, int64_t K) {
+  return sizeof(float) * kGemvWaves * 16 * (16 * NB + 1) + (size_t)M * (size_t)(K * 2 + 16);
+}
+
+template <int NB>
+hipError_t launch_gemv(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales, const uint8_t* w_zeros,
+                       int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc, hipStream_t st) {
+  const size_t lds = gemv_lds_bytes<NB>(M, K);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static bool configured[64] = {};
+  if (dev < 64 && !configured[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_w4a16_gemv<NB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(gemv_lds_bytes<NB>(0, 0) + kGemvStageMax));
+    if (e != hipSuccess) return e;
+    configured[dev] = true;
+  }
+  hipLaunchKernelGGL(k_w4a16_gemv<NB>, dim3((unsigned)((N + 16 * NB - 1) / (16 * NB))), dim3(64 * kGemvWaves), lds, st,
+                     a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales,
                              const uint8_t* w_zeros, int64_t M, int64_t N, int64_t K, uint16_t* c,
                              int64_t ldc, hipStream_t st) {
+  // Small M: the GEMV kernel when the activation rows fit its LDS stage.
+  if (M <= 16 && M * (K * 2 + 16) <= kGemvStageMax) {
+    return M <= 4 ? launch_gemv<1>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st)
+                  : launch_gemv<3>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
+  }
   if (M <= 64) {
     const dim3 grid((unsigned)((N + 31) / 32)), block(256);
     if (M <= 16) hipLaunchKernelGGL(k_w4a16_small<1>, grid, block, 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
@@ -272,7 +444,8 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16
   return hipGetLastError();
 }
 
-const char* gemm_w4a16_kernel_name(int64_t M, int64_t, int64_t) {
+const char* gemm_w4a16_kernel_name(int64_t M, int64_t, int64_t K) {
+  if (M <= 16 && M * (K * 2 + 16) <= kGemvStageMax) return M <= 4 ? "k_w4a16_gemv<16 cols>" : "k_w4a16_gemv<48 cols>";
   if (M <= 16) return "k_w4a16_small<16>";
   if (M <= 32) return "k_w4a16_small<32>";
   if (M <= 64) return "k_w4a16_small<64>";

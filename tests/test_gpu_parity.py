@@ -140,6 +140,23 @@ def test_qgemm_matches_oracle(scheme, M, N, K):
     assert err <= 5e-3   # expected ~2^-9 from the bf16 output rounding; flags a drift early
 
 
+# More output tiles than the 256 persistent workgroups, so some workgroups walk
+# two tiles through one load stream (the next tile's first K regions are
+# fetched while the current one finishes); ragged M and N tails included.  K is
+# a multiple of 256 so MXFP4 runs its region-pipelined kernel too.
+@pytest.mark.parametrize("scheme", FP_SCHEMES)
+def test_qgemm_multi_tile_workgroups(scheme):
+    M, N, K = 4300, 4200, 512
+    a = wl.small_case(7100, M, K, 1.0)
+    w = wl.small_case(7200, N if scheme != "fp8_block128" else 4224, K, 0.02)
+    aq, wq = oracle.quantize(a, scheme, "activation"), oracle.quantize(w, scheme, "weight")
+    c = pql.qgemm(pql.from_numpy(aq, DEV), pql.from_numpy(wq, DEV))
+    c_gpu = F.bf16_to_f32(down_bf16(c)).astype(np.float64)
+    err = oracle.rel_fro_error(c_gpu, oracle.gemm_ref(aq, wq))
+    assert err <= TOL, f"{scheme}: rel err {err:.3e}"
+    assert err <= 5e-3
+
+
 @pytest.mark.parametrize("M", [1, 5, 16, 33, 64, 65, 300])
 @pytest.mark.parametrize("sym", [False, True])
 def test_w4a16_gemm_matches_oracle(M, sym):
