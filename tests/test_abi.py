@@ -85,7 +85,9 @@ def test_kernel_names_distinct_per_scheme():
     fp = [names[s] for s in ("fp8_row", "fp8_block128", "mxfp8", "mxfp4")]
     assert len(set(fp)) == 4
     assert pql.kernel_name("quantize", "w4a16_asym", "activation") == ""
-    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 1, 12288, 3072).startswith("k_w4a16_small")
+    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 1, 12288, 3072).startswith("k_w4a16_gemv")
+    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 16, 12288, 3072).startswith("k_w4a16_gemv")
+    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 32, 12288, 3072).startswith("k_w4a16_small")
     assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 4096, 12288, 3072).startswith("k_w4a16_tile")
 
 
