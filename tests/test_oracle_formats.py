@@ -179,3 +179,28 @@ def test_int4_packing_bit_positions():
     p = F.pack_int4(codes)
     assert p.tolist() == [[0x76543210, 0xFEDCBA98]]
     assert np.array_equal(F.unpack_int4(p), codes)
+
+
+# ----------------------------------------------------------------- packed MX exponents
+def test_pack_mx_scales_hand_example():
+    # 2 rows x 5 blocks, chunk 4: chunk 0 holds blocks 0-3 of each row, chunk 1
+    # block 4 and three pad bytes of 127 (written out by hand).
+    s = np.array([[10, 11, 12, 13, 14],
+                  [20, 21, 22, 23, 24]], np.uint8)
+    want = np.array([[[10, 11, 12, 13], [20, 21, 22, 23]],
+                     [[14, 127, 127, 127], [24, 127, 127, 127]]], np.uint8)
+    assert np.array_equal(F.pack_mx_scales(s, 4), want)
+
+
+def test_pack_mx_scales_positions():
+    # every exponent lands at [blk // c, r, blk % c], each position is used once,
+    # and the pads are 127
+    rng = np.random.default_rng(3)
+    for rows, nblk, c in ((3, 8, 8), (5, 12, 4), (4, 36, 8), (1, 1, 4)):
+        s = rng.integers(0, 255, (rows, nblk)).astype(np.uint8)
+        p = F.pack_mx_scales(s, c)
+        assert p.shape == (-(-nblk // c), rows, c)
+        for r in range(rows):
+            for blk in range(nblk):
+                assert p[blk // c, r, blk % c] == s[r, blk]
+        assert (p.size - rows * nblk) == int(np.sum(p == 127)) - int(np.sum(s == 127))
