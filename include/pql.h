@@ -32,14 +32,19 @@
  *   FP8_ROW       codes u8 e4m3fn [rows, cols]          scales f32 [rows]
  *   FP8_BLOCK128  codes u8 e4m3fn [rows, cols]          scales f32 [rows, cols/128] (activation)
  *                                                       scales f32 [rows/128, cols/128] (weight)
- *   MXFP8         codes u8 e4m3fn [rows, cols]          scales u8 e8m0 [rows, cols/32]
- *   MXFP4         codes u8 [rows, cols/2], two e2m1,    scales u8 e8m0 [rows, cols/32]
+ *   MXFP8         codes u8 e4m3fn [rows, cols]          scales u8 e8m0, packed [G, rows, 4]
+ *   MXFP4         codes u8 [rows, cols/2], two e2m1,    scales u8 e8m0, packed [G, rows, 8]
  *                 element 2j in the low nibble
  *   W4A16_ASYM    codes u32 [rows, cols/8], element k   scales bf16 [rows, cols/128]
  *                 at bits 4*(k mod 8)                   zeros u8 [rows, cols/128] (0..15)
  *   W4A16_SYM     as W4A16_ASYM with every zero-point 8
- * All of these are K-contiguous, which is the operand order the matrix cores
+ * All codes are K-contiguous, which is the operand order the matrix cores
  * consume, so weights need no re-layout after quantization.
+ * MX scales are packed for the GEMM's staging: with c = 4 (MXFP8) or 8
+ * (MXFP4) and G = ceil(cols / (32 c)), byte [g, r, b] is the exponent of row
+ * r's 32-element block c g + b (K-elements 32 (c g + b) .. + 31); bytes past
+ * the row's last block are 127.  A chunk covers 128 bytes of codes, so the
+ * exponents one GEMM step needs for consecutive rows are consecutive bytes.
  */
 #ifndef PQL_H
 #define PQL_H

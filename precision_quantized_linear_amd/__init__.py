@@ -20,6 +20,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpql.so")
 
+# MX exponent bytes per packed chunk (one chunk = 128 bytes of codes along K).
+MX_CHUNK = {"mxfp8": 4, "mxfp4": 8}
+
 SCHEMES = {"fp8_tensor": 0, "fp8_row": 1, "fp8_block128": 2, "mxfp8": 3, "mxfp4": 4,
            "w4a16_asym": 5, "w4a16_sym": 6}
 ROLES = {"activation": 0, "weight": 1}
@@ -138,7 +141,8 @@ def _alloc_q(scheme: str, role: str, rows: int, cols: int, device) -> QTensor:
     else:
         codes = torch.empty((rows, cols if scheme != "mxfp4" else cols // 2), dtype=torch.uint8, device=device)
         if scheme in ("mxfp8", "mxfp4"):
-            scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=device)
+            c = MX_CHUNK[scheme]
+            scales = torch.empty((-(-cols // (32 * c)), rows, c), dtype=torch.uint8, device=device)
         elif scheme == "fp8_tensor":
             scales = torch.empty((1,), dtype=torch.float32, device=device)
         elif scheme == "fp8_row":
@@ -245,8 +249,29 @@ def qlinear(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None,
     return out.reshape(*lead, w.rows)
 
 
+def pack_mx_scales(scales, chunk: int):
+    """Row-major e8m0 exponents [rows, nblk] (NumPy) -> the library's packed layout
+    [ceil(nblk / chunk), rows, chunk], bytes past a row's last block 127."""
+    import numpy as np
+    s = np.asarray(scales, np.uint8)
+    rows, nblk = s.shape
+    g = -(-nblk // chunk)
+    padded = np.full((rows, g * chunk), 127, np.uint8)
+    padded[:, :nblk] = s
+    return np.ascontiguousarray(padded.reshape(rows, g, chunk).transpose(1, 0, 2))
+
+
+def unpack_mx_scales(packed, nblk: int):
+    """Inverse of pack_mx_scales: [G, rows, chunk] -> [rows, nblk]."""
+    import numpy as np
+    p = np.asarray(packed, np.uint8)
+    g, rows, chunk = p.shape
+    return np.ascontiguousarray(p.transpose(1, 0, 2).reshape(rows, g * chunk)[:, :nblk])
+
+
 def from_numpy(q: dict, device) -> QTensor:
-    """Upload a quantized tensor given as NumPy arrays in the canonical layout."""
+    """Upload a quantized tensor given as NumPy arrays in the canonical layout (MX
+    exponents row-major [rows, cols / 32]; they are packed on the way up)."""
     scheme = q["scheme"]
 
     def up(a, dtype):
@@ -263,13 +288,17 @@ def from_numpy(q: dict, device) -> QTensor:
     else:
         codes = up(q["codes"], None)
         sc = q["scales"]
+        if scheme in MX_CHUNK:
+            sc = pack_mx_scales(sc, MX_CHUNK[scheme])
         scales = up(sc, None)
         zeros = None
     return QTensor(scheme, q["role"], q["rows"], q["cols"], codes, scales, zeros)
 
 
 def to_numpy(q: QTensor) -> dict:
-    """Download a quantized tensor into NumPy arrays in the canonical layout."""
+    """Download a quantized tensor into NumPy arrays in the canonical layout (MX
+    exponents unpacked to row-major [rows, cols / 32]; the packed bytes as they are
+    in device memory under "scales_packed")."""
     import numpy as np
     codes = q.codes.cpu().numpy()
     if q.scheme.startswith("w4a16"):
@@ -279,5 +308,9 @@ def to_numpy(q: QTensor) -> dict:
     else:
         scales = q.scales.cpu().numpy()
         zeros = None
-    return {"scheme": q.scheme, "role": q.role, "rows": q.rows, "cols": q.cols,
-            "codes": codes, "scales": scales, "zeros": zeros}
+    out = {"scheme": q.scheme, "role": q.role, "rows": q.rows, "cols": q.cols,
+           "codes": codes, "scales": scales, "zeros": zeros}
+    if q.scheme in MX_CHUNK:
+        out["scales_packed"] = scales
+        out["scales"] = unpack_mx_scales(scales, q.cols // 32)
+    return out

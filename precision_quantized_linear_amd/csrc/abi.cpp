@@ -91,8 +91,8 @@ Sizes sizes_of(int scheme, int role, int64_t rows, int64_t cols) {
       s.codes = R * C;
       s.scales = role == PQL_ACTIVATION ? 4 * R * (C / 128) : 4 * (R / 128) * (C / 128);
       break;
-    case PQL_MXFP8: s.codes = R * C; s.scales = R * (C / 32); break;
-    case PQL_MXFP4: s.codes = R * C / 2; s.scales = R * (C / 32); break;
+    case PQL_MXFP8: s.codes = R * C; s.scales = R * pql::mx_packed_row_bytes(C, false); break;
+    case PQL_MXFP4: s.codes = R * C / 2; s.scales = R * pql::mx_packed_row_bytes(C, true); break;
     default: s.codes = R * C / 2; s.scales = 2 * R * (C / 128); s.zeros = R * (C / 128); break;
   }
   return s;

@@ -114,16 +114,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs g) {
       rw_reg[i] = inside ? make_uint4(vw.x, vw.y, vw.z, vw.w) : make_uint4(0, 0, 0, 0);
     }
     if constexpr (T::kMx) {
-      const int64_t nblk = g.K / 32;                     // e8m0 scales per row
-      const int64_t b0 = (int64_t)s * (T::kKPerStep / 32);
-      const uint8_t* sa = static_cast<const uint8_t*>(g.a_scales) + sa_row * nblk + b0;
-      const uint8_t* sw = static_cast<const uint8_t*>(g.w_scales) + sw_row * nblk + b0;
+      // packed exponents: a step's kKPerStep / 32 blocks are chunk s of the row
+      constexpr int kC = T::kKPerStep / 32;
+      const uint8_t* sa = static_cast<const uint8_t*>(g.a_scales) + ((int64_t)s * g.M + sa_row) * kC;
+      const uint8_t* sw = static_cast<const uint8_t*>(g.w_scales) + ((int64_t)s * g.N + sw_row) * kC;
       sa_reg.x = *reinterpret_cast<const uint32_t*>(sa);
       sw_reg.x = *reinterpret_cast<const uint32_t*>(sw);
       if constexpr (T::kFp4) {
-        const bool hi = b0 + 4 < nblk;
-        sa_reg.y = hi ? *reinterpret_cast<const uint32_t*>(sa + 4) : 0u;
-        sw_reg.y = hi ? *reinterpret_cast<const uint32_t*>(sw + 4) : 0u;
+        sa_reg.y = *reinterpret_cast<const uint32_t*>(sa + 4);
+        sw_reg.y = *reinterpret_cast<const uint32_t*>(sw + 4);
       }
     } else if constexpr (T::kBlock) {
       const int64_t ng = g.K / 128;

@@ -61,7 +61,6 @@ constexpr int kRegionBytes = 2 * kOpBytes;       // A then W
 constexpr int kScaleBytes = 1024;                // per wave: 128 row scales, then 128 column scales
 constexpr int kEpiRow = 136;                     // staged output row: 64 bf16 + 8 bytes of padding
 constexpr int kEpiBytes = 32 * kEpiRow;          // per wave: 32 output rows staged for row stores
-constexpr int kWaveBytes = kScaleBytes + kEpiBytes;
 constexpr int kPersistentCap = 256;              // one workgroup per CU
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -78,6 +77,7 @@ struct Kind {
   static constexpr int kSB = kFp4 ? 8 : 4;                 // e8m0 bytes per row and region
   static constexpr int kMxRegionBytes = kMx ? 2 * BM * kSB : 0;
   static constexpr int kWaveBytes = kEpiBytes + (kMx ? 0 : kScaleBytes);
+  static constexpr int kScLoads = kMx ? 0 : 4;              // FP8 scale loads per wave and tile
   static constexpr int kLdsBytes = 2 * kRegionBytes + 2 * kMxRegionBytes + 4 * kWaveBytes;
 };
 
@@ -98,7 +98,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int Kb = (int)(T::kFp4 ? g.K / 2 : g.K);   // bytes per operand row
   const int nreg = Kb / kRow;                      // regions (128-byte K spans) per tile
-  const int sb_row = (int)(g.K / 32);              // e8m0 bytes per row (MX)
+  // MX exponents are packed [region][row][kSB] (kSB = exponent bytes per row
+  // and 128-byte region): one region's exponents for consecutive rows are
+  // consecutive bytes, so each exponent load reads 256 contiguous bytes.
+  const int64_t plane_a = g.M * T::kSB, plane_w = g.N * T::kSB;   // bytes per region of exponents
 
   // ---- load stream.  Wave w moves A rows and W rows 64 w .. 64 w + 63 of a tile
   // for one K region, 8 rows per instruction: lane i fetches chunk
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   // refetches its last tile into a region that is never read.  MX scales ride
   // the same stream: per region, each row's kSB exponent bytes.
   const int voff = (lane >> 3) * Kb + (((lane & 7) ^ (lane >> 3)) << 4);
-  const int voff_sc = (lane / (T::kSB / 4)) * sb_row + (lane % (T::kSB / 4)) * 4;
+  const int voff_sc = lane * 4;
   struct Span {
     uint64_t base;
     int bytes;
@@ -129,8 +132,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
     ts.a = Span{reinterpret_cast<uint64_t>(g.a + m0 * Kb), mr * Kb};
     ts.w = Span{reinterpret_cast<uint64_t>(g.w + n0 * Kb), nr * Kb};
     if constexpr (T::kMx) {
-      ts.sa = Span{reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(g.a_scales) + m0 * sb_row), mr * sb_row};
-      ts.sw = Span{reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(g.w_scales) + n0 * sb_row), nr * sb_row};
+      ts.sa = Span{reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(g.a_scales) + m0 * T::kSB), mr * T::kSB};
+      ts.sw = Span{reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(g.w_scales) + n0 * T::kSB), nr * T::kSB};
     }
   };
   auto rsrc_at = [](const Span& sp, int off) __attribute__((always_inline)) {
@@ -143,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   // Load part `part` of local region `lr` (counted from the current tile's
   // start; past nreg it is the next tile's) into LDS slot `slot`.  Parts 0..15
   // are code rows (row group part / 2 of A for even parts, of W for odd ones);
-  // MX parts 16.. are the exponent rows (A, then W; 64 / (4 / kSB)... rows each).
+  // MX parts 16.. are the exponent rows (A, then W; 256 / kSB rows each).
   auto issue_part = [&](int lr, int slot, int part) __attribute__((always_inline)) {
     const bool here = lr < nreg;
     const int rg = here ? lr : lr - nreg;
@@ -159,7 +162,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
       const Span& sp = wop ? (here ? cur.sw : nxt.sw) : (here ? cur.sa : nxt.sa);
       const int rows = wave * 64 + kRowsPer * (wop ? q - per_op : q);
       const uint8_t* dst = mx_sc + (slot & 1) * T::kMxRegionBytes + (wop ? BM * T::kSB : 0) + rows * T::kSB;
-      lds_load4(rsrc_at(sp, rg * T::kSB + rows * sb_row), dst, voff_sc);
+      const int off = rows * T::kSB;
+      const int rge = std::min(rg, nreg - 1);   // past the next tile's end (nreg = 1): a region never read
+      lds_load4(make_rsrc(reinterpret_cast<const void*>(sp.base + (uint64_t)(rge * (wop ? plane_w : plane_a) + off)),
+                          std::max(sp.bytes - off, 0)),
+                dst, voff_sc);
     }
   };
   constexpr int kParts = 16 + (T::kMx ? 2 * (64 * T::kSB / 256) : 0);   // loads per wave and region
@@ -167,15 +174,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   // Fragment offsets within a region for slice h: fp8 uses chunks 4 h + g and
   // 4 h + 2 + g (g = lane / 32), fp4 chunk 2 h + g; rows + 32 i keep the swizzle.
   const int fr = lane & 31, fk = lane >> 5;
+  // They are recomputed after every epilogue from a fresh lane index, so that
+  // they are not live across it: under the epilogue's register pressure they
+  // would be spilled, and the reload's wait would also wait for the epilogue's
+  // stores and the loads in flight.
   int a_off[kSpr][kQ], w_off[kSpr][kQ];
+  auto compute_offsets = [&]() __attribute__((always_inline)) {
+    const int l = fresh_lane();
+    const int r = l & 31, c = l >> 5;
 #pragma unroll
-  for (int h = 0; h < kSpr; ++h)
+    for (int h = 0; h < kSpr; ++h)
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const int chunk = T::kFp4 ? 2 * h + fk : 4 * h + 2 * q + fk;
-      a_off[h][q] = swz128(wm * 128 + fr, chunk);
-      w_off[h][q] = kOpBytes + swz128(wn * 128 + fr, chunk);
-    }
+      for (int q = 0; q < kQ; ++q) {
+        const int chunk = T::kFp4 ? 2 * h + c : 4 * h + 2 * q + c;
+        a_off[h][q] = swz128(wm * 128 + r, chunk);
+        w_off[h][q] = kOpBytes + swz128(wn * 128 + r, chunk);
+      }
+  };
+  compute_offsets();
   // MX exponents of a region: lane l holds, for each of its 4 A (and W) row
   // blocks, the kSB bytes of row 32 i + l % 32, shifted down by l / 32 bytes so
   // that byte 2 h' of dword d is the exponent of the K-block this lane's
@@ -274,8 +290,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
       }
   };
   auto region_ptr = [&](int R) __attribute__((always_inline)) { return smem + (R & 1) * kRegionBytes; };
+  // Barrier before a region's last slice: this wave's loads of the next region
+  // have landed, and so have every other wave's.
   auto barrier_all_loads = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The first such barrier of a tile has younger operations from the tile
+  // change behind the loads it needs: vector memory operations retire in
+  // issue order, so it waits only until `pend` of them are left (the previous
+  // epilogue's row stores and the scale loads), which lets the stores drain
+  // under the next slices; -1 (their number is not fixed: edge tiles) waits
+  // for everything.
+  auto barrier_tile_start = [&](int pend) __attribute__((always_inline)) {
+    if (pend == 32 + T::kScLoads)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(32 + T::kScLoads, 0));
+    else if (pend == T::kScLoads)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(T::kScLoads, 0));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -313,12 +347,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   };
 
   // ---- epilogue of tile k: each lane owns output row m = 32 i + l % 32 of block
-  // i and, per accumulator quad, four consecutive columns.
-  auto epilogue = [&](int k) __attribute__((always_inline)) {
+  // i and, per accumulator quad, four consecutive columns.  Returns whether
+  // the wave's quarter took the interior path (exactly 32 row stores).
+  auto epilogue = [&](int k) __attribute__((always_inline)) -> bool {
     int tm, tn;
     sched.coords(k, tm, tn);
     const int64_t m0 = (int64_t)tm * BM + wm * 128, n0 = (int64_t)tn * BN + wn * 128;
     const bool interior = g.vec_store && m0 + 128 <= g.M && n0 + 128 <= g.N;   // wave-uniform
+    // Per-lane addresses come from a fresh lane index: hoisted out of the tile
+    // loop they would be spilled, and their reload would wait for the loads in
+    // flight.
+    const int el = fresh_lane();
+    const int fr = el & 31, fk = el >> 5;
     if (interior) {
       // The wave's 128 x 128 quarter is inside C.  Rows go out through LDS so
       // that each store writes whole 128-byte lines: per 32-row block i and
@@ -329,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
       // with constant offsets from one per-lane address.
       uint8_t* stg = wave_lds;
       const float4* cs4 = static_cast<const float4*>(__builtin_assume_aligned(sc_cols, 16));
-      const int rr = lane >> 3, rc = lane & 7;             // read-back: row rr + 8 q, 16-byte piece rc
+      const int rr = el >> 3, rc = el & 7;                 // read-back: row rr + 8 q, 16-byte piece rc
       uint8_t* wr = stg + fr * kEpiRow + fk * 8;
       const uint8_t* rd = stg + rr * kEpiRow + rc * 16;
       const uint32_t voff_c = (uint32_t)(rr * g.ldc * 2 + rc * 16);
@@ -361,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
           }
         }
       }
-      return;
+      return true;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -389,6 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
           }
         }
     }
+    return false;
   };
 
   using H0 = std::integral_constant<int, 0>;
@@ -398,7 +439,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
 #pragma unroll
   for (int part = 0; part < kParts; ++part) issue_part(1, 1, part);
   prefetch_scales(0);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kParts + (T::kMx ? 0 : 4), 0));   // region 0 landed
+  constexpr int kPend0 = T::kScLoads;   // issued after region 1's loads
+  int pend = kPend0;
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(kParts + kPend0, 0));   // region 0 landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read_frags(fa0, fw0, smem, H0{});
@@ -440,21 +483,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   for (int k = 0; k < my_tiles; ++k) {
     slice(H0{}, F_FIRST{}, fa0, fw0, fa1, fw1, region_ptr(R), R + 1, 0, 0);
     inner_slices(R);
+    barrier_tile_start(pend);
     for (int r = 0; r + 1 < nreg; ++r, ++R) {
-      barrier_all_loads();
       slice(std::integral_constant<int, kSpr - 1>{}, F_LOAD{}, fa1, fw1, fa0, fw0, region_ptr(R + 1), R + 1, r + 2,
             R);
       adopt_exps();
       slice(H0{}, F_MID{}, fa0, fw0, fa1, fw1, region_ptr(R + 1), R + 2, 0, 0);
       inner_slices(R + 1);
+      barrier_all_loads();
     }
     // The tile's last slice: the next tile's first fragments are read after
     // the epilogue, which keeps their registers free while it runs.
-    barrier_all_loads();
     slice(std::integral_constant<int, kSpr - 1>{}, F_END{}, fa1, fw1, fa0, fw0, region_ptr(R + 1), R + 1, nreg + 1,
           R);
     ++R;
-    epilogue(k);
+    pend = epilogue(k) ? 32 + T::kScLoads : -1;
+    compute_offsets();
     read_frags(fa0, fw0, region_ptr(R), H0{});
     read_exps(eca, ecw, R);
     cur = nxt;

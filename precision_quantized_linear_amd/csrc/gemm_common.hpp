@@ -75,6 +75,15 @@ __device__ __forceinline__ void lds_load4(v4i rsrc, const uint8_t* lds, int voff
                : "memory", "m0");
 }
 
+// The lane index, computed afresh where it is called: the compiler can neither
+// merge it with an earlier copy nor keep one live across the code in between,
+// so values derived from it are rematerialised instead of being spilled.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ uint4 lds16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __device__ __forceinline__ v8i cat(uint4 lo, uint4 hi) {

@@ -12,6 +12,16 @@ namespace pql {
 // Number of per-block partial maxima the per-tensor amax pass writes.
 constexpr int kTensorAmaxBlocks = 1024;
 
+// Packed MX exponents: the e8m0 bytes of a [rows, cols] operand are stored as
+// [ceil(cols / (32 c)), rows, c] with c = 4 (MXFP8) or 8 (MXFP4) -- byte b of
+// chunk g of row r is the exponent of 32-block c g + b, and bytes past the
+// row's last block hold 127.  One chunk covers the 128 K-bytes of codes that
+// the GEMM stages per step, so a step's exponents for consecutive rows are
+// consecutive bytes.
+constexpr int mx_chunk(bool fp4) { return fp4 ? 8 : 4; }
+constexpr int64_t mx_chunks(int64_t cols, bool fp4) { return (cols / 32 + mx_chunk(fp4) - 1) / mx_chunk(fp4); }
+constexpr int64_t mx_packed_row_bytes(int64_t cols, bool fp4) { return mx_chunks(cols, fp4) * mx_chunk(fp4); }
+
 // ---------------------------------------------------------------- quantize
 hipError_t launch_quant_fp8_tensor(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                    uint8_t* codes, float* scale, float* ws_partials, hipStream_t st);

@@ -266,7 +266,14 @@ __global__ __launch_bounds__(256) void k_mx(const uint16_t* __restrict__ x, int6
     const int64_t c = g.c0 + 64 * u;
     const int X = mx_shared_exponent(group4_max(chunk_absmax(v[u])), FP4 ? 2 : 8);
     if (c >= cpr) continue;
-    if ((c & 3) == 0) scales[g.row * (cols >> 5) + (c >> 2)] = (uint8_t)(X + 127);
+    if ((c & 3) == 0) {   // packed exponent layout: [chunk][row][kC]
+      constexpr int kC = mx_chunk(FP4);
+      const int64_t b = c >> 2;
+      uint8_t* sp = scales + ((b / kC) * rows + g.row) * kC + (b % kC);
+      sp[0] = (uint8_t)(X + 127);
+      if (b == (cols >> 5) - 1)   // the row's last block fills the rest of its chunk
+        for (int p = 1; p < kC - (int)(b % kC); ++p) sp[p] = 127;
+    }
     const float inv = exp2i(-X);
     float f[8];
     chunk_to_f32(v[u], f);
@@ -393,7 +400,8 @@ __global__ __launch_bounds__(256) void k_dequant(int kind, const uint8_t* __rest
     if (kind <= 5) {
       if (kind == 5) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (cols >> 1) + c * 4);
-        const float sc = e8m0_value(static_cast<const uint8_t*>(scales)[r * (cols >> 5) + (c >> 2)]);
+        const int64_t b = c >> 2;
+        const float sc = e8m0_value(static_cast<const uint8_t*>(scales)[((b >> 3) * rows + r) * 8 + (b & 7)]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((w >> (4 * j)) & 0xF) * sc;
       } else {
@@ -405,7 +413,10 @@ __global__ __launch_bounds__(256) void k_dequant(int kind, const uint8_t* __rest
           case 1: sc = sf[r]; break;
           case 2: sc = sf[r * (cols >> 7) + (c >> 4)]; break;
           case 3: sc = sf[(r >> 7) * (cols >> 7) + (c >> 4)]; break;
-          default: sc = e8m0_value(static_cast<const uint8_t*>(scales)[r * (cols >> 5) + (c >> 2)]);
+          default: {
+            const int64_t b = c >> 2;
+            sc = e8m0_value(static_cast<const uint8_t*>(scales)[((b >> 2) * rows + r) * 4 + (b & 3)]);
+          }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[j] = e4m3_decode((w.x >> (8 * j)) & 0xFF) * sc;

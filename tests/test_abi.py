@@ -43,6 +43,9 @@ def test_quantized_sizes():
     assert _sizes("fp8_block128", "weight", 13824, 5120) == (13824 * 5120, 4 * 108 * 40, 0)
     assert _sizes("mxfp8", "activation", 20280, 5120) == (20280 * 5120, 20280 * 160, 0)
     assert _sizes("mxfp4", "weight", 5120, 5120) == (5120 * 2560, 5120 * 160, 0)
+    # packed exponents round each row up to whole chunks (4 bytes MXFP8, 8 bytes MXFP4)
+    assert _sizes("mxfp8", "activation", 3, 96) == (3 * 96, 3 * 4, 0)
+    assert _sizes("mxfp4", "activation", 3, 384) == (3 * 192, 3 * 16, 0)
     assert _sizes("w4a16_asym", "weight", 12288, 3072) == (12288 * 1536, 2 * 12288 * 24, 12288 * 24)
 
 

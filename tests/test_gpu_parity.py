@@ -23,6 +23,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TOL = 1e-2
 FP_SCHEMES = ("fp8_tensor", "fp8_row", "fp8_block128", "mxfp8", "mxfp4")
+MX_CHUNK = {"mxfp8": 4, "mxfp4": 8}   # exponent bytes per packed chunk (128 bytes of codes)
 
 
 def up(bits: np.ndarray) -> torch.Tensor:
@@ -90,6 +91,8 @@ def test_quantize_bit_exact(scheme, role, rows, cols):
     ref = oracle.quantize(x, scheme, role)
     got = pql.to_numpy(pql.quantize(up(x), scheme, role))
     assert_q_equal(got, ref, f"{scheme}/{role} {rows}x{cols}")
+    if scheme in MX_CHUNK:   # the packed device layout itself, pad bytes included
+        assert np.array_equal(got["scales_packed"], F.pack_mx_scales(ref["scales"], MX_CHUNK[scheme]))
 
 
 @pytest.mark.parametrize("scheme", FP_SCHEMES + ("w4a16_asym",))
