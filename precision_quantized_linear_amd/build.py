@@ -37,9 +37,16 @@ def compile_flags():
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# Per-file code-generation options.  The block-128 GEMM promotes every matrix-core
+# partial product with VALU FMAs; taking the MFMA results in VGPRs (instead of
+# AGPRs) spares one v_accvgpr_read per element.
+EXTRA_FLAGS = {"gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OUT, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *compile_flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

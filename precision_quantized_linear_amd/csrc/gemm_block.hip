@@ -75,52 +75,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
   uint8_t* const sw_lds = sa_lds + kSlots * kSaBytes;                    // [slot][wave][64] floats
   uint8_t* const epi = sw_lds + kSlots * 4 * kSwBytes + wave * kEpiBytes;
 
-  // ---- load stream (see the file comment).  Spans cover the tile's valid rows
-  // only, so rows past M / N read 0.
-  const int voff = (lane >> 3) * Kb + (((lane & 7) ^ (lane >> 3)) << 4);
-  const int voff_sa = lane * G * 4;
-  struct Span {
-    uint64_t base;
-    int bytes;
+  // ---- load stream (see the file comment).  One buffer descriptor per operand
+  // and tile covers the tile's valid rows; each load's per-lane offset (fixed
+  // for the whole kernel) holds its row and swizzled chunk, so rows past M / N
+  // fall outside the descriptor and read 0, and the region's K offset rides in
+  // the scalar offset, which stays inside a row.  Code part p of A is rows
+  // 64 wave + 8 p .. + 7 of the tile, of W rows 32 wave + 8 p .. + 7; the
+  // activation scales are rows 64 wave .. + 63, one lane per row.
+  const int vchunk = ((lane & 7) ^ (lane >> 3)) << 4;
+  int voff_a[8], voff_w[4];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) voff_a[p] = (wave * 64 + 8 * p + (lane >> 3)) * Kb + vchunk;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) voff_w[p] = (wave * 32 + 8 * p + (lane >> 3)) * Kb + vchunk;
+  const int voff_sa = (wave * 64 + lane) * G * 4;
+  struct TileRsrc {
+    v4i a, w, sa, sw;   // codes, activation scales, this tile's row of weight scales
   };
-  struct TileSpans {
-    Span a, w, sa, sw;   // codes, activation scales, this tile's row of weight scales
-  };
-  auto tile_spans = [&](int k, TileSpans& ts) __attribute__((always_inline)) {
+  auto tile_rsrc = [&](int k, TileRsrc& tr) __attribute__((always_inline)) {
     int tm, tn;
     sched.coords(std::min(k, my_tiles - 1), tm, tn);
     tm = __builtin_amdgcn_readfirstlane(tm);
     tn = __builtin_amdgcn_readfirstlane(tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int mr = (int)std::min<int64_t>(BM, g.M - m0), nr = (int)std::min<int64_t>(BN, g.N - n0);
-    ts.a = Span{reinterpret_cast<uint64_t>(g.a + m0 * Kb), mr * Kb};
-    ts.w = Span{reinterpret_cast<uint64_t>(g.w + n0 * Kb), nr * Kb};
-    ts.sa = Span{reinterpret_cast<uint64_t>(sa_g + m0 * G), mr * G * 4};
-    ts.sw = Span{reinterpret_cast<uint64_t>(sw_g + (n0 / 128) * G), G * 4};
+    tr.a = make_rsrc(g.a + m0 * Kb, mr * Kb);
+    tr.w = make_rsrc(g.w + n0 * Kb, nr * Kb);
+    tr.sa = make_rsrc(sa_g + m0 * G, mr * G * 4);
+    tr.sw = make_rsrc(sw_g + (n0 / 128) * G, G * 4);
   };
-  auto rsrc_at = [](const Span& sp, int off) __attribute__((always_inline)) {
-    return make_rsrc(reinterpret_cast<const void*>(sp.base + (uint64_t)off), std::max(sp.bytes - off, 0));
-  };
-  TileSpans cur, nxt;
-  tile_spans(0, cur);
-  tile_spans(1, nxt);
-  // Part `part` (0..13) of local region `lr` (past G: the next tile's) into slot `slot`.
-  auto issue_part = [&](int lr, int slot, int part) __attribute__((always_inline)) {
-    const bool here = lr < G;
-    const TileSpans& ts = here ? cur : nxt;
-    const int rg = here ? lr : lr - G;
+  TileRsrc cur, nxt;
+  tile_rsrc(0, cur);
+  tile_rsrc(1, nxt);
+  // Part `part` (0..13) of K-group `rg` of tile `tr` into slot `slot`.
+  auto issue_part = [&](const TileRsrc& tr, int rg, int slot, int part) __attribute__((always_inline)) {
     uint8_t* const base = smem + slot * kRegion;
-    if (part < 8) {                                  // A rows wave * 64 + 8 part
-      const int rows = wave * 64 + 8 * part;
-      lds_load16(rsrc_at(ts.a, rg * kRow + rows * Kb), base + rows * kRow, voff);
-    } else if (part < 12) {                          // W rows wave * 32 + 8 (part - 8)
-      const int rows = wave * 32 + 8 * (part - 8);
-      lds_load16(rsrc_at(ts.w, rg * kRow + rows * Kb), base + kAOp + rows * kRow, voff);
-    } else if (part == 12) {                         // A scales of rows wave * 64 .. + 63
-      lds_load4(rsrc_at(ts.sa, rg * 4 + wave * 64 * G * 4), sa_lds + slot * kSaBytes + wave * 256, voff_sa);
-    } else {                                         // the W scale, to every lane's slot
-      lds_load4(rsrc_at(ts.sw, rg * 4), sw_lds + (slot * 4 + wave) * kSwBytes, 0);
-    }
+    if (part < 8)
+      lds_load16_so(tr.a, base + (wave * 64 + 8 * part) * kRow, voff_a[part], rg * kRow);
+    else if (part < 12)
+      lds_load16_so(tr.w, base + kAOp + (wave * 32 + 8 * (part - 8)) * kRow, voff_w[part - 8], rg * kRow);
+    else if (part == 12)
+      lds_load4_so(tr.sa, sa_lds + slot * kSaBytes + wave * 256, voff_sa, rg * 4);
+    else   // the W scale, to every lane's slot
+      lds_load4_so(tr.sw, sw_lds + (slot * 4 + wave) * kSwBytes, 0, rg * 4);
+  };
+  // Local region `lr` counts from the current tile's start; past G it is the
+  // next tile's.  Past the next tile's end (only when G < 3, one tile per
+  // workgroup) the group is clamped: those slots are never read.
+  auto region_src = [&](int lr, int& rg) __attribute__((always_inline)) -> const TileRsrc& {
+    const bool here = lr < G;
+    rg = std::min(here ? lr : lr - G, G - 1);
+    return here ? cur : nxt;
   };
 
   // ---- fragments: 16x16x128 operands, lane row l % 16, chunks g4 and 4 + g4.
@@ -171,6 +176,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
     constexpr bool reads = decltype(reads_c)::value;
     const uint8_t* next = smem + ((R + 1) % kSlots) * kRegion;
     const int load_slot = R % kSlots;
+    int load_rg;
+    const TileRsrc& load_tr = region_src(lr + 3, load_rg);
     v4f_t P[4];
 #pragma unroll
     for (int s = 0; s < 34; ++s) {
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
         for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(P[p & 3][e], sc[i], acc[i][j][e]);
       }
       if (reads && s < 24) read_one(na, nw, next, s);
-      if ((s & 1) == 0 && s < 2 * kLoads) issue_part(lr + 3, load_slot, s >> 1);
+      if ((s & 1) == 0 && s < 2 * kLoads) issue_part(load_tr, load_rg, load_slot, s >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (reads) read_scales(nsc, (R + 1) % kSlots);
@@ -249,9 +256,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
 
   // ---- prologue: regions 0, 1, 2 in flight; then region 0's fragments.
 #pragma unroll
-  for (int s = 0; s < kSlots; ++s)
+  for (int s = 0; s < kSlots; ++s) {
+    int rg;
+    const TileRsrc& tr = region_src(s, rg);
 #pragma unroll
-    for (int part = 0; part < kLoads; ++part) issue_part(s, s, part);
+    for (int part = 0; part < kLoads; ++part) issue_part(tr, rg, s, part);
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoads, 0));   // region 0 landed
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
     // (complete: the last barrier waited for region R).
     read_all(fa0, fw0, sc0, R % kSlots);
     cur = nxt;
-    tile_spans(k + 2, nxt);
+    tile_rsrc(k + 2, nxt);
   }
   __builtin_amdgcn_s_waitcnt(0);
 }

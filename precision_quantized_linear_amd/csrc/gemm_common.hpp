@@ -67,6 +67,24 @@ __device__ __forceinline__ void lds_load16(v4i rsrc, const uint8_t* lds, int vof
                : "memory", "m0");
 }
 
+// The same with a scalar offset: 16 bytes per lane from rsrc + voff + soff.
+// Only voff is checked against the descriptor's byte count, so voff must carry
+// everything that can leave the valid range (the row) and soff only offsets
+// that stay inside a valid row.
+__device__ __forceinline__ void lds_load16_so(v4i rsrc, const uint8_t* lds, int voff, int soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff),
+               "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_load4_so(v4i rsrc, const uint8_t* lds, int voff, int soff) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0), "v"(voff),
+               "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 // One direct-to-LDS load of 4 bytes per lane: rsrc + voff into LDS at lds + 4 * lane.
 __device__ __forceinline__ void lds_load4(v4i rsrc, const uint8_t* lds, int voff) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
