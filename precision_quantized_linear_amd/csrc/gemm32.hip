@@ -106,21 +106,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   // ---- load stream.  Wave w moves A rows and W rows 64 w .. 64 w + 63 of a tile
   // for one K region, 8 rows per instruction: lane i fetches chunk
   // (i % 8) ^ (i / 8) of row i / 8 of the group, which lands at LDS offset 16 i,
-  // the swizzled position.  Each load's descriptor starts at its row group and
-  // K region and covers only the tile's valid rows (rows past M / N read 0), so
-  // the per-lane offset is the one loop-invariant register `voff`.  Regions
-  // past a tile's end come from the next tile, whose (base, bytes) pairs are
-  // kept beside the current ones; past this workgroup's last tile the stream
-  // refetches its last tile into a region that is never read.  MX scales ride
-  // the same stream: per region, each row's kSB exponent bytes.
-  const int voff = (lane >> 3) * Kb + (((lane & 7) ^ (lane >> 3)) << 4);
+  // the swizzled position.  One buffer descriptor per operand and tile covers
+  // the tile's valid rows; the per-lane offset of row group p (fixed for the
+  // whole kernel, shared by A and W) holds the row, so rows past M / N fall
+  // outside the descriptor and read 0, and the region's K offset rides in the
+  // scalar offset, which stays inside a row.  Regions past a tile's end come
+  // from the next tile, whose descriptors are kept beside the current ones;
+  // past this workgroup's last tile the stream refetches its last tile into a
+  // region that is never read.  MX scales ride the same stream: per region,
+  // each row's kSB exponent bytes.
+  const int vchunk = ((lane & 7) ^ (lane >> 3)) << 4;
+  int voff_p[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) voff_p[p] = (wave * 64 + 8 * p + (lane >> 3)) * Kb + vchunk;
   const int voff_sc = lane * 4;
   struct Span {
     uint64_t base;
     int bytes;
   };
   struct TileSpans {
-    Span a, w, sa, sw;
+    v4i a, w;      // codes
+    Span sa, sw;   // MX exponents
   };
   auto tile_spans = [&](int k, TileSpans& ts) __attribute__((always_inline)) {
     int tm, tn;
@@ -129,15 +135,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
     tn = __builtin_amdgcn_readfirstlane(tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
     const int mr = (int)std::min<int64_t>(BM, g.M - m0), nr = (int)std::min<int64_t>(BN, g.N - n0);
-    ts.a = Span{reinterpret_cast<uint64_t>(g.a + m0 * Kb), mr * Kb};
-    ts.w = Span{reinterpret_cast<uint64_t>(g.w + n0 * Kb), nr * Kb};
+    ts.a = make_rsrc(g.a + m0 * Kb, mr * Kb);
+    ts.w = make_rsrc(g.w + n0 * Kb, nr * Kb);
     if constexpr (T::kMx) {
       ts.sa = Span{reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(g.a_scales) + m0 * T::kSB), mr * T::kSB};
       ts.sw = Span{reinterpret_cast<uint64_t>(static_cast<const uint8_t*>(g.w_scales) + n0 * T::kSB), nr * T::kSB};
     }
-  };
-  auto rsrc_at = [](const Span& sp, int off) __attribute__((always_inline)) {
-    return make_rsrc(reinterpret_cast<const void*>(sp.base + (uint64_t)off), std::max(sp.bytes - off, 0));
   };
   TileSpans cur, nxt;
   tile_spans(0, cur);
@@ -147,29 +150,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   // start; past nreg it is the next tile's) into LDS slot `slot`.  Parts 0..15
   // are code rows (row group part / 2 of A for even parts, of W for odd ones);
   // MX parts 16.. are the exponent rows (A, then W; 256 / kSB rows each).
-  auto issue_part = [&](int lr, int slot, int part) __attribute__((always_inline)) {
-    const bool here = lr < nreg;
-    const int rg = here ? lr : lr - nreg;
+  // `ts` / `rg` are the tile and its region, from load_src().
+  auto issue_part = [&](const TileSpans& ts, int rg, int slot, int part) __attribute__((always_inline)) {
     if (part < 16) {
-      const Span& sp = (part & 1) ? (here ? cur.w : nxt.w) : (here ? cur.a : nxt.a);
       const int rows = wave * 64 + 8 * (part >> 1);
       const uint8_t* dst = smem + (slot & 1) * kRegionBytes + (part & 1) * kOpBytes + rows * kRow;
-      lds_load16(rsrc_at(sp, rg * kRow + rows * Kb), dst, voff);
+      lds_load16_so((part & 1) ? ts.w : ts.a, dst, voff_p[part >> 1], rg * kRow);
     } else if constexpr (T::kMx) {
       constexpr int kRowsPer = 256 / T::kSB;                     // exponent rows per instruction
       const int q = part - 16, per_op = 64 / kRowsPer;
       const bool wop = q >= per_op;
-      const Span& sp = wop ? (here ? cur.sw : nxt.sw) : (here ? cur.sa : nxt.sa);
+      const Span& sp = wop ? ts.sw : ts.sa;
       const int rows = wave * 64 + kRowsPer * (wop ? q - per_op : q);
       const uint8_t* dst = mx_sc + (slot & 1) * T::kMxRegionBytes + (wop ? BM * T::kSB : 0) + rows * T::kSB;
       const int off = rows * T::kSB;
-      const int rge = std::min(rg, nreg - 1);   // past the next tile's end (nreg = 1): a region never read
-      lds_load4(make_rsrc(reinterpret_cast<const void*>(sp.base + (uint64_t)(rge * (wop ? plane_w : plane_a) + off)),
+      lds_load4(make_rsrc(reinterpret_cast<const void*>(sp.base + (uint64_t)(rg * (wop ? plane_w : plane_a) + off)),
                           std::max(sp.bytes - off, 0)),
                 dst, voff_sc);
     }
   };
   constexpr int kParts = 16 + (T::kMx ? 2 * (64 * T::kSB / 256) : 0);   // loads per wave and region
+  // Local region `lr` counts from the current tile's start; past nreg it is the
+  // next tile's, and past the next tile's end (nreg = 1: one tile per
+  // workgroup) it is clamped into a region that is never read.
+  auto load_src = [&](int lr, int& rg) __attribute__((always_inline)) -> TileSpans {
+    const bool here = lr < nreg;
+    rg = std::min(here ? lr : lr - nreg, nreg - 1);
+    return here ? cur : nxt;   // by value: a select of the (scalar) fields
+  };
 
   // Fragment offsets within a region for slice h: fp8 uses chunks 4 h + g and
   // 4 h + 2 + g (g = lane / 32), fp4 chunk 2 h + g; rows + 32 i keep the swizzle.
@@ -255,6 +263,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
     constexpr bool region_end = h == kSpr - 1;
     constexpr int d = T::kFp4 ? (h >> 1) : 0;
     constexpr int opsel = T::kFp4 ? 2 * (h & 1) : 2 * h;
+    int load_rg = 0;
+    const TileSpans load_ts = load_src(load_lr, load_rg);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -283,8 +293,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
           }
         }
         if constexpr (loads) {
-          issue_part(load_lr, load_slot, k);
-          if (k < kParts - 16) issue_part(load_lr, load_slot, 16 + k);
+          issue_part(load_ts, load_rg, load_slot, k);
+          if (k < kParts - 16) issue_part(load_ts, load_rg, load_slot, 16 + k);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -359,85 +369,82 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
     // flight.
     const int el = fresh_lane();
     const int fr = el & 31, fk = el >> 5;
-    if (interior) {
-      // The wave's 128 x 128 quarter is inside C.  Rows go out through LDS so
-      // that each store writes whole 128-byte lines: per 32-row block i and
-      // 64-column half p, lanes write their bf16 quads (8 bytes) into a 32-row
-      // staging block, then read it back as 16-byte row pieces (8 lanes per
-      // row, 8 rows per instruction).  Staged rows are padded to 136 bytes,
-      // which keeps both the quad writes and the row reads on distinct banks
-      // with constant offsets from one per-lane address.
-      uint8_t* stg = wave_lds;
-      const float4* cs4 = static_cast<const float4*>(__builtin_assume_aligned(sc_cols, 16));
-      const int rr = el >> 3, rc = el & 7;                 // read-back: row rr + 8 q, 16-byte piece rc
-      uint8_t* wr = stg + fr * kEpiRow + fk * 8;
-      const uint8_t* rd = stg + rr * kEpiRow + rc * 16;
-      const uint32_t voff_c = (uint32_t)(rr * g.ldc * 2 + rc * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float rs = T::kMx ? 1.0f : sc_rows[i * 32 + fr];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int j = 2 * p + jj;
-            float4 cs[4];
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) cs[rq] = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : cs4[j * 8 + rq * 2 + fk];
-            const v16f a = acc[i][j];
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq)
-              *reinterpret_cast<uint2*>(wr + (jj * 8 + rq * 2) * 8) =
-                  uint2{pack_bf16x2(out_val(a[4 * rq + 0], rs, cs[rq].x), out_val(a[4 * rq + 1], rs, cs[rq].y)),
-                        pack_bf16x2(out_val(a[4 * rq + 2], rs, cs[rq].z), out_val(a[4 * rq + 3], rs, cs[rq].w))};
-            __builtin_amdgcn_sched_barrier(0);   // one accumulator block at a time
-          }
-#pragma unroll
-          for (int qr = 0; qr < 4; ++qr) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow + 8);
-            char* base = reinterpret_cast<char*>(g.c + (m0 + i * 32 + 8 * qr) * g.ldc + n0 + p * 64);
-            *reinterpret_cast<uint4*>(base + voff_c) = uint4{lo.x, lo.y, hi.x, hi.y};
-          }
-        }
-      }
-      return true;
-    }
+    // Rows go out through LDS so that each store writes whole 128-byte lines:
+    // per 32-row block i and 64-column half p, lanes write their bf16 quads
+    // (8 bytes) into a 32-row staging block, then read it back as 16-byte row
+    // pieces (8 lanes per row, 8 rows per instruction).  Staged rows are padded
+    // to 136 bytes, which keeps both the quad writes and the row reads on
+    // distinct banks with constant offsets from one per-lane address.  Interior
+    // quarters store every piece; edge quarters (and C without 16-byte rows)
+    // mask rows past M and columns past N.  One staging path for both keeps
+    // the accumulators' reads in one place, which the register allocator needs.
+    uint8_t* stg = wave_lds;
+    const float4* cs4 = static_cast<const float4*>(__builtin_assume_aligned(sc_cols, 16));
+    const int rr = el >> 3, rc = el & 7;                 // read-back: row rr + 8 q, 16-byte piece rc
+    uint8_t* wr = stg + fr * kEpiRow + fk * 8;
+    const uint8_t* rd = stg + rr * kEpiRow + rc * 16;
+    const uint32_t voff_c = (uint32_t)(rr * g.ldc * 2 + rc * 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t row = m0 + i * 32 + fr;
       const float rs = T::kMx ? 1.0f : sc_rows[i * 32 + fr];
-      uint16_t* dst_row = g.c + row * g.ldc;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int p = 0; p < 2; ++p) {
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int cl = j * 32 + rq * 8 + fk * 4;
-          const float4 cs = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const float4*>(sc_cols + cl);
-          const uint32_t lo = pack_bf16x2(out_val(acc[i][j][4 * rq + 0], rs, cs.x), out_val(acc[i][j][4 * rq + 1], rs, cs.y));
-          const uint32_t hi = pack_bf16x2(out_val(acc[i][j][4 * rq + 2], rs, cs.z), out_val(acc[i][j][4 * rq + 3], rs, cs.w));
-          const int64_t col = n0 + cl;
-          if (row < g.M) {
-            if (g.vec_store && col + 4 <= g.N) {
-              *reinterpret_cast<uint2*>(dst_row + col) = uint2{lo, hi};
-            } else {
-              const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * p + jj;
+          float4 cs[4];
 #pragma unroll
-              for (int c = 0; c < 4; ++c)
-                if (col + c < g.N) dst_row[col + c] = e[c];
+          for (int rq = 0; rq < 4; ++rq) cs[rq] = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : cs4[j * 8 + rq * 2 + fk];
+          const v16f a = acc[i][j];
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *reinterpret_cast<uint2*>(wr + (jj * 8 + rq * 2) * 8) =
+                uint2{pack_bf16x2(out_val(a[4 * rq + 0], rs, cs[rq].x), out_val(a[4 * rq + 1], rs, cs[rq].y)),
+                      pack_bf16x2(out_val(a[4 * rq + 2], rs, cs[rq].z), out_val(a[4 * rq + 3], rs, cs[rq].w))};
+          __builtin_amdgcn_sched_barrier(0);   // one accumulator block at a time
+        }
+#pragma unroll
+        for (int qr = 0; qr < 4; ++qr) {
+          const uint2 lo = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow);
+          const uint2 hi = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow + 8);
+          if (interior) {
+            char* base = reinterpret_cast<char*>(g.c + (m0 + i * 32 + 8 * qr) * g.ldc + n0 + p * 64);
+            *reinterpret_cast<uint4*>(base + voff_c) = uint4{lo.x, lo.y, hi.x, hi.y};
+          } else {
+            const int64_t row = m0 + i * 32 + 8 * qr + rr, col = n0 + p * 64 + rc * 8;
+            if (row < g.M) {
+              uint16_t* dst = g.c + row * g.ldc + col;
+              if (g.vec_store && col + 8 <= g.N) {
+                *reinterpret_cast<uint4*>(dst) = uint4{lo.x, lo.y, hi.x, hi.y};
+              } else {
+                const uint32_t wds[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                  if (col + c < g.N) dst[c] = (uint16_t)(wds[c >> 1] >> (16 * (c & 1)));
+              }
             }
           }
         }
+        __builtin_amdgcn_sched_barrier(0);   // the staging block is read before it is rewritten
+      }
     }
-    return false;
+    return interior;
   };
 
   using H0 = std::integral_constant<int, 0>;
   // ---- prologue: regions 0 and 1 in flight, then slice 0's fragments.
 #pragma unroll
-  for (int part = 0; part < kParts; ++part) issue_part(0, 0, part);
+  for (int part = 0; part < kParts; ++part) {
+    int rg;
+    const TileSpans ts = load_src(0, rg);
+    issue_part(ts, rg, 0, part);
+  }
 #pragma unroll
-  for (int part = 0; part < kParts; ++part) issue_part(1, 1, part);
+  for (int part = 0; part < kParts; ++part) {
+    int rg;
+    const TileSpans ts = load_src(1, rg);
+    issue_part(ts, rg, 1, part);
+  }
   prefetch_scales(0);
   constexpr int kPend0 = T::kScLoads;   // issued after region 1's loads
   int pend = kPend0;

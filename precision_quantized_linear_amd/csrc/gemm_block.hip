@@ -122,10 +122,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
   // Local region `lr` counts from the current tile's start; past G it is the
   // next tile's.  Past the next tile's end (only when G < 3, one tile per
   // workgroup) the group is clamped: those slots are never read.
-  auto region_src = [&](int lr, int& rg) __attribute__((always_inline)) -> const TileRsrc& {
+  auto region_src = [&](int lr, int& rg) __attribute__((always_inline)) -> TileRsrc {
     const bool here = lr < G;
     rg = std::min(here ? lr : lr - G, G - 1);
-    return here ? cur : nxt;
+    return here ? cur : nxt;   // by value: a select of the (scalar) fields
   };
 
   // ---- fragments: 16x16x128 operands, lane row l % 16, chunks g4 and 4 + g4.
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
     const uint8_t* next = smem + ((R + 1) % kSlots) * kRegion;
     const int load_slot = R % kSlots;
     int load_rg;
-    const TileRsrc& load_tr = region_src(lr + 3, load_rg);
+    const TileRsrc load_tr = region_src(lr + 3, load_rg);
     v4f_t P[4];
 #pragma unroll
     for (int s = 0; s < 34; ++s) {
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
 #pragma unroll
   for (int s = 0; s < kSlots; ++s) {
     int rg;
-    const TileRsrc& tr = region_src(s, rg);
+    const TileRsrc tr = region_src(s, rg);
 #pragma unroll
     for (int part = 0; part < kLoads; ++part) issue_part(tr, rg, s, part);
   }

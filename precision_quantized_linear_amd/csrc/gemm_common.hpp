@@ -71,7 +71,17 @@ __device__ __forceinline__ void lds_load16(v4i rsrc, const uint8_t* lds, int vof
 // Only voff is checked against the descriptor's byte count, so voff must carry
 // everything that can leave the valid range (the row) and soff only offsets
 // that stay inside a valid row.
+// The operands are uniform; readfirstlane keeps them in SGPRs (free when the
+// compiler already holds them there, a move when register pressure parked
+// them in VGPRs).
+__device__ __forceinline__ v4i uniform4(v4i r) {
+  return v4i{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+             __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+
 __device__ __forceinline__ void lds_load16_so(v4i rsrc, const uint8_t* lds, int voff, int soff) {
+  rsrc = uniform4(rsrc);
+  soff = __builtin_amdgcn_readfirstlane(soff);
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff),
                "s"(rsrc), "s"(soff)
@@ -79,6 +89,8 @@ __device__ __forceinline__ void lds_load16_so(v4i rsrc, const uint8_t* lds, int 
 }
 
 __device__ __forceinline__ void lds_load4_so(v4i rsrc, const uint8_t* lds, int voff, int soff) {
+  rsrc = uniform4(rsrc);
+  soff = __builtin_amdgcn_readfirstlane(soff);
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds" ::"s"(m0), "v"(voff),
                "s"(rsrc), "s"(soff)
