@@ -197,8 +197,8 @@ def all_workloads(torch, pql, steps, warmup, only=None):
     codes, zeros, scales = wl.int4_weight_parts(w)
     wq = pql.QTensor("w4a16_asym", "weight", w.N, w.K,
                      torch.from_numpy(wl.pack_int4_codes(codes).view(np.int32)).cuda(),
-                     torch.from_numpy(scales.view(np.int16)).view(torch.bfloat16).cuda(),
-                     torch.from_numpy(zeros).cuda())
+                     torch.from_numpy(np.ascontiguousarray(scales.T).view(np.int16)).view(torch.bfloat16).cuda(),
+                     torch.from_numpy(np.ascontiguousarray(zeros.T)).cuda())   # group-major
     for M in w.m_sweep:
         a0 = up(torch, wl.activation(w, M))
         R = rotation(a0.numel() * 2 + w.N * w.K // 2)

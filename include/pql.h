@@ -35,11 +35,14 @@
  *   MXFP8         codes u8 e4m3fn [rows, cols]          scales u8 e8m0, packed [G, rows, 4]
  *   MXFP4         codes u8 [rows, cols/2], two e2m1,    scales u8 e8m0, packed [G, rows, 8]
  *                 element 2j in the low nibble
- *   W4A16_ASYM    codes u32 [rows, cols/8], element k   scales bf16 [rows, cols/128]
- *                 at bits 4*(k mod 8)                   zeros u8 [rows, cols/128] (0..15)
+ *   W4A16_ASYM    codes u32 [rows, cols/8], element k   scales bf16 [cols/128, rows]
+ *                 at bits 4*(k mod 8)                   zeros u8 [cols/128, rows] (0..15)
  *   W4A16_SYM     as W4A16_ASYM with every zero-point 8
  * All codes are K-contiguous, which is the operand order the matrix cores
  * consume, so weights need no re-layout after quantization.
+ * W4A16 scales and zero-points are group-major ([group, row]): one K-group's
+ * values for consecutive weight rows are consecutive, which is how the GEMM
+ * stages them.
  * MX scales are packed for the GEMM's staging: with c = 4 (MXFP8) or 8
  * (MXFP4) and G = ceil(cols / (32 c)), byte [g, r, b] is the exponent of row
  * r's 32-element block c g + b (K-elements 32 (c g + b) .. + 31); bytes past

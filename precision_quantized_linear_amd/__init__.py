@@ -136,8 +136,8 @@ def _alloc_q(scheme: str, role: str, rows: int, cols: int, device) -> QTensor:
     cb, sb, zb = quantized_sizes(scheme, role, rows, cols)
     if scheme.startswith("w4a16"):
         codes = torch.empty((rows, cols // 8), dtype=torch.int32, device=device)
-        scales = torch.empty((rows, cols // 128), dtype=torch.bfloat16, device=device)
-        zeros = torch.empty((rows, cols // 128), dtype=torch.uint8, device=device)
+        scales = torch.empty((cols // 128, rows), dtype=torch.bfloat16, device=device)   # group-major
+        zeros = torch.empty((cols // 128, rows), dtype=torch.uint8, device=device)
     else:
         codes = torch.empty((rows, cols if scheme != "mxfp4" else cols // 2), dtype=torch.uint8, device=device)
         if scheme in ("mxfp8", "mxfp4"):
@@ -271,20 +271,21 @@ def unpack_mx_scales(packed, nblk: int):
 
 def from_numpy(q: dict, device) -> QTensor:
     """Upload a quantized tensor given as NumPy arrays in the canonical layout (MX
-    exponents row-major [rows, cols / 32]; they are packed on the way up)."""
+    exponents row-major [rows, cols / 32], W4A16 scales and zero-points [rows,
+    cols / 128]; both go up in the device layout)."""
+    import numpy as np
     scheme = q["scheme"]
 
     def up(a, dtype):
-        import numpy as np
         t = torch.from_numpy(np.ascontiguousarray(a))
         if dtype is not None:
             t = t.view(dtype)
         return t.to(device)
 
-    if scheme.startswith("w4a16"):
+    if scheme.startswith("w4a16"):   # scales / zero-points go up group-major
         codes = up(q["codes"].view("int32"), None)
-        scales = up(q["scales"].view("int16"), torch.bfloat16)
-        zeros = up(q["zeros"], None)
+        scales = up(np.ascontiguousarray(np.asarray(q["scales"]).T).view("int16"), torch.bfloat16)
+        zeros = up(np.ascontiguousarray(np.asarray(q["zeros"]).T), None)
     else:
         codes = up(q["codes"], None)
         sc = q["scales"]
@@ -297,14 +298,15 @@ def from_numpy(q: dict, device) -> QTensor:
 
 def to_numpy(q: QTensor) -> dict:
     """Download a quantized tensor into NumPy arrays in the canonical layout (MX
-    exponents unpacked to row-major [rows, cols / 32]; the packed bytes as they are
-    in device memory under "scales_packed")."""
+    exponents unpacked to row-major [rows, cols / 32], the packed bytes as they are
+    in device memory under "scales_packed"; W4A16 scales and zero-points as
+    [rows, cols / 128])."""
     import numpy as np
     codes = q.codes.cpu().numpy()
-    if q.scheme.startswith("w4a16"):
+    if q.scheme.startswith("w4a16"):   # group-major on the device, [rows, groups] here
         codes = codes.view(np.uint32)
-        scales = q.scales.view(torch.int16).cpu().numpy().view(np.uint16)
-        zeros = q.zeros.cpu().numpy()
+        scales = np.ascontiguousarray(q.scales.view(torch.int16).cpu().numpy().view(np.uint16).T)
+        zeros = np.ascontiguousarray(q.zeros.cpu().numpy().T)
     else:
         scales = q.scales.cpu().numpy()
         zeros = None

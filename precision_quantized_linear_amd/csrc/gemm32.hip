@@ -36,7 +36,7 @@
 // the compiler's alias tracking cannot tell the regions of one LDS array
 // apart and would order every LDS read behind them; all waits on them are the
 // explicit counts below.  Rows are 128 bytes (eight 16-byte chunks); chunk c
-// of row r sits at position c ^ (r % 8), which keeps each 8-lane group of a
+// of row r sits at position c ^ ((r / 2) % 8), which keeps each 16-lane group of a
 // fragment read on distinct banks.
 #include <algorithm>
 #include <tuple>
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
 
   // ---- load stream.  Wave w moves A rows and W rows 64 w .. 64 w + 63 of a tile
   // for one K region, 8 rows per instruction: lane i fetches chunk
-  // (i % 8) ^ (i / 8) of row i / 8 of the group, which lands at LDS offset 16 i,
+  // dma_chunk(i) of row i / 8 of the group, which lands at LDS offset 16 i,
   // the swizzled position.  One buffer descriptor per operand and tile covers
   // the tile's valid rows; the per-lane offset of row group p (fixed for the
   // whole kernel, shared by A and W) holds the row, so rows past M / N fall
@@ -115,10 +115,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   // past this workgroup's last tile the stream refetches its last tile into a
   // region that is never read.  MX scales ride the same stream: per region,
   // each row's kSB exponent bytes.
-  const int vchunk = ((lane & 7) ^ (lane >> 3)) << 4;
   int voff_p[8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) voff_p[p] = (wave * 64 + 8 * p + (lane >> 3)) * Kb + vchunk;
+  for (int p = 0; p < 8; ++p) voff_p[p] = (wave * 64 + 8 * p + (lane >> 3)) * Kb + (dma_chunk(lane, p & 1) << 4);
   const int voff_sc = lane * 4;
   struct Span {
     uint64_t base;

@@ -18,8 +18,8 @@
 // Pipeline: one 128-byte K-group per "region"; LDS holds three regions
 // (A 256 rows + W 128 rows of 128 bytes, the A scales of the group, and the W
 // scale), filled by direct-to-LDS loads of whole 128-byte lines (lane i of an
-// 8-row load fetches chunk (i % 8) ^ (i / 8) of row i / 8, which is the
-// swizzled position: chunk c of row r at c ^ (r % 8)).  Before region R the
+// 8-row load fetches the chunk of row i / 8 whose swizzled position is i % 8, which is the
+// swizzled position: chunk c of row r at c ^ ((r / 2) % 8)).  Before region R the
 // waves wait for region R + 1 and meet at a barrier; region R's 32 MFMAs are
 // interleaved with the LDS reads of region R + 1's fragments and with the loads
 // of region R + 3 into region R's slot.  The grid is persistent, one
@@ -82,12 +82,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
   // the scalar offset, which stays inside a row.  Code part p of A is rows
   // 64 wave + 8 p .. + 7 of the tile, of W rows 32 wave + 8 p .. + 7; the
   // activation scales are rows 64 wave .. + 63, one lane per row.
-  const int vchunk = ((lane & 7) ^ (lane >> 3)) << 4;
   int voff_a[8], voff_w[4];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) voff_a[p] = (wave * 64 + 8 * p + (lane >> 3)) * Kb + vchunk;
+  for (int p = 0; p < 8; ++p) voff_a[p] = (wave * 64 + 8 * p + (lane >> 3)) * Kb + (dma_chunk(lane, p & 1) << 4);
 #pragma unroll
-  for (int p = 0; p < 4; ++p) voff_w[p] = (wave * 32 + 8 * p + (lane >> 3)) * Kb + vchunk;
+  for (int p = 0; p < 4; ++p) voff_w[p] = (wave * 32 + 8 * p + (lane >> 3)) * Kb + (dma_chunk(lane, p & 1) << 4);
   const int voff_sa = (wave * 64 + lane) * G * 4;
   struct TileRsrc {
     v4i a, w, sa, sw;   // codes, activation scales, this tile's row of weight scales

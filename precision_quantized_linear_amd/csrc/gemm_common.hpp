@@ -17,8 +17,21 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // left at its maximum, lgkmcnt in bits 11:8.
 constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
 
-// 128-byte LDS rows: 16-byte chunk c of row r sits at chunk position c ^ (r % 8).
-__device__ __forceinline__ int swz128(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// 128-byte LDS rows: 16-byte chunk c of row r sits at chunk position
+// c ^ ((r / 2) % 8).  gfx950's LDS serves 16 lanes of a 16-byte read per
+// cycle from 64 banks (256 bytes, two rows): a fragment read, whose 16 lanes
+// take the same chunk of 16 consecutive rows, then finds the even rows on
+// distinct positions of one bank half and the odd rows on the other.  (A
+// period of 8 rows would put rows r and r + 8 on the same banks.)
+__device__ __forceinline__ int swz128(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+// Chunk that lane i fetches in an 8-row direct-to-LDS load (8 lanes per
+// 128-byte row, lane i landing at LDS byte 16 i): the one whose swizzled
+// position is i % 8 in row i / 8 of the group.  `odd_group` is the parity of
+// the group's index (row / 8), which sets bit 2 of (row / 2) % 8.
+__device__ __forceinline__ int dma_chunk(int lane, int odd_group) {
+  return (lane & 7) ^ ((odd_group << 2) | ((lane >> 4) & 3));
+}
 
 // Persistent schedule.  Workgroup b runs on XCD b % 8 (dispatch is round-robin
 // over the XCDs).  Each XCD owns a contiguous range of the tile order, and its

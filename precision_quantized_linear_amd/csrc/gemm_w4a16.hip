@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_tile(const uint16_t* __restric
       v4i v = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, t * (int)Wb + s * 32 + h * 16, 0, 0);
       rw[h] = make_uint4(v.x, v.y, v.z, v.w);
     }
-    const int64_t gi = wrow * ngroups + (s >> 1);
+    const int64_t gi = (s >> 1) * N + wrow;   // group-major
     s_reg = __uint_as_float((uint32_t)w_scales[gi] << 16);
     zs_reg = -(float)w_zeros[gi] * s_reg;      // exact: z * s fits in fp32
   };
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void k_w4a16_small(const uint16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       code[j] = ldg16_nt(wq + wrow[j] * wpr + gidx * 16 + g4 * 4);
-      const int64_t gi = wrow[j] * ngroups + gidx;
+      const int64_t gi = gidx * N + wrow[j];   // group-major scales / zero-points
       s[j] = __uint_as_float((uint32_t)w_scales[gi] << 16);
       zs[j] = -(float)w_zeros[gi] * s[j];
     }
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           code[u][nb] = ldg16_nt(wrow[nb] + (int64_t)G * 16 + g * 4);
-          const int64_t gi = nrow[nb] * ng + G;
+          const int64_t gi = (int64_t)G * N + nrow[nb];   // group-major
           s[u][nb] = __uint_as_float((uint32_t)w_scales[gi] << 16);
           z[u][nb] = 128.0f + (float)w_zeros[gi];
         }
@@ -428,6 +428,7 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16
     else hipLaunchKernelGGL(k_w4a16_small<4>, grid, block, 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
     return hipGetLastError();
   }
+  if (w4a16_mm_supported(M, N, K)) return launch_gemm_w4a16_mm(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
   const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
   const size_t lds = 2 * kStageBytes;
   int dev = 0;
@@ -444,11 +445,12 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16
   return hipGetLastError();
 }
 
-const char* gemm_w4a16_kernel_name(int64_t M, int64_t, int64_t K) {
+const char* gemm_w4a16_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M <= 16 && M * (K * 2 + 16) <= kGemvStageMax) return M <= 4 ? "k_w4a16_gemv<16 cols>" : "k_w4a16_gemv<48 cols>";
   if (M <= 16) return "k_w4a16_small<16>";
   if (M <= 32) return "k_w4a16_small<32>";
   if (M <= 64) return "k_w4a16_small<64>";
+  if (w4a16_mm_supported(M, N, K)) return "k_w4a16_mm_256x128x64";
   return "k_w4a16_tile_256x256x64";
 }
 

@@ -1,0 +1,314 @@
+// W4A16 GEMM for M > 64 on gfx950: C[M, N] = A (bf16) * W_hat^T with
+// W_hat[n, k] = bf16((q[n, k] - z[g, n]) * s[g, n]), g = k / 128 (int4 codes, a bf16
+// scale and a 4-bit zero-point per 128-element K-group: "vLLM-Omni accelerates
+// inference with AutoRound quantization", section "Usage").  The product
+// (q - z) * s is exact in fp32, so W_hat equals the library's dequantize.
+//
+// One 256 x 128 output tile per workgroup of 4 waves (2 x 2, each 128 x 64 as
+// 4 x 2 blocks of v_mfma_f32_32x32x16_bf16).  K advances in steps of 64
+// elements.  Per step the workgroup needs A (256 rows x 128 bytes, bf16) and
+// the codes of its 128 weight rows (32 bytes each); both arrive by
+// direct-to-LDS loads (A in 128-byte rows with chunk c of row r at c ^ ((r / 2) % 8),
+// lane i of an 8-row load fetching the chunk of row i / 8 that lands at position i % 8; codes
+// row-major).  Each step's codes are expanded once per workgroup into a bf16
+// weight tile in LDS (same swizzle), which all 4 waves read as MFMA operands:
+// every weight element is converted once per 256 output rows.
+//
+// Pipeline (one barrier per step, in its middle): during step s the waves run
+// step s's MFMAs and, between them, expand step s + 1's codes into the other
+// weight buffer and issue the loads of A for step s + 2 (3-slot ring) and of
+// codes for step s + 5 (6-slot ring), plus, when step s + 5 starts a group,
+// that group's scales and zero-points for the tile's rows (group-major in
+// memory, so one 256-byte and one 128-byte load; 3 slots).  The weight stream
+// comes from HBM and gets the longer lead.  The barrier waits for the A loads
+// issued one step earlier and everything before them (loads retire in issue
+// order), leaving that step's younger code and scale loads in flight.
+#include <algorithm>
+#include <type_traits>
+
+#include "gemm_common.hpp"
+#include "pql_device.hpp"
+#include "pql_internal.hpp"
+
+namespace pql {
+
+namespace {
+
+using namespace gemm;
+
+constexpr int BM = 256, BN = 128;
+constexpr int kARow = 128;                         // A bytes per row per step (64 bf16)
+constexpr int kAStage = BM * kARow;                // 32 KB
+constexpr int kAStages = 3;
+constexpr int kCRow = 32;                          // code bytes per weight row per step
+constexpr int kCStage = BN * kCRow;                // 4 KB
+constexpr int kLead = 5;                           // codes (and scales) run this many steps ahead
+constexpr int kCStages = kLead + 1;
+constexpr int kSZSlots = 3;
+constexpr int kWRow = 128;                         // expanded bf16 bytes per weight row per step
+constexpr int kWBuf = BN * kWRow;                  // 16 KB
+constexpr int kSZ = 512;                           // per group slot: 128 bf16 scales, then 128 zero-points (+ pad)
+constexpr int kOffC = kAStages * kAStage;
+constexpr int kOffW = kOffC + kCStages * kCStage;
+constexpr int kOffSZ = kOffW + 2 * kWBuf;
+constexpr int kLds = kOffSZ + kSZSlots * kSZ;      // 153.5 KB
+constexpr int kEpiRow = 136;                       // staged output row: 64 bf16 + 8 bytes of padding
+constexpr int kEpiBytes = 32 * kEpiRow;            // per wave, inside the (idle) A stages at the end
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
+                                                    const uint16_t* __restrict__ w_scales,
+                                                    const uint8_t* __restrict__ w_zeros, int64_t M, int64_t N,
+                                                    int64_t K, uint16_t* __restrict__ c, int64_t ldc) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+
+  // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
+  // contiguous range of tiles, walked in 4-tile-tall column groups.
+  const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+  int tm, tn;
+  {
+    const int T = tiles_m * tiles_n, b = blockIdx.x;
+    const int xcd = b & 7, idx = b >> 3, per = T >> 3, rem = T & 7;
+    const int L = xcd * per + min(xcd, rem) + idx;
+    constexpr int kGroupM = 4;
+    const int group = L / (kGroupM * tiles_n), first_m = group * kGroupM;
+    const int gm = min(tiles_m - first_m, kGroupM), l = L - group * kGroupM * tiles_n;
+    tm = __builtin_amdgcn_readfirstlane(first_m + l % gm);
+    tn = __builtin_amdgcn_readfirstlane(l / gm);
+  }
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+  const int mr = (int)std::min<int64_t>(BM, M - m0), nr = (int)std::min<int64_t>(BN, N - n0);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int nsteps = (int)(K / 64), ng = (int)(K / 128);
+
+  if (wave >= 4) {
+    // ================= helper waves: loads and weight expansion =================
+    const int hw = wave - 4, ht = t - 256;
+    const int Ab = (int)(K * 2), Wb = (int)(K / 2);   // bytes per A row, per code row
+    // Per-tile descriptors cover the tile's valid rows (rows past M / N read
+    // 0); lane offsets carry the row, the step's K offset rides in the scalar
+    // offset.  Helper wave h moves A rows 64 h .. + 63 (8 loads of 8 rows) and
+    // the codes of weight rows 32 h .. + 31 (one load).
+    const v4i a_rsrc = make_rsrc(a + m0 * K, mr * Ab);
+    const v4i w_rsrc = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + n0 * Wb, nr * Wb);
+    int voff_a[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) voff_a[p] = (hw * 64 + 8 * p + (lane >> 3)) * Ab + (dma_chunk(lane, p & 1) << 4);
+    const int voff_c = (hw * 32 + (lane >> 1)) * Wb + (lane & 1) * 16;
+    auto load_a = [&](int s, int stage, int p) __attribute__((always_inline)) {
+      lds_load16_so(a_rsrc, smem + stage * kAStage + (hw * 64 + 8 * p) * kARow, voff_a[p],
+                    std::min(s, nsteps - 1) * kARow);
+    };
+    auto load_codes = [&](int s) __attribute__((always_inline)) {
+      lds_load16_so(w_rsrc, smem + kOffC + (s % kCStages) * kCStage + hw * 32 * kCRow, voff_c,
+                    std::min(s, nsteps - 1) * kCRow);
+    };
+    auto load_group = [&](int g) __attribute__((always_inline)) {   // waves 0 and 1 of the helpers
+      const int gc = std::min(g, ng - 1);
+      uint8_t* slot = smem + kOffSZ + (g % kSZSlots) * kSZ;
+      if (hw == 0) lds_load4(make_rsrc(w_scales + (int64_t)gc * N + n0, nr * 2), slot, lane * 4);
+      else lds_load4(make_rsrc(w_zeros + (int64_t)gc * N + n0, nr), slot + 256, lane * 4);
+    };
+
+    // Expansion of step s's codes into weight buffer s & 1: helper thread h
+    // owns weight row h / 2, elements 32 (h % 2) .. + 31 of the step (chunks
+    // 4 (h % 2) .. + 3 of the row); even and odd nibbles are spread into the
+    // bytes of two words, so each code converts with one byte-to-float
+    // instruction.
+    const int er = ht >> 1, eh = ht & 1;
+    auto expand = [&](int s) __attribute__((always_inline)) {
+      const uint8_t* cs = smem + kOffC + (s % kCStages) * kCStage;
+      const uint4 code = *reinterpret_cast<const uint4*>(cs + er * kCRow + eh * 16);
+      const uint8_t* sz = smem + kOffSZ + ((s >> 1) % kSZSlots) * kSZ;
+      const uint32_t sb = *reinterpret_cast<const uint16_t*>(sz + er * 2);
+      const uint32_t zb = sz[256 + er];
+      const float sc = __uint_as_float(sb << 16);
+      const float zs = -(float)zb * sc;   // exact: z * s fits in fp32
+      uint8_t* wb = smem + kOffW + (s & 1) * kWBuf;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = q == 0 ? code.x : q == 1 ? code.y : q == 2 ? code.z : code.w;
+        uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+        asm volatile("" : "+v"(ev), "+v"(od));   // keep the byte planes
+        uint32_t pr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pr[j] = pack_bf16x2(__builtin_fmaf((float)((ev >> (8 * j)) & 0xFF), sc, zs),
+                              __builtin_fmaf((float)((od >> (8 * j)) & 0xFF), sc, zs));
+        *reinterpret_cast<uint4*>(wb + swz128(er, 4 * eh + q)) = uint4{pr[0], pr[1], pr[2], pr[3]};
+      }
+    };
+
+    // Prologue: A of steps 0, 1; codes of steps 0 .. kLead - 1; groups 0 .. 2.
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      load_a(0, 0, p);
+      load_a(1, 1, p);
+    }
+#pragma unroll
+    for (int s = 0; s < kLead; ++s) load_codes(s);
+    if (hw < 2) {
+#pragma unroll
+      for (int g = 0; g < kSZSlots; ++g) load_group(g);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __builtin_amdgcn_s_barrier();
+    expand(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    __builtin_amdgcn_s_barrier();
+    // Step s (between barriers B(s - 1) and B(s)): loads of A for step s + 2
+    // (its stage was last read before B(s - 1)), of codes for step s + kLead
+    // and, when that step starts a group, of the group's scales; then the
+    // expansion of step s + 1 (codes and scales landed before B(s - 1)).
+    // B(s) needs A of step s + 1 (issued during step s - 1) and everything
+    // older; younger are step s - 1's code load and, on every other step, its
+    // scale load (helper waves 0 and 1), then this step's 9 or 10 loads.
+    for (int s = 0; s < nsteps; ++s) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) load_a(s + 2, (s + 2) % kAStages, p);
+      load_codes(s + kLead);
+      if (((s + kLead) & 1) == 0 && hw < 2) load_group((s + kLead) >> 1);
+      expand(s + 1);   // the last step expands a clamped step that is never read
+      if (hw < 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(11, 0));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_imm(10, 0));
+      __builtin_amdgcn_s_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // every load has landed before LDS is reused
+    __builtin_amdgcn_s_barrier();
+    return;
+  }
+
+  // ================= MFMA waves: one 128 x 64 quarter of the tile each =================
+  // v_mfma_f32_32x32x16_bf16 (the form that runs at the full bf16 rate on
+  // gfx950): lane l feeds row l % 32 and, with g = l / 32, K-elements
+  // 8 g .. 8 g + 7 of a 16-element quarter step kq, i.e. chunk 2 kq + g of the
+  // 128-byte row; the same assignment for both operands pairs every K-element
+  // with itself.  The weight fragment is the first operand, so accumulator
+  // register r of lane l holds C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]:
+  // four consecutive columns per register quad.
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fg = lane >> 5;
+  int aoff[4], woff[4];
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) {
+    aoff[kq] = swz128(wm * 128 + fr, 2 * kq + fg);
+    woff[kq] = swz128(wn * 64 + fr, 2 * kq + fg);
+  }
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  uint4 fa[2][4], fw[2][2];   // two register sets, alternating by quarter step
+  auto read_quarter = [&](int s, int kq, int set) __attribute__((always_inline)) {
+    const uint8_t* As = smem + (s % kAStages) * kAStage;
+    const uint8_t* Ws = smem + kOffW + (s & 1) * kWBuf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[set][i] = lds16(As + aoff[kq] + i * 32 * kARow);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fw[set][j] = lds16(Ws + woff[kq] + j * 32 * kWRow);
+  };
+  __builtin_amdgcn_s_barrier();   // the helpers' prologue loads have landed
+  __builtin_amdgcn_s_barrier();   // step 0's weights are expanded
+  __builtin_amdgcn_sched_barrier(0);
+  read_quarter(0, 0, 0);
+  // Step s: quarter steps kq = 0..3 of 4 x 2 MFMAs each, register set kq & 1,
+  // the next quarter's 6 fragment reads interleaved.  Every read of step s's
+  // stage and weight buffer is issued before quarter 3, so B(s) comes there;
+  // past it, step s + 1's A and weights are complete, and its first quarter
+  // is read under quarter 3's MFMAs.
+  auto quarter = [&](int s, auto kqc) __attribute__((always_inline)) {
+    constexpr int kq = decltype(kqc)::value, cs = kq & 1, ns = cs ^ 1;
+    if constexpr (kq == 3) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fw[cs][j]),
+                                                            __builtin_bit_cast(v8bf, fa[cs][i]), acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const int e = j * 4 + i;
+        if (e < 6) {
+          const int sn = kq == 3 ? s + 1 : s, kn = (kq + 1) & 3;
+          const uint8_t* As = smem + (sn % kAStages) * kAStage;
+          const uint8_t* Ws = smem + kOffW + (sn & 1) * kWBuf;
+          if (e < 4) fa[ns][e] = lds16(As + aoff[kn] + e * 32 * kARow);
+          else fw[ns][e - 4] = lds16(Ws + woff[kn] + (e - 4) * 32 * kWRow);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  for (int s = 0; s < nsteps; ++s) {
+    quarter(s, std::integral_constant<int, 0>{});
+    quarter(s, std::integral_constant<int, 1>{});
+    quarter(s, std::integral_constant<int, 2>{});
+    quarter(s, std::integral_constant<int, 3>{});
+  }
+
+  // ---- epilogue: every load has landed (the helpers wait) before the A
+  // stages are reused for staging.  Per 32-row block i the wave stages its
+  // 32 x 64 outputs (bf16 quads of consecutive columns) and writes them as
+  // 16-byte row pieces (8 lanes per row, 8 rows per instruction).
+  __builtin_amdgcn_s_barrier();
+  uint8_t* stg = smem + wave * kEpiBytes;
+  const int rr = lane >> 3, rc = lane & 7;
+  const int64_t wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 64;
+  const bool vec = (ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0;
+  const bool interior = vec && wrow0 + 128 <= M && wcol0 + 64 <= N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const v16f& v = acc[i][j];
+        *reinterpret_cast<uint2*>(stg + fr * kEpiRow + (j * 32 + 8 * rq + 4 * fg) * 2) =
+            uint2{pack_bf16x2(v[4 * rq + 0], v[4 * rq + 1]), pack_bf16x2(v[4 * rq + 2], v[4 * rq + 3])};
+      }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint8_t* src = stg + (q * 8 + rr) * kEpiRow + rc * 16;   // 8-byte aligned (136-byte rows)
+      const uint2 lo = *reinterpret_cast<const uint2*>(src), hi = *reinterpret_cast<const uint2*>(src + 8);
+      const uint4 v = uint4{lo.x, lo.y, hi.x, hi.y};
+      const int64_t row = wrow0 + i * 32 + q * 8 + rr, col = wcol0 + rc * 8;
+      uint16_t* dst = c + row * ldc + col;
+      if (interior) {
+        *reinterpret_cast<uint4*>(dst) = v;
+      } else if (row < M) {
+        if (vec && col + 8 <= N) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (col + e < N) dst[e] = (uint16_t)(wds[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // staging block read before it is rewritten
+  }
+}
+
+}  // namespace
+
+bool w4a16_mm_supported(int64_t M, int64_t N, int64_t K) {
+  // group-major scale / zero loads of a tile's 128 rows are dword loads
+  return M > 0 && N % 4 == 0 && K % 128 == 0 && K / 64 >= 1 && K * 2 * 256 < (int64_t)1 << 31;
+}
+
+hipError_t launch_gemm_w4a16_mm(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales,
+                                const uint8_t* w_zeros, int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc,
+                                hipStream_t st) {
+  const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+  hipLaunchKernelGGL(k_w4a16_mm, dim3(tiles), dim3(512), 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace pql

@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void k_int4(const uint16_t* __restrict__ x, in
     for (int j = 0; j < 8; ++j) w |= (uint32_t)fminf(fmaxf(__builtin_rintf(q[j]) + z, 0.0f), 15.0f) << (4 * j);
     codes[g.row * cpr + c] = w;
     if ((c & 15) == 0) {
-      const int64_t gi = g.row * (cols >> 7) + (c >> 4);
+      const int64_t gi = (c >> 4) * rows + g.row;   // group-major
       scales[gi] = (uint16_t)(__float_as_uint(s) >> 16);
       zeros[gi] = (uint8_t)z;
     }
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(256) void k_dequant(int kind, const uint8_t* __rest
       }
     } else {
       const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[r * cpr + c];
-      const int64_t gi = r * (cols >> 7) + (c >> 4);
+      const int64_t gi = (c >> 4) * rows + r;   // group-major
       const float s = __uint_as_float((uint32_t)static_cast<const uint16_t*>(scales)[gi] << 16);
       const float z = (float)zeros[gi];
 #pragma unroll

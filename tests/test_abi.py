@@ -91,7 +91,10 @@ def test_kernel_names_distinct_per_scheme():
     assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 1, 12288, 3072).startswith("k_w4a16_gemv")
     assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 16, 12288, 3072).startswith("k_w4a16_gemv")
     assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 32, 12288, 3072).startswith("k_w4a16_small")
-    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 4096, 12288, 3072).startswith("k_w4a16_tile")
+    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 4096, 12288, 3072).startswith("k_w4a16_mm")
+    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 256, 12288, 3072).startswith("k_w4a16_mm")
+    # N not a multiple of 4 (dword scale loads of a tile's rows) keeps the older tile kernel
+    assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 256, 12290, 3072).startswith("k_w4a16_tile")
 
 
 # ----------------------------------------------------------------- validation before launch

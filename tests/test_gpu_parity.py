@@ -89,10 +89,28 @@ for scheme in FP_SCHEMES + ("w4a16_asym", "w4a16_sym"):
 def test_quantize_bit_exact(scheme, role, rows, cols):
     x = hard_input(rows * 7 + cols, rows, cols, 0.02 if role == "weight" else 1.0)
     ref = oracle.quantize(x, scheme, role)
-    got = pql.to_numpy(pql.quantize(up(x), scheme, role))
+    q = pql.quantize(up(x), scheme, role)
+    got = pql.to_numpy(q)
     assert_q_equal(got, ref, f"{scheme}/{role} {rows}x{cols}")
     if scheme in MX_CHUNK:   # the packed device layout itself, pad bytes included
         assert np.array_equal(got["scales_packed"], F.pack_mx_scales(ref["scales"], MX_CHUNK[scheme]))
+    if scheme.startswith("w4a16"):   # device layout: group-major [cols / 128, rows]
+        assert tuple(q.scales.shape) == (cols // 128, rows) and tuple(q.zeros.shape) == (cols // 128, rows)
+        assert np.array_equal(q.scales.view(torch.int16).cpu().numpy().view(np.uint16), ref["scales"].T)
+        assert np.array_equal(q.zeros.cpu().numpy(), ref["zeros"].T)
+
+
+@pytest.mark.parametrize("M,N,K", [(257, 388, 384), (1000, 260, 640), (512, 1024, 256), (130, 390, 384)])
+def test_w4a16_gemm_tile_shapes(M, N, K):
+    # ragged M and N tails across several 256 x 128 tiles, an odd number of
+    # K-groups, and N % 4 != 0 (which takes the older tile kernel)
+    a = wl.small_case(5000 + M, M, K, 1.0)
+    w = wl.small_case(6000 + N, N, K, 0.02)
+    wq = oracle.quantize(w, "w4a16_asym", "weight")
+    c = pql.qgemm(up(a), pql.from_numpy(wq, DEV))
+    err = oracle.rel_fro_error(F.bf16_to_f32(down_bf16(c)), oracle.gemm_ref(a, wq))
+    assert err <= TOL, f"{M}x{N}x{K}: rel err {err:.3e}"
+    assert err <= 5e-3
 
 
 @pytest.mark.parametrize("scheme", FP_SCHEMES + ("w4a16_asym",))
