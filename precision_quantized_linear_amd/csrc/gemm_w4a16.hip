@@ -20,6 +20,7 @@
 //     4 waves are added in LDS.
 #include <algorithm>
 
+#include "gemm_common.hpp"
 #include "pql_device.hpp"
 #include "pql_internal.hpp"
 
@@ -278,6 +279,9 @@ __device__ __forceinline__ uint4 pair_k_k4(uint4 a) {
 constexpr int kGemvBatch = 4;   // K-groups whose code loads are in flight together, per wave
 constexpr int kGemvWaves = 8;   // waves per workgroup, splitting the K-groups
 constexpr int kGemvStageMax = 128 * 1024;  // LDS bytes for the staged activation rows
+// LDS bytes per staged activation row: K bf16 rounded up to whole 1 KB loads,
+// plus 16 bytes, which spreads the 16 rows of a fragment read over the banks.
+__host__ __device__ constexpr int64_t gemv_a_row_bytes(int64_t K) { return (K * 2 + 1023) / 1024 * 1024 + 16; }
 
 // NB column blocks of 16 per workgroup: every A fragment feeds NB weight row
 // blocks.  The activation rows (M <= 16) are staged once per workgroup in LDS
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
   extern __shared__ __attribute__((aligned(16))) uint8_t gemv_lds[];
   float (*part)[16][16 * NB + 1] = reinterpret_cast<float (*)[16][16 * NB + 1]>(gemv_lds);
   uint8_t* a_lds = gemv_lds + sizeof(float) * kGemvWaves * 16 * (16 * NB + 1);
-  const int64_t a_row_bytes = K * 2 + 16;
+  const int64_t a_row_bytes = gemv_a_row_bytes(K);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int n16 = lane & 15, g = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
@@ -311,8 +315,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
   const uint8_t* arow = a_lds + n16 * a_row_bytes;             // A row m = l % 16 of the A operand
   const v8bf ones = as_v8bf(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 
+  // Codes, scales and zero-points of a batch of groups; the scale and zero
+  // bytes stay raw until used, so that no load waits for another.
   uint4 code[kGemvBatch][NB];
-  float s[kGemvBatch][NB], z[kGemvBatch][NB];
+  uint32_t sraw[kGemvBatch][NB], zraw[kGemvBatch][NB];
   auto fetch = [&](int b0) {
 #pragma unroll
     for (int u = 0; u < kGemvBatch; ++u) {
@@ -322,18 +328,24 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
         for (int nb = 0; nb < NB; ++nb) {
           code[u][nb] = ldg16_nt(wrow[nb] + (int64_t)G * 16 + g * 4);
           const int64_t gi = (int64_t)G * N + nrow[nb];   // group-major
-          s[u][nb] = __uint_as_float((uint32_t)w_scales[gi] << 16);
-          z[u][nb] = 128.0f + (float)w_zeros[gi];
+          sraw[u][nb] = w_scales[gi];
+          zraw[u][nb] = w_zeros[gi];
         }
       }
     }
   };
   fetch(gbeg);
-  // Stage A: M rows of K bf16, 16-byte pieces.
-  const int64_t pieces = M * (K / 8);
-  for (int64_t e = t; e < pieces; e += 64 * kGemvWaves) {
-    const int64_t m = e / (K / 8), q = e - m * (K / 8);
-    *reinterpret_cast<uint4*>(a_lds + m * a_row_bytes + q * 16) = ldg16(a + m * K + q * 8);
+  // Stage A (M rows of K bf16) with direct-to-LDS loads of 1 KB (64 lanes x 16
+  // bytes of one row); a row's slot is rounded up to whole loads, so the last
+  // load of a row stays inside it.  Then one wait covers these and the batch.
+  {
+    const int per_row = (int)((K * 2 + 1023) / 1024);
+    const v4i a_rsrc = gemm::make_rsrc(a, (int)(M * K * 2));
+    for (int idx = wave; idx < M * per_row; idx += kGemvWaves) {
+      const int m = idx / per_row, j = idx - m * per_row;
+      gemm::lds_load16(a_rsrc, a_lds + m * a_row_bytes + j * 1024, (int)(m * K * 2) + j * 1024 + lane * 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
   }
   __syncthreads();
 
@@ -366,7 +378,8 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          acc[nb][r] = __builtin_fmaf(s[u][nb], __builtin_fmaf(-z[u][nb], Q[r], P[nb][r]), acc[nb][r]);
+          acc[nb][r] = __builtin_fmaf(__uint_as_float(sraw[u][nb] << 16),
+                                      __builtin_fmaf(-(128.0f + (float)zraw[u][nb]), Q[r], P[nb][r]), acc[nb][r]);
     }
   }
 #pragma unroll
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
 
 template <int NB>
 size_t gemv_lds_bytes(int64_t M, int64_t K) {
-  return sizeof(float) * kGemvWaves * 16 * (16 * NB + 1) + (size_t)M * (size_t)(K * 2 + 16);
+  return sizeof(float) * kGemvWaves * 16 * (16 * NB + 1) + (size_t)M * (size_t)gemv_a_row_bytes(K);
 }
 
 template <int NB>
@@ -417,7 +430,7 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16
                              const uint8_t* w_zeros, int64_t M, int64_t N, int64_t K, uint16_t* c,
                              int64_t ldc, hipStream_t st) {
   // Small M: the GEMV kernel when the activation rows fit its LDS stage.
-  if (M <= 16 && M * (K * 2 + 16) <= kGemvStageMax) {
+  if (M <= 16 && M * gemv_a_row_bytes(K) <= kGemvStageMax) {
     return M <= 4 ? launch_gemv<1>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st)
                   : launch_gemv<3>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
   }
@@ -446,7 +459,7 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16
 }
 
 const char* gemm_w4a16_kernel_name(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16 && M * (K * 2 + 16) <= kGemvStageMax) return M <= 4 ? "k_w4a16_gemv<16 cols>" : "k_w4a16_gemv<48 cols>";
+  if (M <= 16 && M * gemv_a_row_bytes(K) <= kGemvStageMax) return M <= 4 ? "k_w4a16_gemv<16 cols>" : "k_w4a16_gemv<48 cols>";
   if (M <= 16) return "k_w4a16_small<16>";
   if (M <= 32) return "k_w4a16_small<32>";
   if (M <= 64) return "k_w4a16_small<64>";
