@@ -8,16 +8,19 @@
 // (v_mfma_f32_16x16x32_bf16: lane l feeds row l % 16 with K-elements
 // 8 * (l / 16) .. +7; accumulator lane l holds C[4 * (l / 16) + r][l % 16]).
 //
-// Two kernels:
-//   * M > 64: compute-bound.  256 x 256 output tile per 256-thread workgroup,
-//     K steps of 64.  Per step the workgroup stages A (bf16, 32 KB) and the
-//     expanded W tile (bf16, 32 KB) in double-buffered LDS; each thread
-//     expands one W row-slice of 64 codes.  LDS layout and bank swizzle are
-//     the same as the fp8 kernel's (128-byte rows, chunk c at c ^ (row & 7)).
-//   * M <= 64: weight-bandwidth-bound.  A workgroup owns 32 output columns;
-//     its 4 waves split the K-groups, each wave streams 16-byte code chunks
-//     straight into registers (no LDS staging), and the partial sums of the
-//     4 waves are added in LDS.
+// Dispatch by M:
+//   * M <= 16 (activation rows fit the LDS stage): k_w4a16_gemv, weight-
+//     bandwidth-bound; codes stay integers on the bf16 MFMA and each group is
+//     promoted with its scale and zero-point (below).
+//   * M <= 64: k_w4a16_small, weight-bandwidth-bound.  A workgroup owns 32
+//     output columns; its 4 waves split the K-groups, each wave streams 16-byte
+//     code chunks straight into registers (no LDS staging), and the partial
+//     sums of the 4 waves are added in LDS.
+//   * M > 64: compute-bound; the wave-specialized kernel of gemm_w4a16_mm.hip
+//     when N % 4 == 0, else k_w4a16_tile here: 256 x 256 output tile per
+//     256-thread workgroup, K steps of 64, A (bf16, 32 KB) and the expanded W
+//     tile (bf16, 32 KB) double-buffered in LDS, each thread expanding one W
+//     row-slice of 64 codes (128-byte rows, chunk c at c ^ (row & 7)).
 #include <algorithm>
 
 #include "gemm_common.hpp"

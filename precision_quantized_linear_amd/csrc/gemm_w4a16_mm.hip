@@ -4,25 +4,32 @@
 // inference with AutoRound quantization", section "Usage").  The product
 // (q - z) * s is exact in fp32, so W_hat equals the library's dequantize.
 //
-// One 256 x 128 output tile per workgroup of 4 waves (2 x 2, each 128 x 64 as
-// 4 x 2 blocks of v_mfma_f32_32x32x16_bf16).  K advances in steps of 64
-// elements.  Per step the workgroup needs A (256 rows x 128 bytes, bf16) and
-// the codes of its 128 weight rows (32 bytes each); both arrive by
-// direct-to-LDS loads (A in 128-byte rows with chunk c of row r at c ^ ((r / 2) % 8),
-// lane i of an 8-row load fetching the chunk of row i / 8 that lands at position i % 8; codes
-// row-major).  Each step's codes are expanded once per workgroup into a bf16
-// weight tile in LDS (same swizzle), which all 4 waves read as MFMA operands:
-// every weight element is converted once per 256 output rows.
+// One 256 x 128 output tile per workgroup of 8 waves, specialized by role.
+// Waves 0-3 (one per SIMD) only read LDS and run the matrix core: a 2 x 2
+// grid of 128 x 64 quarters, each 4 x 2 blocks of v_mfma_f32_32x32x16_bf16.
+// Waves 4-7 (the second wave on each SIMD) issue every global load and expand
+// the int4 codes into bf16, so that VALU work runs beside the other wave's
+// MFMAs instead of between them (a wave's own VALU and MFMA instructions do
+// not overlap).  K advances in steps of 64 elements.  Per step the workgroup
+// needs A (256 rows x 128 bytes, bf16) and the codes of its 128 weight rows
+// (32 bytes each); both arrive by direct-to-LDS loads (A in 128-byte rows with
+// chunk c of row r at c ^ ((r / 2) % 8), lane i of an 8-row load fetching the
+// chunk of row i / 8 that lands at position i % 8; codes row-major).  Each
+// step's codes are expanded once per workgroup into a bf16 weight tile in LDS
+// (same swizzle), read by all 4 MFMA waves: every weight element is
+// converted once per 256 output rows.
 //
-// Pipeline (one barrier per step, in its middle): during step s the waves run
-// step s's MFMAs and, between them, expand step s + 1's codes into the other
-// weight buffer and issue the loads of A for step s + 2 (3-slot ring) and of
-// codes for step s + 5 (6-slot ring), plus, when step s + 5 starts a group,
-// that group's scales and zero-points for the tile's rows (group-major in
-// memory, so one 256-byte and one 128-byte load; 3 slots).  The weight stream
-// comes from HBM and gets the longer lead.  The barrier waits for the A loads
-// issued one step earlier and everything before them (loads retire in issue
-// order), leaving that step's younger code and scale loads in flight.
+// Pipeline (one barrier B(s) per step, shared by all 8 waves): during step s
+// the MFMA waves run step s's 4 quarter steps (the barrier sits before the
+// last, after every read of step s's buffers has been issued), while the
+// helper waves issue the loads of A for step s + 2 (3-slot ring) and of codes
+// for step s + 5 (6-slot ring), plus, when step s + 5 starts a group, that
+// group's scales and zero-points for the tile's rows (group-major in memory,
+// so one 256-byte and one 128-byte load; 3 slots), and expand step s + 1's
+// codes into the other weight buffer.  The weight stream comes from HBM and
+// gets the longer lead.  Before B(s) a helper waits for the A loads issued one
+// step earlier and everything before them (loads retire in issue order),
+// leaving that step's younger code and scale loads in flight.
 #include <algorithm>
 #include <type_traits>
 
