@@ -59,8 +59,6 @@ constexpr int kRow = 128;                        // K bytes per LDS row: one pai
 constexpr int kOpBytes = BM * kRow;              // one operand's rows in a region (32 KB)
 constexpr int kRegionBytes = 2 * kOpBytes;       // A then W
 constexpr int kScaleBytes = 1024;                // per wave: 128 row scales, then 128 column scales
-constexpr int kEpiRow = 136;                     // staged output row: 64 bf16 + 8 bytes of padding
-constexpr int kEpiBytes = 32 * kEpiRow;          // per wave: 32 output rows staged for row stores
 constexpr int kPersistentCap = 256;              // one workgroup per CU
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -76,7 +74,7 @@ struct Kind {
   static constexpr int kFmt = kFp4 ? 4 : 0;                // MFMA operand format: e2m1 or e4m3
   static constexpr int kSB = kFp4 ? 8 : 4;                 // e8m0 bytes per row and region
   static constexpr int kMxRegionBytes = kMx ? 2 * BM * kSB : 0;
-  static constexpr int kWaveBytes = kEpiBytes + (kMx ? 0 : kScaleBytes);
+  static constexpr int kWaveBytes = kMx ? 0 : kScaleBytes;
   static constexpr int kScLoads = kMx ? 0 : 4;              // FP8 scale loads per wave and tile
   static constexpr int kLdsBytes = 2 * kRegionBytes + 2 * kMxRegionBytes + 4 * kWaveBytes;
 };
@@ -309,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   // The first such barrier of a tile has younger operations from the tile
   // change behind the loads it needs: vector memory operations retire in
   // issue order, so it waits only until `pend` of them are left (the previous
-  // epilogue's row stores and the scale loads), which lets the stores drain
+  // epilogue's 32 stores and the scale loads), which lets the stores drain
   // under the next slices; -1 (their number is not fixed: edge tiles) waits
   // for everything.
   auto barrier_tile_start = [&](int pend) __attribute__((always_inline)) {
@@ -328,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
   // the previous tile's epilogue; the next barrier's wait retires them.
   // Per-tensor scales have stride 0: every lane then reads the one scale.
   uint8_t* wave_lds = smem + 2 * kRegionBytes + 2 * T::kMxRegionBytes + wave * T::kWaveBytes;
-  const float* sc_rows = reinterpret_cast<const float*>(wave_lds + kEpiBytes);
+  const float* sc_rows = reinterpret_cast<const float*>(wave_lds);
   const float* sc_cols = sc_rows + 128;
   auto prefetch_scales = [&](int k) __attribute__((always_inline)) {
     if constexpr (!T::kMx) {
@@ -342,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
       const v4i ra = make_rsrc(static_cast<const float*>(g.a_scales) + sa_first, (int)(sa_rows * 4));
       const v4i rw = make_rsrc(static_cast<const float*>(g.w_scales) + sw_first, (int)(sw_rows * 4));
       const int va = (int)g.a_scale_stride * lane * 4, vw = (int)g.w_scale_stride * lane * 4;
-      uint8_t* scr = wave_lds + kEpiBytes;
+      uint8_t* scr = wave_lds;
       lds_load4(ra, scr, va);
       lds_load4(ra, scr + 256, va + (int)g.a_scale_stride * 256);
       lds_load4(rw, scr + 512, vw);
@@ -357,7 +355,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
 
   // ---- epilogue of tile k: each lane owns output row m = 32 i + l % 32 of block
   // i and, per accumulator quad, four consecutive columns.  Returns whether
-  // the wave's quarter took the interior path (exactly 32 row stores).
+  // the wave's quarter took the interior path (exactly 32 stores).
   auto epilogue = [&](int k) __attribute__((always_inline)) -> bool {
     int tm, tn;
     sched.coords(k, tm, tn);
@@ -368,55 +366,47 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
     // flight.
     const int el = fresh_lane();
     const int fr = el & 31, fk = el >> 5;
-    // Rows go out through LDS so that each store writes whole 128-byte lines:
-    // per 32-row block i and 64-column half p, lanes write their bf16 quads
-    // (8 bytes) into a 32-row staging block, then read it back as 16-byte row
-    // pieces (8 lanes per row, 8 rows per instruction).  Staged rows are padded
-    // to 136 bytes, which keeps both the quad writes and the row reads on
-    // distinct banks with constant offsets from one per-lane address.  Interior
-    // quarters store every piece; edge quarters (and C without 16-byte rows)
-    // mask rows past M and columns past N.  One staging path for both keeps
-    // the accumulators' reads in one place, which the register allocator needs.
-    uint8_t* stg = wave_lds;
+    // Stores go straight from registers.  In block (i, j) lane (fr, fk) holds,
+    // per register quad rq, columns 8 rq + 4 fk .. + 3 of row 32 i + fr.  One
+    // v_permlane32_swap per packed dword trades quad 2 h + 1 of the lower half
+    // (fk = 0) for quad 2 h of the upper half, after which lane (fr, fk) holds
+    // the 8 consecutive columns 16 h + 8 fk .. + 7: one 16-byte store, and each
+    // instruction writes 32 contiguous bytes of 32 rows.  Interior quarters
+    // store every piece; edge quarters (and C without 16-byte rows) mask rows
+    // past M and columns past N.
     const float4* cs4 = static_cast<const float4*>(__builtin_assume_aligned(sc_cols, 16));
-    const int rr = el >> 3, rc = el & 7;                 // read-back: row rr + 8 q, 16-byte piece rc
-    uint8_t* wr = stg + fr * kEpiRow + fk * 8;
-    const uint8_t* rd = stg + rr * kEpiRow + rc * 16;
-    const uint32_t voff_c = (uint32_t)(rr * g.ldc * 2 + rc * 16);
+    const int64_t lane_off = (int64_t)fr * g.ldc + 8 * fk;   // elements from the block's first row and column
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float rs = T::kMx ? 1.0f : sc_rows[i * 32 + fr];
+      uint16_t* blk = g.c + (m0 + i * 32) * g.ldc + n0;   // wave-uniform
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
+      for (int j = 0; j < 4; ++j) {
+        float4 cs[4];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = 2 * p + jj;
-          float4 cs[4];
+        for (int rq = 0; rq < 4; ++rq) cs[rq] = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : cs4[j * 8 + rq * 2 + fk];
+        const v16f a = acc[i][j];
+        uint32_t d[4][2];
 #pragma unroll
-          for (int rq = 0; rq < 4; ++rq) cs[rq] = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : cs4[j * 8 + rq * 2 + fk];
-          const v16f a = acc[i][j];
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq)
-            *reinterpret_cast<uint2*>(wr + (jj * 8 + rq * 2) * 8) =
-                uint2{pack_bf16x2(out_val(a[4 * rq + 0], rs, cs[rq].x), out_val(a[4 * rq + 1], rs, cs[rq].y)),
-                      pack_bf16x2(out_val(a[4 * rq + 2], rs, cs[rq].z), out_val(a[4 * rq + 3], rs, cs[rq].w))};
-          __builtin_amdgcn_sched_barrier(0);   // one accumulator block at a time
+        for (int rq = 0; rq < 4; ++rq) {
+          d[rq][0] = pack_bf16x2(out_val(a[4 * rq + 0], rs, cs[rq].x), out_val(a[4 * rq + 1], rs, cs[rq].y));
+          d[rq][1] = pack_bf16x2(out_val(a[4 * rq + 2], rs, cs[rq].z), out_val(a[4 * rq + 3], rs, cs[rq].w));
         }
 #pragma unroll
-        for (int qr = 0; qr < 4; ++qr) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(rd + qr * 8 * kEpiRow + 8);
+        for (int h = 0; h < 2; ++h) {
+          const auto s0 = __builtin_amdgcn_permlane32_swap(d[2 * h][0], d[2 * h + 1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(d[2 * h][1], d[2 * h + 1][1], false, false);
+          const uint4 v = uint4{s0[0], s1[0], s0[1], s1[1]};
           if (interior) {
-            char* base = reinterpret_cast<char*>(g.c + (m0 + i * 32 + 8 * qr) * g.ldc + n0 + p * 64);
-            *reinterpret_cast<uint4*>(base + voff_c) = uint4{lo.x, lo.y, hi.x, hi.y};
+            *reinterpret_cast<uint4*>(blk + lane_off + j * 32 + h * 16) = v;
           } else {
-            const int64_t row = m0 + i * 32 + 8 * qr + rr, col = n0 + p * 64 + rc * 8;
+            const int64_t row = m0 + i * 32 + fr, col = n0 + j * 32 + h * 16 + 8 * fk;
             if (row < g.M) {
               uint16_t* dst = g.c + row * g.ldc + col;
               if (g.vec_store && col + 8 <= g.N) {
-                *reinterpret_cast<uint4*>(dst) = uint4{lo.x, lo.y, hi.x, hi.y};
+                *reinterpret_cast<uint4*>(dst) = v;
               } else {
-                const uint32_t wds[4] = {lo.x, lo.y, hi.x, hi.y};
+                const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int c = 0; c < 8; ++c)
                   if (col + c < g.N) dst[c] = (uint16_t)(wds[c >> 1] >> (16 * (c & 1)));
@@ -424,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
             }
           }
         }
-        __builtin_amdgcn_sched_barrier(0);   // the staging block is read before it is rewritten
+        __builtin_amdgcn_sched_barrier(0);   // one accumulator block at a time
       }
     }
     return interior;
