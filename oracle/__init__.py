@@ -21,6 +21,10 @@ Sources (page title, section):
 * "vLLM-Omni accelerates inference with AutoRound quantization", section
   "Usage" (quantizing a new model): int4 weights, group size 128, zero
   tuning iterations read as round-to-nearest.
+* The same FP8 section's scheme keys for static (supplied) tensor and
+  128-block scales; the online-quantization guide's int8 online path
+  (sections "Key parameters in detail" and "How online quantization works
+  underneath") and its fused FP8 epilogue alpha * (A @ B) + bias.
 
 Every function is pinned by the CPU tests (closed forms, exhaustive code
 tables, exact reproduction, error bounds, brute-force tiny GEMMs).  No
@@ -31,5 +35,7 @@ from .formats import (  # noqa: F401
     e8m0_decode, bf16_to_f32, f32_to_bf16_rne, pack_fp4, unpack_fp4,
     pack_int4, unpack_int4,
 )
-from .quant import SCHEMES, quantize, dequantize, dequant_exact, mx_exponent  # noqa: F401
+from .quant import (  # noqa: F401
+    SCHEMES, STATIC_SCHEMES, quantize, quantize_static, dequantize, dequant_exact, mx_exponent,
+)
 from .gemm import gemm_ref, gemm_ref_entries, rel_fro_error  # noqa: F401

@@ -12,6 +12,10 @@ quantized weight, and restores the shape ("vLLM-Omni Online Quantization
 complete guide", section "How online quantization works underneath",
 step 3).  A is [M, K] (tokens x input channels), W is [N, K] (output x input
 channels, the linear layer's own layout), C is [M, N].
+
+The fused epilogue alpha * (A @ B) + bias, named for the FP8 path in the same
+section, is C = alpha * (A_hat @ W_hat^T) + bias[n] with a scalar fp32 alpha
+and a bf16 bias per output column, both widened exactly.
 """
 from __future__ import annotations
 
@@ -30,24 +34,40 @@ def _a_hat(a) -> np.ndarray:
     return bf16_to_f32(a).astype(np.float64)
 
 
-def gemm_ref(a, w_q: dict) -> np.ndarray:
-    """float64 C[M, N] = A_hat @ W_hat^T.
+def _epilogue(prod, alpha, bias, cols=None):
+    if alpha is not None and alpha != 1.0:
+        prod = float(np.float32(alpha)) * prod
+    if bias is not None:
+        b = np.asarray(bias)
+        if b.dtype != np.uint16 or b.ndim != 1:
+            raise ValueError("bias must be a 1-D array of bf16 bits (uint16)")
+        b = bf16_to_f32(b).astype(np.float64)
+        prod = prod + (b if cols is None else b[np.asarray(cols)])[None, :]
+    return prod
+
+
+def gemm_ref(a, w_q: dict, alpha=None, bias=None) -> np.ndarray:
+    """float64 C[M, N] = alpha * (A_hat @ W_hat^T) + bias.
 
     ``a`` is a quantized activation (dict from ``quantize``) or, for W4A16,
-    the bf16 activation bits.  ``w_q`` is a quantized weight.
+    the bf16 activation bits.  ``w_q`` is a quantized weight.  ``alpha``
+    (fp32, default 1) and ``bias`` (bf16 bits [N], default none) are the
+    fused epilogue.
     """
     A = _a_hat(a)
     W = dequant_exact(w_q)
     if A.shape[1] != W.shape[1]:
         raise ValueError("K mismatch")
-    return A @ W.T
+    if bias is not None and np.asarray(bias).shape != (W.shape[0],):
+        raise ValueError("bias must have one entry per output column")
+    return _epilogue(A @ W.T, alpha, bias)
 
 
-def gemm_ref_entries(a, w_q: dict, rows, cols) -> np.ndarray:
+def gemm_ref_entries(a, w_q: dict, rows, cols, alpha=None, bias=None) -> np.ndarray:
     """C[rows[i], cols[j]] for the given index lists, each as one dot product."""
     A = _a_hat(a)[np.asarray(rows)]
     W = dequant_exact(w_q)[np.asarray(cols)]
-    return A @ W.T
+    return _epilogue(A @ W.T, alpha, bias, cols)
 
 
 def rel_fro_error(c_test, c_ref) -> float:

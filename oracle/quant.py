@@ -16,13 +16,19 @@ mxfp4          u8 two e2m1 [rows, cols/2]    u8 e8m0 [rows, cols/32]
 w4a16_asym     u32 eight int4 [rows, cols/8] bf16 [rows, cols/128]
                                              (u8 zero-points [rows, cols/128])
 w4a16_sym      as w4a16_asym, zero-point fixed at 8
+int8_row       i8 [rows, cols]               f32 [rows]
 =============  ============================  ===============================
 
 Sources: FP8 scale granularities (tensor, token, 128x128 block, all dynamic
 and symmetric) from "[vLLM] Other quantization: FP8, ModelOpt, INC, TorchAO,
 Quark", section "FP8".  MX scales (one e8m0 exponent per 32 K-elements) and
 fp4 packing from "vLLM-Omni Online Quantization complete guide", section "How
-online quantization works underneath", steps 2-3.  int4 group-128 from
+online quantization works underneath", steps 2-3.  Static FP8 scales (a
+supplied scale per tensor or per 128-block instead of a computed one) from
+the FP8 section's list of scheme keys.  int8 W8A8 online (dynamic
+activation scales only; a static activation scheme is an error) from the
+online-quantization guide, sections "Key parameters in detail" and "How
+online quantization works underneath".  int4 group-128 from
 "vLLM-Omni accelerates inference with AutoRound quantization", section
 "Usage" (the auto-round command and the checkpoint's quantization_config).
 
@@ -31,6 +37,12 @@ Readings where the pages are silent (all listed in the design notes):
   first, then rounded to e4m3fn (round-to-nearest-even, saturating).
   If s comes out 0 (amax = 0, or amax so small that amax/448 underflows),
   s = 1.
+* Static FP8: the supplied fp32 scale replaces s; the quotient is rounded
+  the same way and saturates at +-448 (a calibrated scale can be smaller
+  than amax / 448).  Static schemes are FP8 per tensor and per 128-block.
+* int8 (symmetric, per row: per token for activations, per output channel
+  for weights): s = fp32(amax / 127), 1 if that is 0;
+  q = clamp(rne(fp32(x / s)), -128, 127).
 * MX shared exponent X = clamp(floor(log2 amax) - emax, -127, 127), emax = 8
   for e4m3 and 2 for e2m1; the element is rounded from x * 2^-X; amax = 0
   gives X = -127 (code 0).
@@ -51,7 +63,8 @@ from .formats import (
 )
 
 SCHEMES = ("fp8_tensor", "fp8_row", "fp8_block128", "mxfp8", "mxfp4",
-           "w4a16_asym", "w4a16_sym")
+           "w4a16_asym", "w4a16_sym", "int8_row")
+STATIC_SCHEMES = ("fp8_tensor", "fp8_block128")
 ROLES = ("activation", "weight")
 
 _F32 = np.float32
@@ -176,6 +189,15 @@ def _quant_int4(x, sym: bool):
     return pack_int4(q), s_bits.astype(np.uint16), z.astype(np.uint8)
 
 
+# ---------------------------------------------------------------- int8, fp32 scale
+def _quant_int8_row(x):
+    amax = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], _F32)
+    s = (amax.astype(_F32) / _F32(127.0)).astype(_F32)
+    s = np.where(s == 0, _F32(1.0), s).astype(_F32)
+    q = _rne_int((x / s[:, None]).astype(_F32))              # fp32 quotient, then RNE
+    return np.clip(q, -128, 127).astype(np.int8), s
+
+
 # ---------------------------------------------------------------- public API
 def quantize(x_bits, scheme: str, role: str = "activation") -> dict:
     """Quantize a bf16 tensor; returns {"codes", "scales", "zeros"} (canonical layouts)."""
@@ -192,10 +214,40 @@ def quantize(x_bits, scheme: str, role: str = "activation") -> dict:
         codes, scales = _quant_fp8_block(x, role)
     elif scheme in ("mxfp8", "mxfp4"):
         codes, scales = _quant_mx(x, scheme)
+    elif scheme == "int8_row":
+        codes, scales = _quant_int8_row(x)
     else:
         codes, scales, zeros = _quant_int4(x, scheme == "w4a16_sym")
     return {"scheme": scheme, "role": role, "rows": rows, "cols": cols,
             "codes": codes, "scales": scales, "zeros": zeros}
+
+
+def _static_scale_shape(scheme, role, rows, cols):
+    if scheme == "fp8_tensor":
+        return (1,)
+    return (rows, cols // 128) if role == "activation" else (rows // 128, cols // 128)
+
+
+def quantize_static(x_bits, scheme: str, role: str, scales) -> dict:
+    """FP8 quantization with supplied (static, calibrated) fp32 scales.
+
+    ``scales`` has the scheme's canonical scale shape (f32[1] per tensor;
+    f32[rows, cols/128] or f32[rows/128, cols/128] per 128-block) and every
+    value must be finite and positive.  Codes are RNE_sat(fp32(x / s)): the
+    amax pass is skipped, and values beyond 448 s saturate.
+    """
+    if scheme not in STATIC_SCHEMES:
+        raise ValueError(f"static scales are defined for {STATIC_SCHEMES} only, not {scheme!r}")
+    x_bits, rows, cols = _check(x_bits, scheme, role)
+    x = bf16_to_f32(x_bits)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input is outside the quantizer's domain")
+    s = np.asarray(scales, dtype=_F32).reshape(_static_scale_shape(scheme, role, rows, cols))
+    if not (np.all(np.isfinite(s)) and np.all(s > 0)):
+        raise ValueError("static scales must be finite and positive")
+    q = {"scheme": scheme, "role": role, "rows": rows, "cols": cols, "scales": s.copy(), "zeros": None}
+    q["codes"] = _fp8_codes(x, _expand_scale_f32(q))
+    return q
 
 
 def _expand_scale_f32(q) -> np.ndarray:
@@ -203,7 +255,7 @@ def _expand_scale_f32(q) -> np.ndarray:
     rows, cols, s = q["rows"], q["cols"], np.asarray(q["scales"], dtype=_F32)
     if q["scheme"] == "fp8_tensor":
         return np.full((rows, cols), s.reshape(-1)[0], dtype=_F32)
-    if q["scheme"] == "fp8_row":
+    if q["scheme"] in ("fp8_row", "int8_row"):
         return np.repeat(s.reshape(rows, 1), cols, axis=1)
     if q["role"] == "activation":
         return np.repeat(s.reshape(rows, cols // 128), 128, axis=1)
@@ -215,6 +267,8 @@ def _decoded(q):
     scheme, rows, cols = q["scheme"], q["rows"], q["cols"]
     if scheme in ("fp8_tensor", "fp8_row", "fp8_block128"):
         return e4m3_decode(q["codes"]), _expand_scale_f32(q).astype(np.float64)
+    if scheme == "int8_row":
+        return np.asarray(q["codes"], dtype=np.int8).astype(np.float64), _expand_scale_f32(q).astype(np.float64)
     if scheme in ("mxfp8", "mxfp4"):
         vals = e4m3_decode(q["codes"]) if scheme == "mxfp8" else e2m1_decode(unpack_fp4(q["codes"]))
         sc = np.repeat(e8m0_decode(q["scales"]).reshape(rows, cols // 32), 32, axis=1)

@@ -93,6 +93,10 @@ def _frac_dequant(q):
                 else:
                     s = q["scales"][r // 128, k // 128]
                 out[r][k] = v * Fraction(float(s))
+            elif scheme == "int8_row":
+                byte = int(np.asarray(q["codes"]).view(np.uint8)[r, k])
+                v = Fraction(byte - 256 if byte > 127 else byte)       # two's complement by hand
+                out[r][k] = v * Fraction(float(q["scales"][r]))
             elif scheme in ("mxfp8", "mxfp4"):
                 if scheme == "mxfp8":
                     c = q["codes"][r, k]
@@ -113,7 +117,7 @@ def _frac_dequant(q):
 
 
 @pytest.mark.parametrize("scheme", ["fp8_tensor", "fp8_row", "fp8_block128", "mxfp8", "mxfp4",
-                                    "w4a16_asym"])
+                                    "w4a16_asym", "int8_row"])
 def test_random_tiny_gemm_against_exact_rationals(scheme):
     rng = np.random.default_rng(7 + len(scheme) * 31 + ord(scheme[-1]))
     for trial in range(3):
@@ -158,3 +162,49 @@ def test_rel_fro_error():
     ref = np.array([[3.0, 4.0]])
     assert oracle.rel_fro_error(ref, ref) == 0.0
     assert abs(oracle.rel_fro_error(np.array([[3.0, 4.05]]), ref) - 0.01) < 1e-12
+
+
+def test_epilogue_alpha_bias_hand_checked():
+    """FP8 per tensor, K = 32: A codes all 1.0 (0x38) with s_a = 2; W row 0 all 0.5
+    (0x30), row 1 all 2.0 (0x40), s_w = 1.  Products 2*32*0.5 = 32 and 2*32*2 = 128;
+    alpha = 0.5, bias = [1, -3]: C = [17, 61]."""
+    a = {"scheme": "fp8_tensor", "role": "activation", "rows": 1, "cols": 32,
+         "codes": np.full((1, 32), 0x38, np.uint8), "scales": np.array([2.0], np.float32), "zeros": None}
+    w = {"scheme": "fp8_tensor", "role": "weight", "rows": 2, "cols": 32,
+         "codes": np.stack([np.full(32, 0x30), np.full(32, 0x40)]).astype(np.uint8),
+         "scales": np.array([1.0], np.float32), "zeros": None}
+    bias = f32_to_bf16_bits(np.array([1.0, -3.0], np.float32))
+    assert oracle.gemm_ref(a, w).tolist() == [[32.0, 128.0]]
+    assert oracle.gemm_ref(a, w, alpha=0.5, bias=bias).tolist() == [[17.0, 61.0]]
+    assert oracle.gemm_ref_entries(a, w, [0], [1], alpha=0.5, bias=bias).tolist() == [[61.0]]
+
+
+def test_int8_hand_checked():
+    """int8 per row, K = 4: A = [127, -128, 1, 0] with s_a = 0.5, W = [1, 1, 2, 5] with
+    s_w = 4: sum = 127 - 128 + 2 = 1, C = 1 * 0.5 * 4 = 2."""
+    a = {"scheme": "int8_row", "role": "activation", "rows": 1, "cols": 4,
+         "codes": np.array([[127, -128, 1, 0]], np.int8), "scales": np.array([0.5], np.float32), "zeros": None}
+    w = {"scheme": "int8_row", "role": "weight", "rows": 1, "cols": 4,
+         "codes": np.array([[1, 1, 2, 5]], np.int8), "scales": np.array([4.0], np.float32), "zeros": None}
+    assert oracle.gemm_ref(a, w).tolist() == [[2.0]]
+
+
+@pytest.mark.parametrize("scheme", ["fp8_tensor", "fp8_row", "fp8_block128", "int8_row"])
+def test_random_tiny_epilogue_against_exact_rationals(scheme):
+    """alpha * sum + bias against Fractions: a dropped alpha, a bias on the wrong axis
+    (rows instead of columns) or a bias scaled by alpha fails."""
+    rng = np.random.default_rng(17 + len(scheme))
+    M, N, K = 3, 128 if scheme == "fp8_block128" else 5, 256
+    a_q = oracle.quantize(small_case(300, M, K, 1.0), scheme, "activation")
+    w_q = oracle.quantize(small_case(301, N, K, 0.02), scheme, "weight")
+    alpha = np.float32(rng.uniform(0.25, 3.0))
+    bias = f32_to_bf16_bits(rng.normal(0, 1, N).astype(np.float32))
+    bias_f = [Fraction(float(v)) for v in F.bf16_to_f32(bias)]
+    A, W = _frac_dequant(a_q), _frac_dequant(w_q)
+    c = oracle.gemm_ref(a_q, w_q, alpha=alpha, bias=bias)
+    for m in range(M):
+        for n in range(min(N, 6)):
+            terms = [A[m][k] * W[n][k] for k in range(K)]
+            exact = Fraction(float(alpha)) * sum(terms, Fraction(0)) + bias_f[n]
+            bound = 4 * K * 2.0 ** -53 * (float(alpha) * float(sum(abs(t) for t in terms)) + abs(float(bias_f[n])))
+            assert abs(c[m, n] - float(exact)) <= bound + 1e-300, (m, n)

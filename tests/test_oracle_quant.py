@@ -370,3 +370,113 @@ def test_scheme_validation():
         oracle.quantize(np.zeros((64, 128), np.uint16), "fp8_block128", "weight")
     with pytest.raises(ValueError):
         oracle.quantize(x, "nvfp4")
+
+
+# ---------------------------------------------------------------- static FP8 scales
+def test_golden_fp8_static_tensor():
+    g = keyed("fp8_static_tensor_worked_example.txt")
+    x = bf16(np.stack([parse_floats(r) for r in g["input"]]))
+    s = np.array([float(g["scale"][0][0])], np.float32)
+    q = oracle.quantize_static(x, "fp8_tensor", "activation", s)
+    expect = np.stack([parse_hex(r) for r in g["codes"]]).astype(np.uint8)
+    assert np.array_equal(q["codes"], expect)
+    assert q["scales"].tolist() == [0.03125]
+
+
+@pytest.mark.parametrize("role", ["activation", "weight"])
+def test_fp8_static_block_exact_reproduction_and_placement(role):
+    """Static 128-block scales: x built as codes times a distinct power-of-two scale per
+    block comes back unchanged only if each block is divided by its own scale (a
+    transposed or mis-indexed scale array fails)."""
+    rng = np.random.default_rng(5)
+    rows, cols = 256, 384
+    vals = F.e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8))
+    codes = rng.choice(np.arange(0x00, 0x7F), size=(rows, cols)).astype(np.uint8)
+    signs = rng.choice([0, 0x80], size=(rows, cols)).astype(np.uint8)
+    codes = codes | signs
+    codes[codes == 0x80] = 0x00
+    if role == "activation":
+        sh = (rows, cols // 128)
+        s = np.ldexp(1.0, rng.integers(-12, 4, size=sh)).astype(np.float32)
+        per = np.repeat(s, 128, axis=1)
+    else:
+        sh = (rows // 128, cols // 128)
+        s = np.ldexp(1.0, rng.integers(-12, 4, size=sh)).astype(np.float32)
+        per = np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
+    x = F.e4m3_decode(codes) * per
+    xb = bf16(x.astype(np.float32))
+    q = oracle.quantize_static(xb, "fp8_block128", role, s)
+    assert np.array_equal(q["codes"], codes)
+    assert vals.max() == 448.0
+
+
+def test_fp8_static_saturates_beyond_448_s():
+    """A static scale below amax / 448 saturates: |x| / s above 448 gives +-448."""
+    x = bf16([[1.0, -1.0, 0.5, 2.0 ** -20, -2.0 ** 10, 448.0 / 64]])
+    q = oracle.quantize_static(x, "fp8_tensor", "activation", np.array([2.0 ** -6], np.float32))
+    # 64, -64, 32, 2^-14 (below the smallest subnormal 2^-9, rounds to 0), -65536 -> -448, 448
+    assert q["codes"].tolist() == [[0x68, 0xE8, 0x60, 0x00, 0xFE, 0x7E]]
+
+
+def test_fp8_static_with_the_dynamic_scale_equals_dynamic():
+    x = small_case(11, 6, 256, 1.0)
+    for scheme, role in (("fp8_tensor", "activation"), ("fp8_block128", "activation")):
+        d = oracle.quantize(x, scheme, role)
+        s = oracle.quantize_static(x, scheme, role, d["scales"])
+        assert np.array_equal(d["codes"], s["codes"])
+
+
+def test_static_scheme_validation():
+    x = small_case(1, 2, 128, 1.0)
+    with pytest.raises(ValueError):
+        oracle.quantize_static(x, "fp8_row", "activation", np.ones(2, np.float32))
+    with pytest.raises(ValueError):
+        oracle.quantize_static(x, "int8_row", "activation", np.ones(2, np.float32))
+    with pytest.raises(ValueError):
+        oracle.quantize_static(x, "fp8_tensor", "activation", np.array([0.0], np.float32))
+    with pytest.raises(ValueError):
+        oracle.quantize_static(x, "fp8_tensor", "activation", np.array([np.inf], np.float32))
+
+
+# ---------------------------------------------------------------- int8 per row
+def test_golden_int8_row():
+    g = keyed("int8_row_worked_example.txt")
+    x = bf16(np.stack([parse_floats(r) for r in g["input"]]))
+    for role in ("activation", "weight"):
+        q = oracle.quantize(x, "int8_row", role)
+        assert q["scales"].tolist() == [float(v) for v in g["scale"][0]]
+        expect = np.stack([parse_hex(r) for r in g["codes"]]).astype(np.uint8)
+        assert np.array_equal(q["codes"].view(np.uint8), expect)
+
+
+def test_int8_exact_reproduction():
+    """Rows k * 2^e with integer k in [-127, 127] and k = 127 present: s = 2^e and the
+    codes are k, row by row with distinct e (a mis-indexed scale fails)."""
+    rng = np.random.default_rng(9)
+    rows, cols = 8, 96
+    k = rng.integers(-127, 128, size=(rows, cols))
+    k[:, 5] = 127
+    e = np.arange(-6, -6 + rows)
+    x = bf16((k * np.ldexp(1.0, e)[:, None]).astype(np.float32))
+    q = oracle.quantize(x, "int8_row", "activation")
+    assert np.array_equal(q["codes"].astype(np.int64), k)
+    assert np.array_equal(q["scales"], np.ldexp(1.0, e).astype(np.float32))
+
+
+def test_int8_error_bound_and_range():
+    x = small_case(3, 16, 512, 1.0)
+    q = oracle.quantize(x, "int8_row", "weight")
+    xf = F.bf16_to_f32(x).astype(np.float64)
+    s = q["scales"].astype(np.float64)[:, None]
+    assert q["codes"].min() >= -127 and q["codes"].max() <= 127
+    # half a step, plus the fp32 rounding of the quotient (at most 127 * 2^-24 steps)
+    assert np.all(np.abs(q["codes"] * s - xf) <= s * (0.5 + 2.0 ** -16))
+    assert np.all(np.abs(q["codes"]).max(axis=1) == 127)
+
+
+def test_int8_dequantize_rounds_once():
+    x = small_case(4, 3, 64, 1.0)
+    q = oracle.quantize(x, "int8_row", "activation")
+    y = F.bf16_to_f32(oracle.dequantize(q))
+    prod = (q["codes"].astype(np.float32) * q["scales"][:, None]).astype(np.float32)
+    assert np.array_equal(y, F.bf16_to_f32(F.f32_to_bf16_rne(prod)))
