@@ -38,6 +38,8 @@
  *   W4A16_ASYM    codes u32 [rows, cols/8], element k   scales bf16 [cols/128, rows]
  *                 at bits 4*(k mod 8)                   zeros u8 [cols/128, rows] (0..15)
  *   W4A16_SYM     as W4A16_ASYM with every zero-point 8
+ *   INT8_ROW      codes i8 [rows, cols] (two's         scales f32 [rows]
+ *                 complement)
  * All codes are K-contiguous, which is the operand order the matrix cores
  * consume, so weights need no re-layout after quantization.
  * W4A16 scales and zero-points are group-major ([group, row]): one K-group's
@@ -59,7 +61,7 @@
 extern "C" {
 #endif
 
-#define PQL_VERSION 1
+#define PQL_VERSION 2
 
 typedef enum pql_status {
   PQL_OK = 0,
@@ -89,6 +91,13 @@ typedef enum pql_status {
  *             z = clamp(rne(fp32(-min(0,min x) / s)), 0, 15)
  *       sym:  s = bf16(fp32(max|x| / 7)), z = 8
  *       q = clamp(rne(fp32(x / s)) + z, 0, 15); s = 0 is replaced by 1 (z = 0 asym).
+ *   INT8_ROW: int8 W8A8, symmetric, one fp32 scale per row (per token for
+ *     activations, per output channel for weights), dynamic only ("vLLM-Omni
+ *     Online Quantization complete guide", sections "Key parameters in
+ *     detail" and "How online quantization works underneath": the int8
+ *     online path quantizes weights with weight scales; its activation
+ *     scales are dynamic, a static activation scheme is an error).
+ *     s = fp32(amax / 127) (1 if that is 0); code = clamp(rne(fp32(x / s)), -128, 127).
  */
 typedef enum pql_scheme {
   PQL_FP8_TENSOR = 0,
@@ -97,7 +106,8 @@ typedef enum pql_scheme {
   PQL_MXFP8 = 3,
   PQL_MXFP4 = 4,
   PQL_W4A16_ASYM = 5,
-  PQL_W4A16_SYM = 6
+  PQL_W4A16_SYM = 6,
+  PQL_INT8_ROW = 7
 } pql_scheme;
 
 typedef enum pql_role { PQL_ACTIVATION = 0, PQL_WEIGHT = 1 } pql_role;
@@ -120,7 +130,7 @@ const char* pql_last_error(void);
  * [rows, cols] tensor in the canonical layout (zeros_bytes is 0 except for
  * W4A16).  Size outputs are host pointers; any may be NULL.
  * Errors: INVALID_ARGUMENT for negative sizes or cols / rows that the scheme
- * cannot block (cols % 32 for FP8 tensor/row and MX, cols % 128 for
+ * cannot block (cols % 32 for FP8 tensor/row, INT8_ROW and MX, cols % 128 for
  * FP8_BLOCK128 and W4A16, rows % 128 for FP8_BLOCK128 weights);
  * UNSUPPORTED for W4A16 activations or an unknown scheme / role. */
 pql_status pql_quantized_sizes(int scheme, int role, int64_t rows, int64_t cols,
@@ -170,6 +180,48 @@ pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t 
                        const void* w_codes, const void* w_scales, const void* w_zeros,
                        int64_t N, void* c, int64_t ldc, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* Static-scale FP8 quantization (FP8_TENSOR and FP8_BLOCK128 only): the
+ * scale is supplied instead of computed from x ("[vLLM] Other quantization:
+ * FP8, ModelOpt, INC, TorchAO, Quark", section "FP8": the static tensor-wise
+ * and static 128-block symmetric scheme keys).  `scales` (device, read only)
+ * is in the scheme's canonical scale layout for `role` (f32 [1]; f32
+ * [rows, cols/128] for activations, f32 [rows/128, cols/128] for weights) and
+ * must hold finite positive values (not checked on the device: a zero, NaN or
+ * infinite scale gives meaningless codes).  codes = e4m3fn(fp32(x / s)),
+ * round to nearest even, saturating at +-448: values beyond 448 s clamp,
+ * which a calibrated scale makes possible.  Same shape rules as
+ * pql_quantize; rows = 0 is a no-op.  UNSUPPORTED for other schemes
+ * (INT8_ROW has no static scheme). */
+pql_status pql_quantize_static(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                               const void* scales, void* codes, void* stream);
+
+/* pql_qgemm with the fused epilogue ("vLLM-Omni Online Quantization complete
+ * guide", section "How online quantization works underneath": the FP8 path's
+ * alpha * (A @ B) + bias):
+ *   C[m, n] = bf16_RNE(alpha * (A_hat W_hat^T)[m, n] + bias[n])
+ * computed in fp32 with one rounding to bf16.  alpha is a finite host fp32;
+ * bias is a device bf16 [N] vector (16-byte aligned, N even) or NULL.
+ * Defined for FP8_TENSOR, FP8_ROW, FP8_BLOCK128 and INT8_ROW; other schemes
+ * are UNSUPPORTED unless alpha == 1 and bias == NULL (then identical to
+ * pql_qgemm).  INT8_ROW sums in int32, then scales in fp32.  Other arguments
+ * and errors as pql_qgemm. */
+pql_status pql_qgemm_ex(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
+                        const void* w_zeros, int64_t M, int64_t N, int64_t K, float alpha, const void* bias,
+                        void* c, int64_t ldc, void* stream);
+
+/* pql_qlinear with the fused epilogue (alpha, bias as pql_qgemm_ex) and,
+ * optionally, static activation scales: with `a_static_scales` non-NULL
+ * (FP8_TENSOR: f32 [1]; FP8_BLOCK128: f32 [M, K/128]; device, read only,
+ * finite and positive) the activation is quantized with those scales as
+ * pql_quantize_static does, and the GEMM reads them in place; NULL means
+ * dynamic scales, as pql_qlinear.  Static scales for any other scheme are
+ * UNSUPPORTED.  The workspace is the one pql_workspace_size(PQL_OP_QLINEAR)
+ * gives, in both cases. */
+pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
+                          const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
+                          const void* bias, void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Name of the kernel that `op` would launch for these sizes (for "no silent
  * fallback" checks); "" if the combination is invalid.  Static string. */

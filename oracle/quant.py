@@ -246,7 +246,11 @@ def quantize_static(x_bits, scheme: str, role: str, scales) -> dict:
     if not (np.all(np.isfinite(s)) and np.all(s > 0)):
         raise ValueError("static scales must be finite and positive")
     q = {"scheme": scheme, "role": role, "rows": rows, "cols": cols, "scales": s.copy(), "zeros": None}
-    q["codes"] = _fp8_codes(x, _expand_scale_f32(q))
+    with np.errstate(over="ignore"):
+        quot = (x / _expand_scale_f32(q)).astype(_F32)   # may overflow to +-inf for tiny s
+    # Saturation first: every |quotient| above 448 (an infinite one included)
+    # encodes as 448 with its sign, exactly as RNE_sat does for finite values.
+    q["codes"] = e4m3_encode(np.clip(quot, -E4M3_MAX, E4M3_MAX).astype(np.float64))
     return q
 
 

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_PKG, "libpql.so")
 MX_CHUNK = {"mxfp8": 4, "mxfp4": 8}
 
 SCHEMES = {"fp8_tensor": 0, "fp8_row": 1, "fp8_block128": 2, "mxfp8": 3, "mxfp4": 4,
-           "w4a16_asym": 5, "w4a16_sym": 6}
+           "w4a16_asym": 5, "w4a16_sym": 6, "int8_row": 7}
+STATIC_SCHEMES = ("fp8_tensor", "fp8_block128")
 ROLES = {"activation": 0, "weight": 1}
 OPS = {"quantize": 0, "dequantize": 1, "qgemm": 2, "qlinear": 3}
 
@@ -55,8 +56,12 @@ def lib() -> ctypes.CDLL:
         L.pql_dequantize.argtypes = [ci, ci, vp, vp, vp, i64, i64, vp, i64, vp]
         L.pql_qgemm.argtypes = [ci, vp, vp, vp, vp, vp, i64, i64, i64, vp, i64, vp]
         L.pql_qlinear.argtypes = [ci, vp, i64, i64, i64, vp, vp, vp, i64, vp, i64, vp, sz, vp]
+        f32 = ctypes.c_float
+        L.pql_quantize_static.argtypes = [ci, ci, vp, i64, i64, i64, vp, vp, vp]
+        L.pql_qgemm_ex.argtypes = [ci, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp, vp, i64, vp]
+        L.pql_qlinear_ex.argtypes = [ci, vp, i64, i64, i64, vp, vp, vp, vp, i64, f32, vp, vp, i64, vp, sz, vp]
         for f in ("pql_quantized_sizes", "pql_workspace_size", "pql_quantize", "pql_dequantize",
-                  "pql_qgemm", "pql_qlinear"):
+                  "pql_qgemm", "pql_qlinear", "pql_quantize_static", "pql_qgemm_ex", "pql_qlinear_ex"):
             getattr(L, f).restype = ci
         _lib = L
     return _lib
@@ -138,6 +143,10 @@ def _alloc_q(scheme: str, role: str, rows: int, cols: int, device) -> QTensor:
         codes = torch.empty((rows, cols // 8), dtype=torch.int32, device=device)
         scales = torch.empty((cols // 128, rows), dtype=torch.bfloat16, device=device)   # group-major
         zeros = torch.empty((cols // 128, rows), dtype=torch.uint8, device=device)
+    elif scheme == "int8_row":
+        codes = torch.empty((rows, cols), dtype=torch.int8, device=device)
+        scales = torch.empty((rows,), dtype=torch.float32, device=device)
+        zeros = None
     else:
         codes = torch.empty((rows, cols if scheme != "mxfp4" else cols // 2), dtype=torch.uint8, device=device)
         if scheme in ("mxfp8", "mxfp4"):
@@ -188,6 +197,33 @@ def quantize(x: torch.Tensor, scheme: str, role: str = "activation", workspace: 
     return q
 
 
+def quantize_static(x: torch.Tensor, scheme: str, role: str, scales: torch.Tensor,
+                    out: QTensor | None = None) -> QTensor:
+    """FP8 quantization with supplied (static, calibrated) fp32 scales in the scheme's
+    canonical scale layout (fp8_tensor: [1]; fp8_block128: [rows, K/128] activations,
+    [rows/128, K/128] weights).  The result holds ``scales`` itself."""
+    if scheme not in STATIC_SCHEMES:
+        raise NotImplementedError(f"static scales are defined for {STATIC_SCHEMES} only, not {scheme!r}")
+    x = _as_2d_bf16(x)
+    rows, cols = x.shape
+    if scales.dtype != torch.float32 or not scales.is_contiguous() or scales.device != x.device:
+        raise ValueError("scales must be a contiguous float32 tensor on the input's device")
+    q = out if out is not None else _alloc_q(scheme, role, rows, cols, x.device)
+    if scales.numel() != q.scales.numel():
+        raise ValueError(f"expected {q.scales.numel()} scales, got {scales.numel()}")
+    _check(lib().pql_quantize_static(_scheme(scheme), _role(role), x.data_ptr(), rows, cols, x.stride(0),
+                                     scales.data_ptr(), q.codes.data_ptr(), _stream(x.device)), "quantize_static")
+    return QTensor(scheme, role, rows, cols, q.codes, scales.reshape(q.scales.shape), None)
+
+
+def _bias_ptr(bias, n: int, device):
+    if bias is None:
+        return None
+    if bias.dtype != torch.bfloat16 or bias.shape != (n,) or not bias.is_contiguous() or bias.device != device:
+        raise ValueError(f"bias must be a contiguous bfloat16 [{n}] tensor on the weight's device")
+    return bias.data_ptr()
+
+
 def dequantize(q: QTensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """bf16 [rows, cols] = bf16(decode(code) * scale)."""
     if out is None:
@@ -198,8 +234,11 @@ def dequantize(q: QTensor, out: torch.Tensor | None = None) -> torch.Tensor:
     return out
 
 
-def qgemm(a, w: QTensor, out: torch.Tensor | None = None) -> torch.Tensor:
-    """C[M, N] = A_hat * W_hat^T on quantized operands (W4A16: ``a`` is the bf16 activation)."""
+def qgemm(a, w: QTensor, out: torch.Tensor | None = None, alpha: float = 1.0,
+          bias: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] = alpha * (A_hat * W_hat^T) + bias on quantized operands (W4A16: ``a`` is the
+    bf16 activation).  ``alpha`` and ``bias`` (bf16 [N]) are the fused epilogue of the FP8
+    and int8 schemes."""
     if w.role != "weight":
         raise ValueError("the second operand must be a quantized weight")
     if isinstance(a, QTensor):
@@ -217,16 +256,20 @@ def qgemm(a, w: QTensor, out: torch.Tensor | None = None) -> torch.Tensor:
         raise ValueError(f"K mismatch: {K} vs {w.cols}")
     if out is None:
         out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=w.device)
-    _check(lib().pql_qgemm(_scheme(w.scheme), a_ptr, as_ptr, w.codes.data_ptr(), w.scales.data_ptr(),
-                           _ptr(w.zeros), M, w.rows, K, out.data_ptr(), out.stride(0),
-                           _stream(w.device)), "qgemm")
+    _check(lib().pql_qgemm_ex(_scheme(w.scheme), a_ptr, as_ptr, w.codes.data_ptr(), w.scales.data_ptr(),
+                              _ptr(w.zeros), M, w.rows, K, float(alpha), _bias_ptr(bias, w.rows, w.device),
+                              out.data_ptr(), out.stride(0), _stream(w.device)), "qgemm")
     return out
 
 
 def qlinear(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None,
-            workspace: torch.Tensor | None = None) -> torch.Tensor:
+            workspace: torch.Tensor | None = None, alpha: float = 1.0, bias: torch.Tensor | None = None,
+            act_scales: torch.Tensor | None = None) -> torch.Tensor:
     """The quantized linear layer's forward: flatten x[..., K] to 2-D, quantize it with the
-    weight's scheme (activation rule), GEMM against ``w``, restore the leading shape."""
+    weight's scheme (activation rule), GEMM against ``w``, restore the leading shape.
+    ``alpha`` / ``bias`` are the fused epilogue; ``act_scales`` (fp32, the scheme's
+    activation scale layout) makes the activation scales static (fp8_tensor and
+    fp8_block128)."""
     if w.role != "weight":
         raise ValueError("w must be a quantized weight")
     lead = x.shape[:-1]
@@ -242,10 +285,14 @@ def qlinear(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None,
     wsb = workspace_size("qlinear", w.scheme, "activation", M, w.rows, K)
     if wsb and workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
-    _check(lib().pql_qlinear(_scheme(w.scheme), x2.data_ptr(), M, K, x2.stride(0), w.codes.data_ptr(),
-                             w.scales.data_ptr(), _ptr(w.zeros), w.rows, out.data_ptr(), out.stride(0),
-                             _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                             _stream(x.device)), "qlinear")
+    if act_scales is not None and (act_scales.dtype != torch.float32 or not act_scales.is_contiguous()
+                                   or act_scales.device != x.device):
+        raise ValueError("act_scales must be a contiguous float32 tensor on the input's device")
+    _check(lib().pql_qlinear_ex(_scheme(w.scheme), x2.data_ptr(), M, K, x2.stride(0), _ptr(act_scales),
+                                w.codes.data_ptr(), w.scales.data_ptr(), _ptr(w.zeros), w.rows, float(alpha),
+                                _bias_ptr(bias, w.rows, x.device), out.data_ptr(), out.stride(0),
+                                _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                _stream(x.device)), "qlinear")
     return out.reshape(*lead, w.rows)
 
 

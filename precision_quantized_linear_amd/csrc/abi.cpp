@@ -45,20 +45,23 @@ const char* scheme_name(int s) {
     case PQL_MXFP4: return "MXFP4";
     case PQL_W4A16_ASYM: return "W4A16_ASYM";
     case PQL_W4A16_SYM: return "W4A16_SYM";
+    case PQL_INT8_ROW: return "INT8_ROW";
   }
   return "?";
 }
 
 bool is_w4a16(int s) { return s == PQL_W4A16_ASYM || s == PQL_W4A16_SYM; }
 bool is_mx(int s) { return s == PQL_MXFP8 || s == PQL_MXFP4; }
+bool valid_scheme(int s) { return s >= PQL_FP8_TENSOR && s <= PQL_INT8_ROW; }
+// Schemes whose GEMM takes the fused epilogue alpha * (A W^T) + bias.
+bool has_epilogue(int s) { return s == PQL_FP8_TENSOR || s == PQL_FP8_ROW || s == PQL_FP8_BLOCK128 || s == PQL_INT8_ROW; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
 int64_t k_granule(int scheme) { return (scheme == PQL_FP8_BLOCK128 || is_w4a16(scheme)) ? 128 : 32; }
 
 pql_status check_scheme_role(int scheme, int role) {
-  if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM)
-    return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
+  if (!valid_scheme(scheme)) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
   if (role != PQL_ACTIVATION && role != PQL_WEIGHT) return fail(PQL_ERR_UNSUPPORTED, "unknown role %d", role);
   if (is_w4a16(scheme) && role == PQL_ACTIVATION)
     return fail(PQL_ERR_UNSUPPORTED, "%s quantizes weights only; activations stay bf16", scheme_name(scheme));
@@ -86,7 +89,8 @@ Sizes sizes_of(int scheme, int role, int64_t rows, int64_t cols) {
   const size_t R = (size_t)rows, C = (size_t)cols;
   switch (scheme) {
     case PQL_FP8_TENSOR: s.codes = R * C; s.scales = 4; break;
-    case PQL_FP8_ROW: s.codes = R * C; s.scales = 4 * R; break;
+    case PQL_FP8_ROW:
+    case PQL_INT8_ROW: s.codes = R * C; s.scales = 4 * R; break;
     case PQL_FP8_BLOCK128:
       s.codes = R * C;
       s.scales = role == PQL_ACTIVATION ? 4 * R * (C / 128) : 4 * (R / 128) * (C / 128);
@@ -136,6 +140,7 @@ hipError_t do_quantize(int scheme, int role, const void* x, int64_t rows, int64_
       return pql::launch_quant_fp8_tensor(xb, rows, cols, ldx, cb, static_cast<float*>(scales),
                                           static_cast<float*>(ws), st);
     case PQL_FP8_ROW: return pql::launch_quant_fp8_row(xb, rows, cols, ldx, cb, static_cast<float*>(scales), st);
+    case PQL_INT8_ROW: return pql::launch_quant_int8_row(xb, rows, cols, ldx, cb, static_cast<float*>(scales), st);
     case PQL_FP8_BLOCK128:
       return role == PQL_ACTIVATION
                  ? pql::launch_quant_fp8_block_act(xb, rows, cols, ldx, cb, static_cast<float*>(scales), st)
@@ -149,9 +154,18 @@ hipError_t do_quantize(int scheme, int role, const void* x, int64_t rows, int64_
   }
 }
 
+pql::GemmKind gemm_kind(int scheme) {
+  return scheme == PQL_FP8_BLOCK128 ? pql::GEMM_FP8_BLOCK
+         : scheme == PQL_MXFP8      ? pql::GEMM_MXFP8
+         : scheme == PQL_MXFP4      ? pql::GEMM_MXFP4
+         : scheme == PQL_INT8_ROW   ? pql::GEMM_INT8_ROW
+                                    : pql::GEMM_FP8_ROWSCALE;
+}
+
 hipError_t do_qgemm(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
-                    const void* w_zeros, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, hipStream_t st) {
-  if (is_w4a16(scheme))
+                    const void* w_zeros, int64_t M, int64_t N, int64_t K, float alpha, const void* bias, void* c,
+                    int64_t ldc, hipStream_t st) {
+  if (is_w4a16(scheme))   // alpha = 1 and no bias here (checked by the callers)
     return pql::launch_gemm_w4a16(static_cast<const uint16_t*>(a), static_cast<const uint32_t*>(w_codes),
                                   static_cast<const uint16_t*>(w_scales), static_cast<const uint8_t*>(w_zeros), M, N,
                                   K, static_cast<uint16_t*>(c), ldc, st);
@@ -168,11 +182,9 @@ hipError_t do_qgemm(int scheme, const void* a, const void* a_scales, const void*
   g.c = static_cast<uint16_t*>(c);
   g.ldc = ldc;
   g.vec_store = aligned16(c) && ldc % 8 == 0;
-  pql::GemmKind kind = scheme == PQL_FP8_BLOCK128 ? pql::GEMM_FP8_BLOCK
-                       : scheme == PQL_MXFP8      ? pql::GEMM_MXFP8
-                       : scheme == PQL_MXFP4      ? pql::GEMM_MXFP4
-                                                  : pql::GEMM_FP8_ROWSCALE;
-  return pql::launch_gemm(kind, g, st);
+  g.alpha = alpha;
+  g.bias = static_cast<const uint16_t*>(bias);
+  return pql::launch_gemm(gemm_kind(scheme), g, st);
 }
 
 pql_status check_gemm_shape(int scheme, int64_t M, int64_t N, int64_t K) {
@@ -219,7 +231,7 @@ pql_status pql_workspace_size(int op, int scheme, int role, int64_t M, int64_t N
     return ok();
   }
   if (op == PQL_OP_QLINEAR) {
-    if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
+    if (!valid_scheme(scheme)) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
     pql_status st = check_gemm_shape(scheme, M, N, K);
     if (st != PQL_OK) return st;
     if (is_w4a16(scheme)) return ok();
@@ -274,6 +286,7 @@ pql_status pql_dequantize(int scheme, int role, const void* codes, const void* s
     case PQL_FP8_BLOCK128: kind = role == PQL_ACTIVATION ? 2 : 3; break;
     case PQL_MXFP8: kind = 4; break;
     case PQL_MXFP4: kind = 5; break;
+    case PQL_INT8_ROW: kind = 7; break;
     default: kind = 6; break;
   }
   return launched(pql::launch_dequant(kind, codes, scales, static_cast<const uint8_t*>(zeros), rows, cols,
@@ -281,11 +294,59 @@ pql_status pql_dequantize(int scheme, int role, const void* codes, const void* s
                   "dequantize launch");
 }
 
-pql_status pql_qgemm(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
-                     const void* w_zeros, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, void* stream) {
-  if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
+}  // extern "C"
+
+namespace {
+
+// Checks of the fused epilogue (alpha, bias) shared by qgemm_ex and qlinear_ex.
+pql_status check_epilogue(int scheme, int64_t N, float alpha, const void* bias) {
+  if (!(alpha == alpha) || alpha - alpha != 0.0f) return fail(PQL_ERR_INVALID_ARGUMENT, "alpha must be finite");
+  if ((alpha != 1.0f || bias) && !has_epilogue(scheme))
+    return fail(PQL_ERR_UNSUPPORTED, "%s has no fused alpha / bias epilogue (FP8 and INT8_ROW only)",
+                scheme_name(scheme));
+  if (bias && !aligned16(bias)) return fail(PQL_ERR_INVALID_ARGUMENT, "bias must be 16-byte aligned");
+  if (bias && N % 2) return fail(PQL_ERR_INVALID_ARGUMENT, "a bias needs an even N (got %lld)", (long long)N);
+  return PQL_OK;
+}
+
+size_t qlinear_ws_bytes(int scheme, int64_t M, int64_t K) {
+  const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
+  return round256(s.codes) + round256(s.scales) + (scheme == PQL_FP8_TENSOR ? kTensorWs : 0);
+}
+
+}  // namespace
+
+extern "C" {
+
+pql_status pql_quantize_static(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                               const void* scales, void* codes, void* stream) {
+  pql_status st = check_scheme_role(scheme, role);
+  if (st != PQL_OK) return st;
+  if (scheme != PQL_FP8_TENSOR && scheme != PQL_FP8_BLOCK128)
+    return fail(PQL_ERR_UNSUPPORTED, "static scales are defined for FP8_TENSOR and FP8_BLOCK128 only (got %s)",
+                scheme_name(scheme));
+  if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
+  if (ldx < cols || ldx % 8) return fail(PQL_ERR_INVALID_ARGUMENT, "ldx must be >= cols and a multiple of 8 (got %lld)",
+                                         (long long)ldx);
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(PQL_ERR_INVALID_ARGUMENT, "x, scales and codes must be non-NULL");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "x, scales and codes must be 16-byte aligned");
+  if ((st = check_device()) != PQL_OK) return st;
+  const int mode = scheme == PQL_FP8_TENSOR ? 0 : role == PQL_ACTIVATION ? 1 : 2;
+  return launched(pql::launch_quant_fp8_static(mode, static_cast<const uint16_t*>(x), rows, cols, ldx,
+                                               static_cast<const float*>(scales), static_cast<uint8_t*>(codes),
+                                               static_cast<hipStream_t>(stream)),
+                  "static quantize launch");
+}
+
+pql_status pql_qgemm_ex(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
+                        const void* w_zeros, int64_t M, int64_t N, int64_t K, float alpha, const void* bias,
+                        void* c, int64_t ldc, void* stream) {
+  if (!valid_scheme(scheme)) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
   pql_status st = check_gemm_shape(scheme, M, N, K);
   if (st != PQL_OK) return st;
+  if ((st = check_epilogue(scheme, N, alpha, bias)) != PQL_OK) return st;
   if (ldc < N) return fail(PQL_ERR_INVALID_ARGUMENT, "ldc must be >= N (got %lld)", (long long)ldc);
   if (M == 0) return ok();
   if (!a || !w_codes || !w_scales || !c) return fail(PQL_ERR_INVALID_ARGUMENT, "a, w_codes, w_scales and c must be non-NULL");
@@ -294,29 +355,37 @@ pql_status pql_qgemm(int scheme, const void* a, const void* a_scales, const void
   if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || (a_scales && !aligned16(a_scales)))
     return fail(PQL_ERR_INVALID_ARGUMENT, "operands and scales must be 16-byte aligned");
   if ((st = check_device()) != PQL_OK) return st;
-  return launched(do_qgemm(scheme, a, a_scales, w_codes, w_scales, w_zeros, M, N, K, c, ldc,
+  return launched(do_qgemm(scheme, a, a_scales, w_codes, w_scales, w_zeros, M, N, K, alpha, bias, c, ldc,
                            static_cast<hipStream_t>(stream)),
                   "qgemm launch");
 }
 
-pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* w_codes,
-                       const void* w_scales, const void* w_zeros, int64_t N, void* c, int64_t ldc, void* workspace,
-                       size_t workspace_bytes, void* stream) {
-  if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
+pql_status pql_qgemm(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
+                     const void* w_zeros, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, void* stream) {
+  return pql_qgemm_ex(scheme, a, a_scales, w_codes, w_scales, w_zeros, M, N, K, 1.0f, nullptr, c, ldc, stream);
+}
+
+pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
+                          const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
+                          const void* bias, void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (!valid_scheme(scheme)) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
   pql_status st = check_gemm_shape(scheme, M, N, K);
   if (st != PQL_OK) return st;
+  if ((st = check_epilogue(scheme, N, alpha, bias)) != PQL_OK) return st;
+  if (a_static_scales && scheme != PQL_FP8_TENSOR && scheme != PQL_FP8_BLOCK128)
+    return fail(PQL_ERR_UNSUPPORTED, "static activation scales are defined for FP8_TENSOR and FP8_BLOCK128 only (got %s)",
+                scheme_name(scheme));
   if (ldc < N) return fail(PQL_ERR_INVALID_ARGUMENT, "ldc must be >= N (got %lld)", (long long)ldc);
   if (is_w4a16(scheme) ? lda != K : (lda < K || lda % 8))
     return fail(PQL_ERR_INVALID_ARGUMENT, is_w4a16(scheme) ? "W4A16 needs lda == K" : "lda must be >= K and a multiple of 8");
   if (M == 0) return ok();
   if (!a || !w_codes || !w_scales || !c) return fail(PQL_ERR_INVALID_ARGUMENT, "a, w_codes, w_scales and c must be non-NULL");
   if (is_w4a16(scheme) && !w_zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "w_zeros must be non-NULL for W4A16");
-  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales))
+  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || (a_static_scales && !aligned16(a_static_scales)))
     return fail(PQL_ERR_INVALID_ARGUMENT, "operands and scales must be 16-byte aligned");
-  size_t need = 0;
   if (!is_w4a16(scheme)) {
-    const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
-    need = round256(s.codes) + round256(s.scales) + (scheme == PQL_FP8_TENSOR ? kTensorWs : 0);
+    const size_t need = qlinear_ws_bytes(scheme, M, K);
     if (!workspace || workspace_bytes < need)
       return fail(PQL_ERR_WORKSPACE, "qlinear needs a %zu-byte workspace (got %zu)", need,
                   workspace ? workspace_bytes : (size_t)0);
@@ -325,26 +394,42 @@ pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t 
   if ((st = check_device()) != PQL_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (is_w4a16(scheme))
-    return launched(do_qgemm(scheme, a, nullptr, w_codes, w_scales, w_zeros, M, N, K, c, ldc, hs), "qlinear launch");
+    return launched(do_qgemm(scheme, a, nullptr, w_codes, w_scales, w_zeros, M, N, K, 1.0f, nullptr, c, ldc, hs),
+                    "qlinear launch");
   const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   void* a_codes = ws;
   void* a_scales = ws + round256(s.codes);
   void* partials = ws + round256(s.codes) + round256(s.scales);
-  hipError_t e = do_quantize(scheme, PQL_ACTIVATION, a, M, K, lda, a_codes, a_scales, nullptr, partials, hs);
+  hipError_t e;
+  if (a_static_scales) {
+    a_scales = const_cast<void*>(a_static_scales);
+    e = pql::launch_quant_fp8_static(scheme == PQL_FP8_TENSOR ? 0 : 1, static_cast<const uint16_t*>(a), M, K, lda,
+                                     static_cast<const float*>(a_static_scales), static_cast<uint8_t*>(a_codes), hs);
+  } else {
+    e = do_quantize(scheme, PQL_ACTIVATION, a, M, K, lda, a_codes, a_scales, nullptr, partials, hs);
+  }
   if (e != hipSuccess) return launched(e, "qlinear activation quantize");
-  return launched(do_qgemm(scheme, a_codes, a_scales, w_codes, w_scales, w_zeros, M, N, K, c, ldc, hs),
+  return launched(do_qgemm(scheme, a_codes, a_scales, w_codes, w_scales, w_zeros, M, N, K, alpha, bias, c, ldc, hs),
                   "qlinear gemm");
 }
 
+pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* w_codes,
+                       const void* w_scales, const void* w_zeros, int64_t N, void* c, int64_t ldc, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return pql_qlinear_ex(scheme, a, M, K, lda, nullptr, w_codes, w_scales, w_zeros, N, 1.0f, nullptr, c, ldc,
+                        workspace, workspace_bytes, stream);
+}
+
 const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, int64_t K) {
-  if (scheme < PQL_FP8_TENSOR || scheme > PQL_W4A16_SYM) return "";
+  if (!valid_scheme(scheme)) return "";
   switch (op) {
     case PQL_OP_QUANTIZE:
       if (is_w4a16(scheme) && role == PQL_ACTIVATION) return "";
       switch (scheme) {
         case PQL_FP8_TENSOR: return "k_amax_partial+k_fp8_tensor";
         case PQL_FP8_ROW: return "k_fp8_row";
+        case PQL_INT8_ROW: return "k_fp8_row<int8>";
         case PQL_FP8_BLOCK128: return role == PQL_ACTIVATION ? "k_fp8_block_act" : "k_fp8_block_wt";
         case PQL_MXFP8: return "k_mx<e4m3>";
         case PQL_MXFP4: return "k_mx<e2m1>";
@@ -354,11 +439,7 @@ const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, 
     case PQL_OP_QGEMM:
     case PQL_OP_QLINEAR:
       if (is_w4a16(scheme)) return pql::gemm_w4a16_kernel_name(M, N, K);
-      return pql::gemm_kernel_name(scheme == PQL_FP8_BLOCK128 ? pql::GEMM_FP8_BLOCK
-                                   : scheme == PQL_MXFP8      ? pql::GEMM_MXFP8
-                                   : scheme == PQL_MXFP4      ? pql::GEMM_MXFP4
-                                                              : pql::GEMM_FP8_ROWSCALE,
-                                   M, N, K);
+      return pql::gemm_kernel_name(gemm_kind(scheme), M, N, K);
   }
   return "";
 }

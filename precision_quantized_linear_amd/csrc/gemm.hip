@@ -300,6 +300,7 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st) {
     case GEMM_FP8_BLOCK: return launch_gemm_block(g, st);
     case GEMM_MXFP8: return launch_gemm32_mx(false, g, st);
     case GEMM_MXFP4: return g.K % 256 == 0 ? launch_gemm32_mx(true, g, st) : launch_kind<GEMM_MXFP4>(g, st);
+    case GEMM_INT8_ROW: return launch_gemm32_int8(g, st);
   }
   return hipErrorInvalidValue;
 }
@@ -310,6 +311,7 @@ const char* gemm_kernel_name(GemmKind kind, int64_t, int64_t, int64_t K) {
     case GEMM_FP8_BLOCK: return "k_gemm_block";
     case GEMM_MXFP8: return "k_gemm32<mxfp8>";
     case GEMM_MXFP4: return K % 256 == 0 ? "k_gemm32<mxfp4>" : "k_gemm<mxfp4>_256x256x256";
+    case GEMM_INT8_ROW: return "k_gemm32<int8>";
   }
   return "";
 }

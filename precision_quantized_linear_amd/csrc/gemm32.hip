@@ -1,9 +1,14 @@
 // Persistent FP8 GEMM for the per-tensor / per-row scale schemes, gfx950.
 //
-// C[M, N] = s_a[m] * s_w[n] * sum_k e4m3(a[m, k]) * e4m3(w[n, k]), bf16 out
-// ("[vLLM] Other quantization: FP8, ModelOpt, INC, TorchAO, Quark", section
-// "FP8": tensor- and token-wise dynamic scales; the weight's per-output-channel
-// scale is the token-wise rule applied to W's rows).
+// C[M, N] = alpha * s_a[m] * s_w[n] * sum_k e4m3(a[m, k]) * e4m3(w[n, k]) + bias[n],
+// bf16 out ("[vLLM] Other quantization: FP8, ModelOpt, INC, TorchAO, Quark",
+// section "FP8": tensor- and token-wise scales; the weight's per-output-channel
+// scale is the token-wise rule applied to W's rows; the fused epilogue
+// alpha * (A @ B) + bias from "vLLM-Omni Online Quantization complete guide",
+// section "How online quantization works underneath").  The same kernel runs
+// MXFP8 / MXFP4 (scaled MFMA, no epilogue scales) and int8 with per-row
+// scales (the guide's int8 online path): v_mfma_i32_32x32x32_i8 twice per
+// 64-byte K slice, int32 sums converted to fp32 in the epilogue.
 //
 // Matrix core: v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales.  Lane l
 // feeds row (l % 32) of its operand; with g = l / 32 its 32 operand bytes are
@@ -58,16 +63,18 @@ constexpr int kSlice = 64;                       // K bytes per MFMA slice
 constexpr int kRow = 128;                        // K bytes per LDS row: one pair of slices
 constexpr int kOpBytes = BM * kRow;              // one operand's rows in a region (32 KB)
 constexpr int kRegionBytes = 2 * kOpBytes;       // A then W
-constexpr int kScaleBytes = 1024;                // per wave: 128 row scales, then 128 column scales
+constexpr int kScaleBytes = 1280;                // per wave: 128 row scales, 128 column scales, 128 bf16 biases
 constexpr int kPersistentCap = 256;              // one workgroup per CU
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 
 
 template <int KIND>
 struct Kind {
   static constexpr bool kMx = KIND == GEMM_MXFP8 || KIND == GEMM_MXFP4;
   static constexpr bool kFp4 = KIND == GEMM_MXFP4;
+  static constexpr bool kInt8 = KIND == GEMM_INT8_ROW;
   static constexpr int kSpr = kFp4 ? 4 : 2;                // MFMA slices per 128-byte row of a region
   static constexpr int kLogSpr = kFp4 ? 2 : 1;
   static constexpr int kQ = kFp4 ? 1 : 2;                  // 16-byte fragment reads per block and slice
@@ -75,7 +82,7 @@ struct Kind {
   static constexpr int kSB = kFp4 ? 8 : 4;                 // e8m0 bytes per row and region
   static constexpr int kMxRegionBytes = kMx ? 2 * BM * kSB : 0;
   static constexpr int kWaveBytes = kMx ? 0 : kScaleBytes;
-  static constexpr int kScLoads = kMx ? 0 : 4;              // FP8 scale loads per wave and tile
+  static constexpr int kScLoads = kMx ? 0 : 5;              // scale and bias loads per wave and tile
   static constexpr int kLdsBytes = 2 * kRegionBytes + 2 * kMxRegionBytes + 4 * kWaveBytes;
 };
 
@@ -267,7 +274,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v16f c = first ? v16f{} : acc[i][j];   // compile-time choice
-        if constexpr (T::kMx)
+        if constexpr (T::kInt8) {
+          // K-elements 0-31 of the slice from chunk g of every lane, 32-63 from
+          // chunk 2 + g: both operands use the same assignment, so each K-element
+          // meets its partner whatever order the MFMA sums in.
+          v16i ci = __builtin_bit_cast(v16i, c);
+          ci = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, fw[j][0]), __builtin_bit_cast(v4i, fa[i][0]),
+                                                    ci, 0, 0, 0);
+          ci = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, fw[j][1]), __builtin_bit_cast(v4i, fa[i][1]),
+                                                    ci, 0, 0, 0);
+          acc[i][j] = __builtin_bit_cast(v16f, ci);
+        } else if constexpr (T::kMx)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(operand(fw[j]), operand(fa[i]), c, T::kFmt,
                                                                       T::kFmt, opsel, ecw[j][d], opsel, eca[i][d]);
         else
@@ -321,10 +338,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- FP8 row / column scales.  Each wave keeps its 128 row and 128 column
-  // scales in its own 1 KB of LDS, fetched by direct-to-LDS loads right after
-  // the previous tile's epilogue; the next barrier's wait retires them.
-  // Per-tensor scales have stride 0: every lane then reads the one scale.
+  // ---- FP8 / int8 row and column scales and the bias.  Each wave keeps its 128
+  // row and 128 column scales and 128 bf16 biases in its own 1.25 KB of LDS,
+  // fetched by direct-to-LDS loads right after the previous tile's epilogue;
+  // the next barrier's wait retires them.  Per-tensor scales have stride 0:
+  // every lane then reads the one scale.  Without a bias the descriptor is
+  // empty and the loads write zeros.
   uint8_t* wave_lds = smem + 2 * kRegionBytes + 2 * T::kMxRegionBytes + wave * T::kWaveBytes;
   const float* sc_rows = reinterpret_cast<const float*>(wave_lds);
   const float* sc_cols = sc_rows + 128;
@@ -345,12 +364,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
       lds_load4(ra, scr + 256, va + (int)g.a_scale_stride * 256);
       lds_load4(rw, scr + 512, vw);
       lds_load4(rw, scr + 768, vw + (int)g.w_scale_stride * 256);
+      const int64_t nb = std::max<int64_t>(0, std::min<int64_t>(128, g.N - n0));
+      lds_load4(make_rsrc(g.bias ? g.bias + n0 : nullptr, g.bias ? (int)(nb * 2) : 0), scr + 1024, lane * 4);
     }
   };
-  // Value of accumulator element (i, j, r) as written to C.
-  auto out_val = [&](float a, float rs, float cs) __attribute__((always_inline)) {
+  const uint16_t* bias_cols = reinterpret_cast<const uint16_t*>(wave_lds + 1024);
+  // Value of accumulator element (i, j, r) as written to C: rs carries alpha
+  // (alpha * s_a[m]), cs is s_w[n], b the bias; int8 sums are converted first.
+  auto out_val = [&](float a, float rs, float cs, float b) __attribute__((always_inline)) {
     if constexpr (T::kMx) return a;
-    else return a * rs * cs;
+    else if constexpr (T::kInt8) return __builtin_fmaf((float)__builtin_bit_cast(int, a) * rs, cs, b);
+    else return __builtin_fmaf(a * rs, cs, b);
   };
 
   // ---- epilogue of tile k: each lane owns output row m = 32 i + l % 32 of block
@@ -378,19 +402,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
     const int64_t lane_off = (int64_t)fr * g.ldc + 8 * fk;   // elements from the block's first row and column
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float rs = T::kMx ? 1.0f : sc_rows[i * 32 + fr];
+      const float rs = T::kMx ? 1.0f : sc_rows[i * 32 + fr] * g.alpha;
       uint16_t* blk = g.c + (m0 + i * 32) * g.ldc + n0;   // wave-uniform
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float4 cs[4];
+        float4 cs[4], bs[4];
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) cs[rq] = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : cs4[j * 8 + rq * 2 + fk];
+        for (int rq = 0; rq < 4; ++rq) {
+          if constexpr (T::kMx) {
+            cs[rq] = float4{1.f, 1.f, 1.f, 1.f};
+            bs[rq] = float4{0.f, 0.f, 0.f, 0.f};
+          } else {
+            cs[rq] = cs4[j * 8 + rq * 2 + fk];
+            const uint2 bw = *reinterpret_cast<const uint2*>(bias_cols + j * 32 + rq * 8 + fk * 4);
+            bs[rq] = float4{__uint_as_float(bw.x << 16), __uint_as_float(bw.x & 0xFFFF0000u),
+                            __uint_as_float(bw.y << 16), __uint_as_float(bw.y & 0xFFFF0000u)};
+          }
+        }
         const v16f a = acc[i][j];
         uint32_t d[4][2];
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          d[rq][0] = pack_bf16x2(out_val(a[4 * rq + 0], rs, cs[rq].x), out_val(a[4 * rq + 1], rs, cs[rq].y));
-          d[rq][1] = pack_bf16x2(out_val(a[4 * rq + 2], rs, cs[rq].z), out_val(a[4 * rq + 3], rs, cs[rq].w));
+          d[rq][0] = pack_bf16x2(out_val(a[4 * rq + 0], rs, cs[rq].x, bs[rq].x),
+                                 out_val(a[4 * rq + 1], rs, cs[rq].y, bs[rq].y));
+          d[rq][1] = pack_bf16x2(out_val(a[4 * rq + 2], rs, cs[rq].z, bs[rq].z),
+                                 out_val(a[4 * rq + 3], rs, cs[rq].w, bs[rq].w));
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -524,6 +560,7 @@ hipError_t launch_kind32(const GemmArgs& g, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_gemm32_fp8(const GemmArgs& g, hipStream_t st) { return launch_kind32<GEMM_FP8_ROWSCALE>(g, st); }
+hipError_t launch_gemm32_int8(const GemmArgs& g, hipStream_t st) { return launch_kind32<GEMM_INT8_ROW>(g, st); }
 hipError_t launch_gemm32_mx(bool fp4, const GemmArgs& g, hipStream_t st) {
   return fp4 ? launch_kind32<GEMM_MXFP4>(g, st) : launch_kind32<GEMM_MXFP8>(g, st);
 }

@@ -3,7 +3,10 @@
 // C[m, n] = bf16( sum_g s_a[m, g] * s_w[n / 128, g] * sum_{k in group g} qa[m, k] qw[n, k] )
 // ("[vLLM] Other quantization: FP8, ModelOpt, INC, TorchAO, Quark", section
 // "FP8": activations with one scale per 1x128 K-group, weights with one scale
-// per 128x128 block).
+// per 128x128 block), optionally as alpha * (...) + bias[n] (the fused
+// epilogue of "vLLM-Omni Online Quantization complete guide", section "How
+// online quantization works underneath"), applied to the fp32 sums before
+// the one rounding to bf16.
 //
 // A 128-wide K-group is exactly one v_mfma_scale_f32_16x16x128_f8f6f4 (unit
 // MFMA scales), so every group's partial product P comes out of the matrix
@@ -209,6 +212,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
     int tm, tn;
     sched.coords(k, tm, tn);
     const int64_t m0 = (int64_t)tm * BM + wm * 128, n0 = (int64_t)tn * BN + wn * 64;
+    if (g.alpha != 1.0f || g.bias) {   // wave-uniform; N % 128 == 0, so every column exists
+      float b[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint2 bw = uint2{0u, 0u};
+        if (g.bias) bw = *reinterpret_cast<const uint2*>(g.bias + n0 + j * 16 + g4 * 4);
+        b[j][0] = __uint_as_float(bw.x << 16);
+        b[j][1] = __uint_as_float(bw.x & 0xFFFF0000u);
+        b[j][2] = __uint_as_float(bw.y << 16);
+        b[j][3] = __uint_as_float(bw.y & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(acc[i][j][e], g.alpha, b[j][e]);
+    }
     const bool interior = g.vec_store && m0 + 128 <= g.M && n0 + 64 <= g.N;   // wave-uniform
     if (interior) {
       const int rr = lane >> 3, rc = lane & 7;

@@ -27,6 +27,11 @@ hipError_t launch_quant_fp8_tensor(const uint16_t* x, int64_t rows, int64_t cols
                                    uint8_t* codes, float* scale, float* ws_partials, hipStream_t st);
 hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                 uint8_t* codes, float* scales, hipStream_t st);
+hipError_t launch_quant_int8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* codes, float* scales, hipStream_t st);
+// Static (supplied) FP8 scales: mode 0 per tensor, 1 per (row, 128-group), 2 per 128x128 block.
+hipError_t launch_quant_fp8_static(int mode, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   const float* scales, uint8_t* codes, hipStream_t st);
 hipError_t launch_quant_fp8_block_act(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                                       uint8_t* codes, float* scales, hipStream_t st);
 hipError_t launch_quant_fp8_block_wt(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
@@ -38,12 +43,12 @@ hipError_t launch_quant_int4(bool sym, const uint16_t* x, int64_t rows, int64_t 
 
 // ---------------------------------------------------------------- dequantize
 // kind: 0 fp8 tensor, 1 fp8 row, 2 fp8 block act, 3 fp8 block weight, 4 mxfp8,
-//       5 mxfp4, 6 int4
+//       5 mxfp4, 6 int4, 7 int8 row
 hipError_t launch_dequant(int kind, const void* codes, const void* scales, const uint8_t* zeros,
                           int64_t rows, int64_t cols, uint16_t* y, int64_t ldy, hipStream_t st);
 
 // ---------------------------------------------------------------- GEMM
-enum GemmKind { GEMM_FP8_ROWSCALE = 0, GEMM_FP8_BLOCK = 1, GEMM_MXFP8 = 2, GEMM_MXFP4 = 3 };
+enum GemmKind { GEMM_FP8_ROWSCALE = 0, GEMM_FP8_BLOCK = 1, GEMM_MXFP8 = 2, GEMM_MXFP4 = 3, GEMM_INT8_ROW = 4 };
 
 struct GemmArgs {
   const uint8_t* a;        // A codes [M, K] (fp4: [M, K/2])
@@ -56,6 +61,8 @@ struct GemmArgs {
   uint16_t* c;             // bf16 [M, ldc]
   int64_t ldc;
   int vec_store;           // 1 if c and ldc allow 16-byte row stores
+  float alpha;             // epilogue: C = alpha * (A_hat W_hat^T) + bias (FP8 and int8 kinds)
+  const uint16_t* bias;    // bf16 [N], or null for none
 };
 
 hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st);
@@ -63,6 +70,8 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st);
 // (MXFP4 needs K % 256 == 0, MXFP8 K % 128 == 0).
 hipError_t launch_gemm32_fp8(const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm32_mx(bool fp4, const GemmArgs& g, hipStream_t st);
+// Same kernel with the int8 matrix cores (int32 sums), per-row scales.
+hipError_t launch_gemm32_int8(const GemmArgs& g, hipStream_t st);
 // Persistent FP8 block-128 kernel (16x16x128 MFMA per K-group, FMA promotion; N % 128 == 0).
 hipError_t launch_gemm_block(const GemmArgs& g, hipStream_t st);
 const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);

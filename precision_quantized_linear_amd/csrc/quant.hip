@@ -13,7 +13,10 @@
 // "vLLM-Omni Online Quantization complete guide", section "How online
 // quantization works underneath", steps 2-3 (MX: e8m0 per 32 K-elements);
 // "vLLM-Omni accelerates inference with AutoRound quantization", section
-// "Usage" (int4, group 128, round-to-nearest).
+// "Usage" (int4, group 128, round-to-nearest).  Static FP8 scales (supplied per
+// tensor or per 128-block) from the FP8 section's scheme keys; int8 per-row
+// dynamic scales from the online-quantization guide's int8 path (sections "Key
+// parameters in detail" and "How online quantization works underneath").
 #include "pql_device.hpp"
 #include "pql_internal.hpp"
 
@@ -81,6 +84,43 @@ __device__ __forceinline__ uint2 fp8_chunk(uint4 c, float s, float rcp) {
   return make_uint2(fp8x4(f[0], f[1], f[2], f[3]), fp8x4(f[4], f[5], f[6], f[7]));
 }
 
+// Static scales: the quotient can exceed 448 (a calibrated scale may be below
+// amax / 448) and even overflow fp32 (then the corrected quotient is inf or
+// NaN), so every quotient outside [-448, 448] becomes 448 with the sign of x
+// before the convert, which is exact inside; zeros keep their sign.
+template <bool FAST>
+__device__ __forceinline__ uint2 fp8_chunk_sat(uint4 c, float s, float rcp) {
+  float f[8];
+  chunk_to_f32(c, f);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float q = quot<FAST>(f[j], s, rcp);
+    f[j] = __builtin_fabsf(q) <= 448.0f ? q : __builtin_copysignf(448.0f, f[j]);
+  }
+  return make_uint2(fp8x4(f[0], f[1], f[2], f[3]), fp8x4(f[4], f[5], f[6], f[7]));
+}
+
+// int8 scale: s = fp32(amax / 127), 1 if that is 0.
+__device__ __forceinline__ float int8_scale(float amax) {
+  float s = __fdiv_rn(amax, 127.0f);
+  return s == 0.0f ? 1.0f : s;
+}
+
+// 8 bf16 -> 8 int8 codes clamp(rne(fp32(x / s)), -128, 127), byte j = element j.
+template <bool FAST>
+__device__ __forceinline__ uint2 int8_chunk(uint4 c, float s, float rcp) {
+  float f[8];
+  chunk_to_f32(c, f);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float r = __builtin_rintf(quot<FAST>(f[j], s, rcp));   // round half to even
+    const int q = (int)__builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
+    w[j >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (j & 3));
+  }
+  return make_uint2(w[0], w[1]);
+}
+
 // ---------------------------------------------------------------- per tensor
 // Pass 1: partial[b] = max |x| over the row segments workgroup b visits.
 __global__ __launch_bounds__(256) void k_amax_partial(const uint16_t* __restrict__ x, int64_t rows,
@@ -137,21 +177,27 @@ __global__ __launch_bounds__(256) void k_fp8_tensor(const uint16_t* __restrict__
 // ---------------------------------------------------------------- per row
 // One wave per row.  CH > 0: the row (at most 64*CH chunks) stays in
 // registers between the max and the cast.  CH == 0: rows too long for that
-// are read twice.
-template <int CH, bool FAST>
+// are read twice.  INT8: the int8 scheme (s = amax / 127, integer codes)
+// instead of FP8.
+template <bool INT8, bool FAST>
+__device__ __forceinline__ uint2 row_chunk(uint4 c, float s, float rcp) {
+  if constexpr (INT8) return int8_chunk<FAST>(c, s, rcp);
+  else return fp8_chunk<FAST>(c, s, rcp);
+}
+template <int CH, bool INT8, bool FAST>
 __device__ __forceinline__ void fp8_row_cast(const uint4 (&c)[CH > 0 ? CH : 1], const uint16_t* xr, uint8_t* cr,
                                              int nch, int lane, float s, float rcp) {
   if constexpr (CH > 0) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int ch = i * 64 + lane;
-      if (ch < nch) stg8(cr + ch * 8, fp8_chunk<FAST>(c[i], s, rcp));
+      if (ch < nch) stg8(cr + ch * 8, row_chunk<INT8, FAST>(c[i], s, rcp));
     }
   } else {
-    for (int ch = lane; ch < nch; ch += 64) stg8(cr + ch * 8, fp8_chunk<FAST>(ldg16(xr + ch * 8), s, rcp));
+    for (int ch = lane; ch < nch; ch += 64) stg8(cr + ch * 8, row_chunk<INT8, FAST>(ldg16(xr + ch * 8), s, rcp));
   }
 }
-template <int CH>
+template <int CH, bool INT8>
 __global__ __launch_bounds__(256) void k_fp8_row(const uint16_t* __restrict__ x, int64_t rows,
                                                  int64_t cols, int64_t ldx,
                                                  uint8_t* __restrict__ codes,
@@ -174,10 +220,38 @@ __global__ __launch_bounds__(256) void k_fp8_row(const uint16_t* __restrict__ x,
   } else {
     for (int ch = lane; ch < nch; ch += 64) m = fmaxf(m, chunk_absmax(ldg16(xr + ch * 8)));
   }
-  const float s = fp8_scale(wave_max(m));
+  const float amax = wave_max(m);
+  const float s = INT8 ? int8_scale(amax) : fp8_scale(amax);
   if (lane == 0) scales[row] = s;
-  if (s >= kSmallestFastScale) fp8_row_cast<CH, true>(c, xr, cr, nch, lane, s, __fdiv_rn(1.0f, s));
-  else fp8_row_cast<CH, false>(c, xr, cr, nch, lane, s, 0.0f);
+  if (s >= kSmallestFastScale) fp8_row_cast<CH, INT8, true>(c, xr, cr, nch, lane, s, __fdiv_rn(1.0f, s));
+  else fp8_row_cast<CH, INT8, false>(c, xr, cr, nch, lane, s, 0.0f);
+}
+
+// ---------------------------------------------------------------- static FP8 scales
+// Row segments; every chunk looks its scale up: MODE 0 one scale per tensor,
+// 1 one per (row, 128-group) (activations), 2 one per 128x128 block (weights).
+template <int MODE>
+__global__ __launch_bounds__(256) void k_fp8_static(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                    int64_t ldx, const float* __restrict__ scales,
+                                                    uint8_t* __restrict__ codes) {
+  const Seg g;
+  if (g.row >= rows) return;
+  const int64_t cpr = cols >> 3, gpr = cols >> 7;
+  const uint16_t* xr = x + g.row * ldx;
+  uint8_t* cr = codes + g.row * cols;
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u;
+    if (c >= cpr) continue;
+    const float s = MODE == 0 ? scales[0]
+                    : MODE == 1 ? scales[g.row * gpr + (c >> 4)]
+                                : scales[(g.row >> 7) * gpr + (c >> 4)];
+    const uint4 v = ldg16(xr + c * 8);
+    uint2 q;
+    if (s >= kSmallestFastScale) q = fp8_chunk_sat<true>(v, s, __fdiv_rn(1.0f, s));
+    else q = fp8_chunk_sat<false>(v, s, 0.0f);
+    stg8(cr + c * 8, q);
+  }
 }
 
 // ---------------------------------------------------------------- 1x128 groups
@@ -423,6 +497,11 @@ __global__ __launch_bounds__(256) void k_dequant(int kind, const uint8_t* __rest
 #pragma unroll
         for (int j = 0; j < 4; ++j) v[4 + j] = e4m3_decode((w.y >> (8 * j)) & 0xFF) * sc;
       }
+    } else if (kind == 7) {
+      const uint2 w = *reinterpret_cast<const uint2*>(codes + r * cols + c * 8);
+      const float sc = static_cast<const float*>(scales)[r];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = (float)(int8_t)(((j < 4 ? w.x : w.y) >> (8 * (j & 3))) & 0xFF) * sc;
     } else {
       const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[r * cpr + c];
       const int64_t gi = (c >> 4) * rows + r;   // group-major
@@ -449,17 +528,37 @@ hipError_t launch_quant_fp8_tensor(const uint16_t* x, int64_t rows, int64_t cols
   return hipGetLastError();
 }
 
-hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
-                                uint8_t* codes, float* scales, hipStream_t st) {
+template <bool INT8>
+hipError_t launch_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes, float* scales,
+                      hipStream_t st) {
   const int64_t nch = cols >> 3;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-  if (nch <= 64) hipLaunchKernelGGL(k_fp8_row<1>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
-  else if (nch <= 128) hipLaunchKernelGGL(k_fp8_row<2>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
-  else if (nch <= 256) hipLaunchKernelGGL(k_fp8_row<4>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
-  else if (nch <= 384) hipLaunchKernelGGL(k_fp8_row<6>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
-  else if (nch <= 512) hipLaunchKernelGGL(k_fp8_row<8>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
-  else if (nch <= 1024) hipLaunchKernelGGL(k_fp8_row<16>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
-  else hipLaunchKernelGGL(k_fp8_row<0>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  if (nch <= 64) hipLaunchKernelGGL((k_fp8_row<1, INT8>), grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  else if (nch <= 128) hipLaunchKernelGGL((k_fp8_row<2, INT8>), grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  else if (nch <= 256) hipLaunchKernelGGL((k_fp8_row<4, INT8>), grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  else if (nch <= 384) hipLaunchKernelGGL((k_fp8_row<6, INT8>), grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  else if (nch <= 512) hipLaunchKernelGGL((k_fp8_row<8, INT8>), grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  else if (nch <= 1024) hipLaunchKernelGGL((k_fp8_row<16, INT8>), grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  else hipLaunchKernelGGL((k_fp8_row<0, INT8>), grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* codes, float* scales, hipStream_t st) {
+  return launch_row<false>(x, rows, cols, ldx, codes, scales, st);
+}
+
+hipError_t launch_quant_int8_row(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                 uint8_t* codes, float* scales, hipStream_t st) {
+  return launch_row<true>(x, rows, cols, ldx, codes, scales, st);
+}
+
+hipError_t launch_quant_fp8_static(int mode, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                   const float* scales, uint8_t* codes, hipStream_t st) {
+  const dim3 grid = seg_grid(rows, cols), block(256);
+  if (mode == 0) hipLaunchKernelGGL(k_fp8_static<0>, grid, block, 0, st, x, rows, cols, ldx, scales, codes);
+  else if (mode == 1) hipLaunchKernelGGL(k_fp8_static<1>, grid, block, 0, st, x, rows, cols, ldx, scales, codes);
+  else hipLaunchKernelGGL(k_fp8_static<2>, grid, block, 0, st, x, rows, cols, ldx, scales, codes);
   return hipGetLastError();
 }
 

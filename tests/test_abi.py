@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert len(names) >= 9
     for n in names:
         assert hasattr(L, n), f"{n} declared in pql.h but not exported"
-    assert L.pql_version() == 1
+    assert L.pql_version() == 2
 
 
 def _sizes(scheme, role, rows, cols):
@@ -47,6 +47,8 @@ def test_quantized_sizes():
     assert _sizes("mxfp8", "activation", 3, 96) == (3 * 96, 3 * 4, 0)
     assert _sizes("mxfp4", "activation", 3, 384) == (3 * 192, 3 * 16, 0)
     assert _sizes("w4a16_asym", "weight", 12288, 3072) == (12288 * 1536, 2 * 12288 * 24, 12288 * 24)
+    assert _sizes("int8_row", "activation", 4096, 3072) == (4096 * 3072, 4 * 4096, 0)
+    assert _sizes("int8_row", "weight", 12288, 3072) == (12288 * 3072, 4 * 12288, 0)
 
 
 @pytest.mark.parametrize("scheme,role,rows,cols", [
@@ -67,7 +69,7 @@ def test_unsupported_combinations():
     with pytest.raises(NotImplementedError):
         _sizes("w4a16_asym", "activation", 4, 128)
     with pytest.raises(NotImplementedError):
-        _sizes(7, "activation", 4, 128)
+        _sizes(8, "activation", 4, 128)
     with pytest.raises(NotImplementedError):
         _sizes("fp8_row", 2, 4, 128)
 
@@ -85,8 +87,9 @@ def test_workspace_sizes():
 def test_kernel_names_distinct_per_scheme():
     names = {s: pql.kernel_name("qgemm", s, "activation", 4096, 4096, 4096) for s in S}
     assert all(names.values())
-    fp = [names[s] for s in ("fp8_row", "fp8_block128", "mxfp8", "mxfp4")]
-    assert len(set(fp)) == 4
+    fp = [names[s] for s in ("fp8_row", "fp8_block128", "mxfp8", "mxfp4", "int8_row")]
+    assert len(set(fp)) == 5
+    assert pql.kernel_name("quantize", "int8_row", "activation") == "k_fp8_row<int8>"
     assert pql.kernel_name("quantize", "w4a16_asym", "activation") == ""
     assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 1, 12288, 3072).startswith("k_w4a16_gemv")
     assert pql.kernel_name("qgemm", "w4a16_asym", "activation", 16, 12288, 3072).startswith("k_w4a16_gemv")
@@ -182,3 +185,41 @@ def test_python_api_errors_map_to_exceptions():
         pql.quantize(torch.zeros(4, 128, dtype=torch.float32), "mxfp8")
     with pytest.raises(ValueError):
         pql.quantize(torch.zeros(4, 128, dtype=torch.bfloat16), "nvfp4")
+
+
+def test_quantize_static_validation():
+    L = pql.lib()
+    q = lambda scheme=S["fp8_tensor"], role=A, x=_p(), rows=16, cols=128, ldx=128, scales=_p(4096), codes=_p(8192): \
+        L.pql_quantize_static(scheme, role, x, rows, cols, ldx, scales, codes, None)
+    assert q(scheme=S["fp8_row"]) == pql.PQL_ERR_UNSUPPORTED          # no static per-row scheme
+    assert q(scheme=S["int8_row"]) == pql.PQL_ERR_UNSUPPORTED         # int8 is dynamic only
+    assert q(scheme=S["mxfp8"]) == pql.PQL_ERR_UNSUPPORTED
+    assert q(scales=None) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert q(scales=_p(4100)) == pql.PQL_ERR_INVALID_ARGUMENT         # misaligned
+    assert q(scheme=S["fp8_block128"], cols=96, ldx=96) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert q(scheme=S["fp8_block128"], role=W, rows=64) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert q(rows=0) == pql.PQL_OK
+    with pytest.raises(NotImplementedError):
+        pql.quantize_static(torch.zeros(4, 128, dtype=torch.bfloat16), "fp8_row", "activation",
+                            torch.ones(4, dtype=torch.float32))
+
+
+def test_qgemm_ex_validation():
+    L = pql.lib()
+    g = lambda scheme=S["fp8_row"], alpha=1.0, bias=None, N=256, M=16: L.pql_qgemm_ex(
+        scheme, _p(), _p(1024), _p(2048), _p(3072), None, M, N, 256, alpha, bias, _p(8192), N, None)
+    assert g(scheme=S["mxfp8"], alpha=2.0) == pql.PQL_ERR_UNSUPPORTED     # no epilogue on MX
+    assert g(scheme=S["mxfp4"], bias=_p(4096)) == pql.PQL_ERR_UNSUPPORTED
+    assert g(alpha=float("nan")) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(alpha=float("inf")) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert g(bias=_p(4100)) == pql.PQL_ERR_INVALID_ARGUMENT               # misaligned bias
+    assert g(bias=_p(4096), N=255) == pql.PQL_ERR_INVALID_ARGUMENT        # odd N with a bias
+    assert g(scheme=S["mxfp8"], M=0) == pql.PQL_OK                        # alpha 1, no bias: any scheme
+    assert g(scheme=S["int8_row"], alpha=0.5, bias=_p(4096), M=0) == pql.PQL_OK
+    q = lambda scheme=S["fp8_tensor"], st=_p(512), alpha=1.0: L.pql_qlinear_ex(
+        scheme, _p(), 16, 256, 256, st, _p(2048), _p(3072), None, 256, alpha, None, _p(8192), 256,
+        _p(16384), 1 << 20, None)
+    assert q(scheme=S["fp8_row"]) == pql.PQL_ERR_UNSUPPORTED             # static scales: tensor / block only
+    assert q(scheme=S["int8_row"]) == pql.PQL_ERR_UNSUPPORTED
+    assert q(st=_p(516)) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert q(scheme=S["w4a16_asym"], st=None, alpha=3.0) == pql.PQL_ERR_UNSUPPORTED

@@ -416,6 +416,10 @@ def test_fp8_static_saturates_beyond_448_s():
     q = oracle.quantize_static(x, "fp8_tensor", "activation", np.array([2.0 ** -6], np.float32))
     # 64, -64, 32, 2^-14 (below the smallest subnormal 2^-9, rounds to 0), -65536 -> -448, 448
     assert q["codes"].tolist() == [[0x68, 0xE8, 0x60, 0x00, 0xFE, 0x7E]]
+    # quotients that overflow fp32 (2^127 / 2^-2 = 2^129) are infinite and saturate with their sign
+    x = bf16([[2.0 ** 127, -(2.0 ** 127), -0.0, 1.0]])
+    q = oracle.quantize_static(x, "fp8_tensor", "activation", np.array([0.25], np.float32))
+    assert q["codes"].tolist() == [[0x7E, 0xFE, 0x80, 0x48]]
 
 
 def test_fp8_static_with_the_dynamic_scale_equals_dynamic():
