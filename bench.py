@@ -29,7 +29,8 @@ import time
 
 import numpy as np
 
-PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "bf16": 2500.0}     # MI355X dense matrix peaks
+PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "bf16": 2500.0, "int8": 5000.0}   # MI355X dense matrix peaks (int8: TOP/s)
+EPI_SCHEMES = ("fp8_tensor", "fp8_row", "fp8_block128", "int8_row")           # GEMMs with the alpha / bias epilogue
 PEAK_HBM_GBS = 8000.0
 
 
@@ -155,9 +156,11 @@ def headline(torch, pql, steps, warmup):
 def all_workloads(torch, pql, steps, warmup, only=None):
     import workloads as wl
     lines = []
+    # int8 W8A8 has no workload of its own on the pages; it runs on the per-token /
+    # per-channel FP8 workload's shape and data, the scheme it mirrors.
     for name, scheme in (("fp8_tensor_small", "fp8_tensor"), ("fp8_row_dit", "fp8_row"),
-                         ("fp8_block_dit", "fp8_block128"), ("mx_video_dit", "mxfp8"),
-                         ("mx_video_dit", "mxfp4")):
+                         ("fp8_row_dit", "int8_row"), ("fp8_block_dit", "fp8_block128"),
+                         ("mx_video_dit", "mxfp8"), ("mx_video_dit", "mxfp4")):
         if only and name != only:
             continue
         w = wl.WORKLOADS[name]
@@ -180,8 +183,24 @@ def all_workloads(torch, pql, steps, warmup, only=None):
         tl = time_loop(torch, lambda i: pql.qlinear(acts[i % Ra], wq, out=out, workspace=ws), steps, warmup)
         flops = 2.0 * w.M * w.N * w.K
         ba, bw = quant_bytes(scheme, "activation", w.M, w.K), quant_bytes(scheme, "weight", w.N, w.K)
-        peak = PEAK_TFLOPS["fp4" if scheme == "mxfp4" else "fp8"]
-        lines.append({"workload": name, "scheme": scheme, "M": w.M, "N": w.N, "K": w.K,
+        peak = PEAK_TFLOPS["fp4" if scheme == "mxfp4" else "int8" if scheme == "int8_row" else "fp8"]
+        extra = {}
+        if scheme in EPI_SCHEMES:   # the fused epilogue alpha * (A W^T) + bias
+            bias = torch.randn(w.N, device="cuda").to(torch.bfloat16)
+            te = time_loop(torch, lambda i: pql.qgemm(aq, wq, out=out, alpha=0.5, bias=bias), steps, warmup)
+            extra.update({"gemm_epi_us": te * 1e3, "gemm_epi_tflops": flops / (te * 1e-3) / 1e12})
+        if scheme in pql.STATIC_SCHEMES:   # static activation scales
+            sa = aq.scales.clone()
+            aqs = pql.quantize_static(a0, scheme, "activation", sa)
+            ts = time_loop(torch, lambda i: pql.quantize_static(acts[i % Ra], scheme, "activation", sa, out=aqs),
+                           steps, warmup)
+            tls = time_loop(torch, lambda i: pql.qlinear(acts[i % Ra], wq, out=out, workspace=ws, alpha=0.5,
+                                                         bias=bias, act_scales=sa), steps, warmup)
+            bs = 2 * w.M * w.K + aq.codes.numel() + sa.numel() * 4   # bf16 in, codes out, scales in
+            extra.update({"quant_a_static_us": ts * 1e3, "quant_a_static_gbs": bs / (ts * 1e-3) / 1e9,
+                          "quant_a_static_hbm_frac": bs / (ts * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "qlinear_static_bias_us": tls * 1e3})
+        lines.append({"workload": name, "scheme": scheme, "M": w.M, "N": w.N, "K": w.K, **extra,
                       "quant_a_us": ta * 1e3, "quant_a_gbs": ba / (ta * 1e-3) / 1e9,
                       "quant_a_hbm_frac": ba / (ta * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "quant_w_us": tw * 1e3, "quant_w_gbs": bw / (tw * 1e-3) / 1e9,
@@ -189,7 +208,7 @@ def all_workloads(torch, pql, steps, warmup, only=None):
                       "gemm_us": tg * 1e3, "gemm_tflops": flops / (tg * 1e-3) / 1e12,
                       "gemm_mfma_frac": flops / (tg * 1e-3) / 1e12 / peak,
                       "qlinear_us": tl * 1e3, "qlinear_tflops": flops / (tl * 1e-3) / 1e12})
-        del acts, wts, aq, wq, out, ws
+        del acts, wts, aq, wq, out, ws, extra
         torch.cuda.empty_cache()
     if only and only != "w4a16_dit":
         return lines

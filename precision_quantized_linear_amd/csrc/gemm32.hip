@@ -70,9 +70,12 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 
-template <int KIND>
+// BIAS: the FP8 / int8 epilogue adds a per-column bias (a separate instance,
+// so the plain path carries no bias loads; alpha rides in the row scale).
+template <int KIND, bool BIAS>
 struct Kind {
   static constexpr bool kMx = KIND == GEMM_MXFP8 || KIND == GEMM_MXFP4;
+  static constexpr bool kBias = BIAS && !kMx;
   static constexpr bool kFp4 = KIND == GEMM_MXFP4;
   static constexpr bool kInt8 = KIND == GEMM_INT8_ROW;
   static constexpr int kSpr = kFp4 ? 4 : 2;                // MFMA slices per 128-byte row of a region
@@ -82,13 +85,13 @@ struct Kind {
   static constexpr int kSB = kFp4 ? 8 : 4;                 // e8m0 bytes per row and region
   static constexpr int kMxRegionBytes = kMx ? 2 * BM * kSB : 0;
   static constexpr int kWaveBytes = kMx ? 0 : kScaleBytes;
-  static constexpr int kScLoads = kMx ? 0 : 5;              // scale and bias loads per wave and tile
+  static constexpr int kScLoads = kMx ? 0 : kBias ? 5 : 4;  // scale and bias loads per wave and tile
   static constexpr int kLdsBytes = 2 * kRegionBytes + 2 * kMxRegionBytes + 4 * kWaveBytes;
 };
 
-template <int KIND>
+template <int KIND, bool BIAS>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
-  using T = Kind<KIND>;
+  using T = Kind<KIND, BIAS>;
   constexpr int kSpr = T::kSpr, kQ = T::kQ;
   __shared__ __attribute__((aligned(16))) uint8_t smem[T::kLdsBytes];
 
@@ -364,17 +367,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
       lds_load4(ra, scr + 256, va + (int)g.a_scale_stride * 256);
       lds_load4(rw, scr + 512, vw);
       lds_load4(rw, scr + 768, vw + (int)g.w_scale_stride * 256);
-      const int64_t nb = std::max<int64_t>(0, std::min<int64_t>(128, g.N - n0));
-      lds_load4(make_rsrc(g.bias ? g.bias + n0 : nullptr, g.bias ? (int)(nb * 2) : 0), scr + 1024, lane * 4);
+      if constexpr (T::kBias) {
+        const int64_t nb = std::max<int64_t>(0, std::min<int64_t>(128, g.N - n0));
+        lds_load4(make_rsrc(g.bias + n0, (int)(nb * 2)), scr + 1024, lane * 4);
+      }
     }
   };
   const uint16_t* bias_cols = reinterpret_cast<const uint16_t*>(wave_lds + 1024);
   // Value of accumulator element (i, j, r) as written to C: rs carries alpha
   // (alpha * s_a[m]), cs is s_w[n], b the bias; int8 sums are converted first.
   auto out_val = [&](float a, float rs, float cs, float b) __attribute__((always_inline)) {
+    const float v = T::kInt8 ? (float)__builtin_bit_cast(int, a) : a;
     if constexpr (T::kMx) return a;
-    else if constexpr (T::kInt8) return __builtin_fmaf((float)__builtin_bit_cast(int, a) * rs, cs, b);
-    else return __builtin_fmaf(a * rs, cs, b);
+    else if constexpr (T::kBias) return __builtin_fmaf(v * rs, cs, b);
+    else return v * rs * cs;
   };
 
   // ---- epilogue of tile k: each lane owns output row m = 32 i + l % 32 of block
@@ -409,11 +415,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
         float4 cs[4], bs[4];
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          if constexpr (T::kMx) {
-            cs[rq] = float4{1.f, 1.f, 1.f, 1.f};
-            bs[rq] = float4{0.f, 0.f, 0.f, 0.f};
-          } else {
-            cs[rq] = cs4[j * 8 + rq * 2 + fk];
+          cs[rq] = T::kMx ? float4{1.f, 1.f, 1.f, 1.f} : cs4[j * 8 + rq * 2 + fk];
+          bs[rq] = float4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (T::kBias) {
             const uint2 bw = *reinterpret_cast<const uint2*>(bias_cols + j * 32 + rq * 8 + fk * 4);
             bs[rq] = float4{__uint_as_float(bw.x << 16), __uint_as_float(bw.x & 0xFFFF0000u),
                             __uint_as_float(bw.y << 16), __uint_as_float(bw.y & 0xFFFF0000u)};
@@ -547,13 +551,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm32(GemmArgs g) {
 template <int KIND>
 hipError_t launch_kind32(const GemmArgs& g, hipStream_t st) {
   const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
-  const int64_t row_bytes = Kind<KIND>::kFp4 ? g.K / 2 : g.K;
+  const int64_t row_bytes = Kind<KIND, false>::kFp4 ? g.K / 2 : g.K;
   // The load stream runs two regions ahead, into the next tile, which is the
   // next tile's own first regions only when a tile has at least two regions;
   // shorter K gets one tile per workgroup (its look-ahead loads then land in a
   // region that is never read).
   const int grid = (row_bytes / kRow >= 2) ? std::min(tiles, kPersistentCap) : tiles;
-  hipLaunchKernelGGL(k_gemm32<KIND>, dim3(grid), dim3(kThreads), 0, st, g);
+  if constexpr (!Kind<KIND, false>::kMx) {
+    if (g.bias) {
+      hipLaunchKernelGGL((k_gemm32<KIND, true>), dim3(grid), dim3(kThreads), 0, st, g);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_gemm32<KIND, false>), dim3(grid), dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
 

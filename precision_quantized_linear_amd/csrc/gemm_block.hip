@@ -57,6 +57,9 @@ constexpr int kPersistentCap = 256;
 
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
+// EPI: apply alpha * (...) + bias in the epilogue (a separate instance, so the
+// plain kernel's code is unchanged).
+template <bool EPI>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
 
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
     int tm, tn;
     sched.coords(k, tm, tn);
     const int64_t m0 = (int64_t)tm * BM + wm * 128, n0 = (int64_t)tn * BN + wn * 64;
-    if (g.alpha != 1.0f || g.bias) {   // wave-uniform; N % 128 == 0, so every column exists
+    if constexpr (EPI) {   // N % 128 == 0, so every column exists
       float b[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -335,7 +338,8 @@ hipError_t launch_gemm_block(const GemmArgs& g, hipStream_t st) {
   // K-groups those loads would reach past the next tile, so short K gets one
   // tile per workgroup (its look-ahead loads land in slots that are never read).
   const int grid = (g.K / kRow >= kSlots) ? std::min(tiles, kPersistentCap) : tiles;
-  hipLaunchKernelGGL(k_gemm_block, dim3(grid), dim3(kThreads), 0, st, g);
+  if (g.alpha != 1.0f || g.bias) hipLaunchKernelGGL(k_gemm_block<true>, dim3(grid), dim3(kThreads), 0, st, g);
+  else hipLaunchKernelGGL(k_gemm_block<false>, dim3(grid), dim3(kThreads), 0, st, g);
   return hipGetLastError();
 }
 
