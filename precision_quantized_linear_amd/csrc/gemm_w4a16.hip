@@ -466,7 +466,7 @@ const char* gemm_w4a16_kernel_name(int64_t M, int64_t N, int64_t K) {
   if (M <= 16) return "k_w4a16_small<16>";
   if (M <= 32) return "k_w4a16_small<32>";
   if (M <= 64) return "k_w4a16_small<64>";
-  if (w4a16_mm_supported(M, N, K)) return "k_w4a16_mm_256x128x64";
+  if (w4a16_mm_supported(M, N, K)) return w4a16_mm_narrow(M, N) ? "k_w4a16_mm_256x64x64" : "k_w4a16_mm_256x128x64";
   return "k_w4a16_tile_256x256x64";
 }
 

@@ -43,32 +43,52 @@ namespace {
 
 using namespace gemm;
 
-constexpr int BM = 256, BN = 128;
+constexpr int BM = 256;
 constexpr int kARow = 128;                         // A bytes per row per step (64 bf16)
 constexpr int kAStage = BM * kARow;                // 32 KB
-constexpr int kAStages = 3;
 constexpr int kCRow = 32;                          // code bytes per weight row per step
-constexpr int kCStage = BN * kCRow;                // 4 KB
 constexpr int kLead = 5;                           // codes (and scales) run this many steps ahead
 constexpr int kCStages = kLead + 1;
 constexpr int kSZSlots = 3;
 constexpr int kWRow = 128;                         // expanded bf16 bytes per weight row per step
-constexpr int kWBuf = BN * kWRow;                  // 16 KB
-constexpr int kSZ = 512;                           // per group slot: 128 bf16 scales, then 128 zero-points (+ pad)
-constexpr int kOffC = kAStages * kAStage;
-constexpr int kOffW = kOffC + kCStages * kCStage;
-constexpr int kOffSZ = kOffW + 2 * kWBuf;
-constexpr int kLds = kOffSZ + kSZSlots * kSZ;      // 153.5 KB
+constexpr int kSZ = 512;                           // per group slot: up to 128 bf16 scales, then the zero-points
 constexpr int kEpiRow = 136;                       // staged output row: 64 bf16 + 8 bytes of padding
 constexpr int kEpiBytes = 32 * kEpiRow;            // per wave, inside the (idle) A stages at the end
 
+// Tile shape: 256 x BN.  BN = 128: each MFMA wave owns 128 x 64 (the large-M
+// shape); BN = 64: each owns 64 x 64, which doubles the number of tiles when
+// M is small and 256 x 128 tiles leave CUs idle, while every weight element is
+// still expanded once per 256 output rows.
+template <int BN>
+struct Shape {
+  // A stages: the loads of step s + kAStages - 1 are issued during step s, so
+  // they have kAStages - 2 steps to land.  (A fourth stage, which the narrow
+  // shape has the LDS for, measured the same: its steps are bounded by the
+  // rate at which each CU takes in the tile's 32 KB of A, not by latency.)
+  static constexpr int kAStages = 3;
+  static constexpr int kCStage = BN * kCRow;                 // codes of one step
+  static constexpr int kWBuf = BN * kWRow;                   // expanded weights of one step
+  static constexpr int kOffC = kAStages * kAStage;
+  static constexpr int kOffW = kOffC + kCStages * kCStage;
+  static constexpr int kOffSZ = kOffW + 2 * kWBuf;
+  static constexpr int kLds = kOffSZ + kSZSlots * kSZ;     // 153.5 KB (BN 128), 125.5 KB (BN 64)
+  static constexpr int kCodeWaves = BN / 32;               // helper waves that load codes (32 rows each)
+  static constexpr int kThreadsPerRow = 256 / BN;          // helper threads expanding one weight row
+  static constexpr int kWaveM = BN == 128 ? 128 : 64;      // MFMA wave tile: kWaveM x 64
+  static constexpr int NI = kWaveM / 32;                   // 32-row blocks per MFMA wave
+};
+
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+template <int BN>
 __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict__ a, const uint32_t* __restrict__ wq,
                                                     const uint16_t* __restrict__ w_scales,
                                                     const uint8_t* __restrict__ w_zeros, int64_t M, int64_t N,
                                                     int64_t K, uint16_t* __restrict__ c, int64_t ldc) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kLds];
+  using S = Shape<BN>;
+  constexpr int kCStage = S::kCStage, kWBuf = S::kWBuf, kOffC = S::kOffC, kOffW = S::kOffW, kOffSZ = S::kOffSZ;
+  constexpr int kAStages = S::kAStages;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S::kLds];
 
   // XCD-aware tile order: workgroup b runs on XCD b % 8; each XCD takes a
   // contiguous range of tiles, walked in 4-tile-tall column groups.
@@ -96,8 +116,8 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
     const int Ab = (int)(K * 2), Wb = (int)(K / 2);   // bytes per A row, per code row
     // Per-tile descriptors cover the tile's valid rows (rows past M / N read
     // 0); lane offsets carry the row, the step's K offset rides in the scalar
-    // offset.  Helper wave h moves A rows 64 h .. + 63 (8 loads of 8 rows) and
-    // the codes of weight rows 32 h .. + 31 (one load).
+    // offset.  Helper wave h moves A rows 64 h .. + 63 (8 loads of 8 rows) and,
+    // for h < BN / 32, the codes of weight rows 32 h .. + 31 (one load).
     const v4i a_rsrc = make_rsrc(a + m0 * K, mr * Ab);
     const v4i w_rsrc = make_rsrc(reinterpret_cast<const uint8_t*>(wq) + n0 * Wb, nr * Wb);
     int voff_a[8];
@@ -109,8 +129,9 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
                     std::min(s, nsteps - 1) * kARow);
     };
     auto load_codes = [&](int s) __attribute__((always_inline)) {
-      lds_load16_so(w_rsrc, smem + kOffC + (s % kCStages) * kCStage + hw * 32 * kCRow, voff_c,
-                    std::min(s, nsteps - 1) * kCRow);
+      if (hw < S::kCodeWaves)
+        lds_load16_so(w_rsrc, smem + kOffC + (s % kCStages) * kCStage + hw * 32 * kCRow, voff_c,
+                      std::min(s, nsteps - 1) * kCRow);
     };
     auto load_group = [&](int g) __attribute__((always_inline)) {   // waves 0 and 1 of the helpers
       const int gc = std::min(g, ng - 1);
@@ -119,15 +140,23 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
       else lds_load4(make_rsrc(w_zeros + (int64_t)gc * N + n0, nr), slot + 256, lane * 4);
     };
 
-    // Expansion of step s's codes into weight buffer s & 1: helper thread h
-    // owns weight row h / 2, elements 32 (h % 2) .. + 31 of the step (chunks
-    // 4 (h % 2) .. + 3 of the row); even and odd nibbles are spread into the
-    // bytes of two words, so each code converts with one byte-to-float
-    // instruction.
-    const int er = ht >> 1, eh = ht & 1;
+    // Expansion of step s's codes into weight buffer s & 1: with T = 256 / BN
+    // helper threads per weight row, thread h owns row h / T and its part
+    // h % T of the step's 8 code words (chunks 8 / T (h % T) .. of the row);
+    // even and odd nibbles are spread into the bytes of two words, so each
+    // code converts with one byte-to-float instruction.
+    constexpr int kWords = 8 / S::kThreadsPerRow;   // code words (8 elements each) per thread
+    const int er = ht / S::kThreadsPerRow, eh = ht % S::kThreadsPerRow;
     auto expand = [&](int s) __attribute__((always_inline)) {
       const uint8_t* cs = smem + kOffC + (s % kCStages) * kCStage;
-      const uint4 code = *reinterpret_cast<const uint4*>(cs + er * kCRow + eh * 16);
+      uint32_t code[kWords];
+      if constexpr (kWords == 4) {
+        const uint4 c4 = *reinterpret_cast<const uint4*>(cs + er * kCRow + eh * 16);
+        code[0] = c4.x, code[1] = c4.y, code[2] = c4.z, code[3] = c4.w;
+      } else {
+        const uint2 c2 = *reinterpret_cast<const uint2*>(cs + er * kCRow + eh * 8);
+        code[0] = c2.x, code[1] = c2.y;
+      }
       const uint8_t* sz = smem + kOffSZ + ((s >> 1) % kSZSlots) * kSZ;
       const uint32_t sb = *reinterpret_cast<const uint16_t*>(sz + er * 2);
       const uint32_t zb = sz[256 + er];
@@ -135,8 +164,8 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
       const float zs = -(float)zb * sc;   // exact: z * s fits in fp32
       uint8_t* wb = smem + kOffW + (s & 1) * kWBuf;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t w = q == 0 ? code.x : q == 1 ? code.y : q == 2 ? code.z : code.w;
+      for (int q = 0; q < kWords; ++q) {
+        const uint32_t w = code[q];
         uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
         asm volatile("" : "+v"(ev), "+v"(od));   // keep the byte planes
         uint32_t pr[4];
@@ -144,16 +173,15 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
         for (int j = 0; j < 4; ++j)
           pr[j] = pack_bf16x2(__builtin_fmaf((float)((ev >> (8 * j)) & 0xFF), sc, zs),
                               __builtin_fmaf((float)((od >> (8 * j)) & 0xFF), sc, zs));
-        *reinterpret_cast<uint4*>(wb + swz128(er, 4 * eh + q)) = uint4{pr[0], pr[1], pr[2], pr[3]};
+        *reinterpret_cast<uint4*>(wb + swz128(er, kWords * eh + q)) = uint4{pr[0], pr[1], pr[2], pr[3]};
       }
     };
 
-    // Prologue: A of steps 0, 1; codes of steps 0 .. kLead - 1; groups 0 .. 2.
+    // Prologue: A of steps 0 .. kAStages - 2; codes of steps 0 .. kLead - 1; groups 0 .. 2.
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      load_a(0, 0, p);
-      load_a(1, 1, p);
-    }
+    for (int st = 0; st + 1 < kAStages; ++st)
+#pragma unroll
+      for (int p = 0; p < 8; ++p) load_a(st, st, p);
 #pragma unroll
     for (int s = 0; s < kLead; ++s) load_codes(s);
     if (hw < 2) {
@@ -165,21 +193,33 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
     expand(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     __builtin_amdgcn_s_barrier();
-    // Step s (between barriers B(s - 1) and B(s)): loads of A for step s + 2
-    // (its stage was last read before B(s - 1)), of codes for step s + kLead
-    // and, when that step starts a group, of the group's scales; then the
-    // expansion of step s + 1 (codes and scales landed before B(s - 1)).
-    // B(s) needs A of step s + 1 (issued during step s - 1) and everything
-    // older; younger are step s - 1's code load and, on every other step, its
-    // scale load (helper waves 0 and 1), then this step's 9 or 10 loads.
+    // Step s (between barriers B(s - 1) and B(s)): loads of A for step
+    // s + kAStages - 1 (its stage was last read before B(s - 1)), of codes for
+    // step s + kLead and, when that step starts a group, of the group's
+    // scales; then the expansion of step s + 1 (codes and scales landed
+    // before B(s - 1)).  B(s) needs A of step s + 1, issued during step
+    // s - kAStages + 2, and everything older; younger are that step's code
+    // load and everything issued in the kAStages - 2 steps after it.  Per step
+    // a wave issues 8 A loads, a code load if h < BN / 32, and, if h < 2, a
+    // scale load on every other step, so the younger count is
+    //   A only:          8 (kAStages - 2)
+    //   A + codes:       1 + 9 (kAStages - 2)
+    //   A + codes + scales: 1 + 9 (kAStages - 2) + the scale loads among
+    //                    kAStages - 1 consecutive steps, at least
+    //                    (kAStages - 1) / 2 rounded down
+    // (waiting for fewer outstanding loads than that only waits longer).
+    constexpr int kYoungA = 8 * (kAStages - 2);
+    constexpr int kYoungAC = 1 + 9 * (kAStages - 2);
+    constexpr int kYoungACS = kYoungAC + (kAStages - 1) / 2;
     for (int s = 0; s < nsteps; ++s) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) load_a(s + 2, (s + 2) % kAStages, p);
+      for (int p = 0; p < 8; ++p) load_a(s + kAStages - 1, (s + kAStages - 1) % kAStages, p);
       load_codes(s + kLead);
       if (((s + kLead) & 1) == 0 && hw < 2) load_group((s + kLead) >> 1);
       expand(s + 1);   // the last step expands a clamped step that is never read
-      if (hw < 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(11, 0));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_imm(10, 0));
+      if (hw < 2) __builtin_amdgcn_s_waitcnt(waitcnt_imm(kYoungACS, 0));   // hw < 2 <= BN / 32: codes too
+      else if (hw < S::kCodeWaves) __builtin_amdgcn_s_waitcnt(waitcnt_imm(kYoungAC, 0));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_imm(kYoungA, 0));
       __builtin_amdgcn_s_barrier();
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));   // every load has landed before LDS is reused
@@ -187,7 +227,7 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
     return;
   }
 
-  // ================= MFMA waves: one 128 x 64 quarter of the tile each =================
+  // ================= MFMA waves: a kWaveM x 64 part of the tile each =================
   // v_mfma_f32_32x32x16_bf16 (the form that runs at the full bf16 rate on
   // gfx950): lane l feeds row l % 32 and, with g = l / 32, K-elements
   // 8 g .. 8 g + 7 of a 16-element quarter step kq, i.e. chunk 2 kq + g of the
@@ -195,25 +235,27 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
   // with itself.  The weight fragment is the first operand, so accumulator
   // register r of lane l holds C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]:
   // four consecutive columns per register quad.
-  const int wm = wave >> 1, wn = wave & 1;
+  // BN = 128: waves form 2 x 2 parts of 128 x 64; BN = 64: 4 x 1 parts of 64 x 64.
+  constexpr int NI = S::NI, kWaveM = S::kWaveM;
+  const int wm = BN == 128 ? wave >> 1 : wave, wn = BN == 128 ? wave & 1 : 0;
   const int fr = lane & 31, fg = lane >> 5;
   int aoff[4], woff[4];
 #pragma unroll
   for (int kq = 0; kq < 4; ++kq) {
-    aoff[kq] = swz128(wm * 128 + fr, 2 * kq + fg);
+    aoff[kq] = swz128(wm * kWaveM + fr, 2 * kq + fg);
     woff[kq] = swz128(wn * 64 + fr, 2 * kq + fg);
   }
-  v16f acc[4][2];
+  v16f acc[NI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
-  uint4 fa[2][4], fw[2][2];   // two register sets, alternating by quarter step
+  uint4 fa[2][NI], fw[2][2];   // two register sets, alternating by quarter step
   auto read_quarter = [&](int s, int kq, int set) __attribute__((always_inline)) {
     const uint8_t* As = smem + (s % kAStages) * kAStage;
     const uint8_t* Ws = smem + kOffW + (s & 1) * kWBuf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[set][i] = lds16(As + aoff[kq] + i * 32 * kARow);
+    for (int i = 0; i < NI; ++i) fa[set][i] = lds16(As + aoff[kq] + i * 32 * kARow);
 #pragma unroll
     for (int j = 0; j < 2; ++j) fw[set][j] = lds16(Ws + woff[kq] + j * 32 * kWRow);
   };
@@ -221,8 +263,8 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
   __builtin_amdgcn_s_barrier();   // step 0's weights are expanded
   __builtin_amdgcn_sched_barrier(0);
   read_quarter(0, 0, 0);
-  // Step s: quarter steps kq = 0..3 of 4 x 2 MFMAs each, register set kq & 1,
-  // the next quarter's 6 fragment reads interleaved.  Every read of step s's
+  // Step s: quarter steps kq = 0..3 of NI x 2 MFMAs each, register set kq & 1,
+  // the next quarter's NI + 2 fragment reads interleaved.  Every read of step s's
   // stage and weight buffer is issued before quarter 3, so B(s) comes there;
   // past it, step s + 1's A and weights are complete, and its first quarter
   // is read under quarter 3's MFMAs.
@@ -236,17 +278,17 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NI; ++i) {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fw[cs][j]),
                                                             __builtin_bit_cast(v8bf, fa[cs][i]), acc[i][j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        const int e = j * 4 + i;
-        if (e < 6) {
+        const int e = j * NI + i;
+        if (e < NI + 2) {
           const int sn = kq == 3 ? s + 1 : s, kn = (kq + 1) & 3;
           const uint8_t* As = smem + (sn % kAStages) * kAStage;
           const uint8_t* Ws = smem + kOffW + (sn & 1) * kWBuf;
-          if (e < 4) fa[ns][e] = lds16(As + aoff[kn] + e * 32 * kARow);
-          else fw[ns][e - 4] = lds16(Ws + woff[kn] + (e - 4) * 32 * kWRow);
+          if (e < NI) fa[ns][e] = lds16(As + aoff[kn] + e * 32 * kARow);
+          else fw[ns][e - NI] = lds16(Ws + woff[kn] + (e - NI) * 32 * kWRow);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -265,11 +307,11 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
   __builtin_amdgcn_s_barrier();
   uint8_t* stg = smem + wave * kEpiBytes;
   const int rr = lane >> 3, rc = lane & 7;
-  const int64_t wrow0 = m0 + wm * 128, wcol0 = n0 + wn * 64;
+  const int64_t wrow0 = m0 + wm * kWaveM, wcol0 = n0 + wn * 64;
   const bool vec = (ldc & 7) == 0 && (reinterpret_cast<uintptr_t>(c) & 15) == 0;
-  const bool interior = vec && wrow0 + 128 <= M && wcol0 + 64 <= N;
+  const bool interior = vec && wrow0 + kWaveM <= M && wcol0 + 64 <= N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -310,11 +352,20 @@ bool w4a16_mm_supported(int64_t M, int64_t N, int64_t K) {
   return M > 0 && N % 4 == 0 && K % 128 == 0 && K / 64 >= 1 && K * 2 * 256 < (int64_t)1 << 31;
 }
 
+// 256 x 64 tiles when 256 x 128 tiles would fill at most half of the CUs: twice
+// the workgroups, each weight element still expanded once per 256 rows.
+bool w4a16_mm_narrow(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + 127) / 128) <= 128; }
+
 hipError_t launch_gemm_w4a16_mm(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales,
                                 const uint8_t* w_zeros, int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc,
                                 hipStream_t st) {
-  const int tiles = (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
-  hipLaunchKernelGGL(k_w4a16_mm, dim3(tiles), dim3(512), 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+  if (w4a16_mm_narrow(M, N)) {
+    const int tiles = (int)(((M + BM - 1) / BM) * ((N + 63) / 64));
+    hipLaunchKernelGGL(k_w4a16_mm<64>, dim3(tiles), dim3(512), 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+  } else {
+    const int tiles = (int)(((M + BM - 1) / BM) * ((N + 127) / 128));
+    hipLaunchKernelGGL(k_w4a16_mm<128>, dim3(tiles), dim3(512), 0, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+  }
   return hipGetLastError();
 }
 

@@ -79,6 +79,8 @@ const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);
 // W4A16: C = A (bf16) * dequant(Wq)^T
 // W4A16, M > 64: pipelined 256 x 128 tile kernel (N % 4 == 0, K % 128 == 0).
 bool w4a16_mm_supported(int64_t M, int64_t N, int64_t K);
+// Whether the 256 x 64 tile shape is used (small M: 256 x 128 tiles would leave CUs idle).
+bool w4a16_mm_narrow(int64_t M, int64_t N);
 hipError_t launch_gemm_w4a16_mm(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales,
                                 const uint8_t* w_zeros, int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc,
                                 hipStream_t st);

@@ -100,10 +100,16 @@ def test_quantize_bit_exact(scheme, role, rows, cols):
         assert np.array_equal(q.zeros.cpu().numpy(), ref["zeros"].T)
 
 
-@pytest.mark.parametrize("M,N,K", [(257, 388, 384), (1000, 260, 640), (512, 1024, 256), (130, 390, 384)])
+@pytest.mark.parametrize("M,N,K", [(257, 388, 384), (1000, 260, 640), (512, 1024, 256), (130, 390, 384),
+                                   (2304, 4100, 256), (300, 4100, 512)])
 def test_w4a16_gemm_tile_shapes(M, N, K):
-    # ragged M and N tails across several 256 x 128 tiles, an odd number of
-    # K-groups, and N % 4 != 0 (which takes the older tile kernel)
+    # ragged M and N tails across several 256 x 64 tiles (few tiles) and 256 x 128
+    # tiles (2304 x 4100: more than 128 of them), an odd number of K-groups, and
+    # N % 4 != 0 (which takes the older tile kernel)
+    narrow = -(-M // 256) * -(-N // 128) <= 128
+    if N % 4 == 0:
+        assert pql.kernel_name("qgemm", "w4a16_asym", "activation", M, N, K) == \
+            ("k_w4a16_mm_256x64x64" if narrow else "k_w4a16_mm_256x128x64")
     a = wl.small_case(5000 + M, M, K, 1.0)
     w = wl.small_case(6000 + N, N, K, 0.02)
     wq = oracle.quantize(w, "w4a16_asym", "weight")
