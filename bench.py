@@ -7,7 +7,7 @@ activation (amax, scale, round-to-nearest-even cast, pack), then the FP8 GEMM
 with the scales applied in its epilogue, bf16 out.  The weight is quantized
 once, before timing, as a layer does at load.
 
-    python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--all] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--all] [--no-cpu]
 
 Prints one JSON line: qlinear TFLOP/s (value), the quantize kernel's GB/s, a
 roofline object for the dominant kernel (the GEMM, timed with HIP events on
@@ -37,8 +37,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    # The GPU's clock settles over the first few milliseconds of load: 20 untimed
+    # steps (~3 ms) come before the timed ones.
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--all", action="store_true", help="also time every workload and kernel")
     p.add_argument("--workload", default=None, help="with --all: only this workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -75,15 +77,23 @@ def quant_bytes(scheme: str, role: str, rows: int, cols: int) -> int:
 
 
 class EventTimer:
-    """Per-launch durations from HIP events recorded on the launching (current) stream."""
+    """Per-launch durations from HIP events recorded on the launching (current) stream.
+    Events are made ahead of time (``reserve``), so timing adds no allocation."""
 
     def __init__(self, torch):
         self.torch = torch
         self.pairs = []
+        self.spare = []
+
+    def reserve(self, n):
+        t = self.torch
+        self.spare = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(n)]
 
     def __call__(self, fn):
-        t = self.torch
-        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        if self.spare:
+            s, e = self.spare.pop()
+        else:
+            s, e = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
         s.record()
         fn()
         e.record()
@@ -131,6 +141,8 @@ def headline(torch, pql, steps, warmup):
     torch.cuda.synchronize()
     tq.pairs.clear()
     tg.pairs.clear()
+    tq.reserve(steps)
+    tg.reserve(steps)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
@@ -289,7 +301,7 @@ def measured_traffic(kernel_source: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     torch, pql = gpu_setup()
