@@ -252,8 +252,8 @@ pql_status pql_quantize(int scheme, int role, const void* x, int64_t rows, int64
   if (rows == 0) return ok();
   if (!x || !codes || !scales) return fail(PQL_ERR_INVALID_ARGUMENT, "x, codes and scales must be non-NULL");
   if (is_w4a16(scheme) && !zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for W4A16");
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
-    return fail(PQL_ERR_INVALID_ARGUMENT, "x, codes and scales must be 16-byte aligned");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || (zeros && !aligned16(zeros)))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "x, codes, scales and zeros must be 16-byte aligned");
   if (scheme == PQL_FP8_TENSOR) {
     if (!workspace || workspace_bytes < kTensorWs)
       return fail(PQL_ERR_WORKSPACE, "FP8_TENSOR needs a %zu-byte workspace (got %zu)", kTensorWs,
@@ -276,8 +276,8 @@ pql_status pql_dequantize(int scheme, int role, const void* codes, const void* s
   if (rows == 0) return ok();
   if (!codes || !scales || !y) return fail(PQL_ERR_INVALID_ARGUMENT, "codes, scales and y must be non-NULL");
   if (is_w4a16(scheme) && !zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for W4A16");
-  if (!aligned16(codes) || !aligned16(scales) || !aligned16(y))
-    return fail(PQL_ERR_INVALID_ARGUMENT, "codes, scales and y must be 16-byte aligned");
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(y) || (zeros && !aligned16(zeros)))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "codes, scales, zeros and y must be 16-byte aligned");
   if ((st = check_device()) != PQL_OK) return st;
   int kind;
   switch (scheme) {
@@ -352,8 +352,9 @@ pql_status pql_qgemm_ex(int scheme, const void* a, const void* a_scales, const v
   if (!a || !w_codes || !w_scales || !c) return fail(PQL_ERR_INVALID_ARGUMENT, "a, w_codes, w_scales and c must be non-NULL");
   if (!is_w4a16(scheme) && !a_scales) return fail(PQL_ERR_INVALID_ARGUMENT, "a_scales must be non-NULL");
   if (is_w4a16(scheme) && !w_zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "w_zeros must be non-NULL for W4A16");
-  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || (a_scales && !aligned16(a_scales)))
-    return fail(PQL_ERR_INVALID_ARGUMENT, "operands and scales must be 16-byte aligned");
+  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || (a_scales && !aligned16(a_scales)) ||
+      (w_zeros && !aligned16(w_zeros)))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "operands, scales and zero-points must be 16-byte aligned");
   if ((st = check_device()) != PQL_OK) return st;
   return launched(do_qgemm(scheme, a, a_scales, w_codes, w_scales, w_zeros, M, N, K, alpha, bias, c, ldc,
                            static_cast<hipStream_t>(stream)),
@@ -382,8 +383,9 @@ pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64
   if (M == 0) return ok();
   if (!a || !w_codes || !w_scales || !c) return fail(PQL_ERR_INVALID_ARGUMENT, "a, w_codes, w_scales and c must be non-NULL");
   if (is_w4a16(scheme) && !w_zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "w_zeros must be non-NULL for W4A16");
-  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || (a_static_scales && !aligned16(a_static_scales)))
-    return fail(PQL_ERR_INVALID_ARGUMENT, "operands and scales must be 16-byte aligned");
+  if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || (a_static_scales && !aligned16(a_static_scales)) ||
+      (w_zeros && !aligned16(w_zeros)))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "operands, scales and zero-points must be 16-byte aligned");
   if (!is_w4a16(scheme)) {
     const size_t need = qlinear_ws_bytes(scheme, M, K);
     if (!workspace || workspace_bytes < need)

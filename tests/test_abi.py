@@ -151,6 +151,7 @@ def test_qgemm_validation():
     assert g(scheme=S["fp8_block128"], N=200, ldc=200) == pql.PQL_ERR_INVALID_ARGUMENT
     assert g(a=_p(8)) == pql.PQL_ERR_INVALID_ARGUMENT
     assert g(scheme=11) == pql.PQL_ERR_UNSUPPORTED
+    assert g(scheme=S["w4a16_asym"], wz=_p(4100)) == pql.PQL_ERR_INVALID_ARGUMENT   # misaligned zero-points
     assert g(M=0) == pql.PQL_OK
 
 
