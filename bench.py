@@ -7,7 +7,7 @@ activation (amax, scale, round-to-nearest-even cast, pack), then the FP8 GEMM
 with the scales applied in its epilogue, bf16 out.  The weight is quantized
 once, before timing, as a layer does at load.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--all] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 100] [--all] [--no-cpu]
 
 Prints one JSON line: qlinear TFLOP/s (value), the quantize kernel's GB/s, a
 roofline object for the dominant kernel (the GEMM, timed with HIP events on
@@ -38,9 +38,10 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    # The GPU's clock settles over the first few milliseconds of load: 20 untimed
-    # steps (~3 ms) come before the timed ones.
-    p.add_argument("--warmup", type=int, default=20)
+    # The GPU's clock settles over the first ~15 ms of load (measured: the GEMM takes
+    # ~137 us after 20 untimed steps, 127 us after 50, 121-123 us after 100-200), so
+    # 100 untimed steps come before the timed ones.
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--all", action="store_true", help="also time every workload and kernel")
     p.add_argument("--workload", default=None, help="with --all: only this workload")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
