@@ -8,22 +8,24 @@
 // online quantization works underneath"), applied to the fp32 sums before
 // the one rounding to bf16.
 //
-// A 128-wide K-group is exactly one v_mfma_scale_f32_16x16x128_f8f6f4 (unit
-// MFMA scales), so every group's partial product P comes out of the matrix
-// core on its own and is promoted into the fp32 sums with one FMA per element:
-// acc += P * (s_a[m, g] * s_w[nb, g]).  The sums are VALU operands, so they
-// live in VGPRs; that caps a wave at a 128 x 64 output block (128 sums per
-// lane) and a workgroup of 4 waves at a 256 x 128 tile.  The W fragment is the
-// MFMA's first operand, so lane l's P holds C[m = l % 16][n = 4 (l / 16) + r]:
-// one row per lane (one activation scale per 16-row block) and four
-// consecutive columns; the weight scale is uniform over the tile.
+// A 128-wide K-group is two v_mfma_scale_f32_32x32x64_f8f6f4 (unit MFMA
+// scales) per 32 x 32 output block, so every group's partial product P comes
+// out of the matrix core on its own and is promoted into the fp32 sums with
+// one FMA per element: acc += P * (s_a[m, g] * s_w[nb, g]).  The sums are VALU
+// operands, so they live in VGPRs; that caps a wave at a 128 x 64 output block
+// (128 sums per lane) and a workgroup of 4 waves at a 256 x 128 tile.  The W
+// fragment is the MFMA's first operand, so lane l's P holds
+// C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4] for r = 0..15: one row per
+// lane (one activation scale per 32-row block) and four quads of consecutive
+// columns; the weight scale is uniform over the tile.  Each block's 16
+// promotion FMAs run behind the next block's two 64-cycle MFMAs.
 //
 // Pipeline: one 128-byte K-group per "region"; LDS holds three regions
 // (A 256 rows + W 128 rows of 128 bytes, the A scales of the group, and the W
 // scale), filled by direct-to-LDS loads of whole 128-byte lines (lane i of an
-// 8-row load fetches the chunk of row i / 8 whose swizzled position is i % 8, which is the
-// swizzled position: chunk c of row r at c ^ ((r / 2) % 8)).  Before region R the
-// waves wait for region R + 1 and meet at a barrier; region R's 32 MFMAs are
+// 8-row load fetches the chunk of row i / 8 whose swizzled position is i % 8;
+// chunk c of row r sits at c ^ ((r / 2) % 8)).  Before region R the waves
+// wait for region R + 1 and meet at a barrier; region R's 16 MFMAs are
 // interleaved with the LDS reads of region R + 1's fragments and with the loads
 // of region R + 3 into region R's slot.  The grid is persistent, one
 // workgroup per CU, with the XCD-aware tile order of the other GEMMs.
@@ -49,13 +51,13 @@ constexpr int kRegion = kAOp + kWOp;               // 48 KB
 constexpr int kSlots = 3;                          // regions in the ring
 constexpr int kSaBytes = BM * 4;                   // A scales of one group
 constexpr int kSwBytes = 256;                      // W scale of one group, one copy per lane of a wave
-constexpr int kEpiRow = 136;                       // staged output row: 64 bf16 + 8 bytes of padding
-constexpr int kEpiBytes = 16 * kEpiRow;            // per wave: 16 output rows
 constexpr int kLoads = 8 + 4 + 1 + 1;              // per wave and region: A rows, W rows, A scales, W scale
+constexpr int kEpiRow = 144;                       // staged output row: 64 bf16 + 16 bytes of padding
+constexpr int kEpiBytes = 16 * kEpiRow;            // per wave: 16 output rows
 constexpr int kLds = kSlots * kRegion + kSlots * kSaBytes + kSlots * 4 * kSwBytes + 4 * kEpiBytes;
 constexpr int kPersistentCap = 256;
 
-typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 // EPI: apply alpha * (...) + bias in the epilogue (a separate instance, so the
 // plain kernel's code is unchanged).
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
 
   uint8_t* const sa_lds = smem + kSlots * kRegion;                       // [slot][256] floats
   uint8_t* const sw_lds = sa_lds + kSlots * kSaBytes;                    // [slot][wave][64] floats
-  uint8_t* const epi = sw_lds + kSlots * 4 * kSwBytes + wave * kEpiBytes;
+  uint8_t* const epi = sw_lds + kSlots * 4 * kSwBytes + wave * kEpiBytes; // this wave's output staging
 
   // ---- load stream (see the file comment).  One buffer descriptor per operand
   // and tile covers the tile's valid rows; each load's per-lane offset (fixed
@@ -133,75 +135,99 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
     return here ? cur : nxt;   // by value: a select of the (scalar) fields
   };
 
-  // ---- fragments: 16x16x128 operands, lane row l % 16, chunks g4 and 4 + g4.
-  const int r16 = lane & 15, g4 = lane >> 4;
-  const int a_lo = swz128(wm * 128 + r16, g4), a_hi = swz128(wm * 128 + r16, 4 + g4);
-  const int w_lo = kAOp + swz128(wn * 64 + r16, g4), w_hi = kAOp + swz128(wn * 64 + r16, 4 + g4);
-  uint4 fa0[8][2], fw0[4][2], fa1[8][2], fw1[4][2];
-  float sc0[8], sc1[8];                              // s_a * s_w per 16-row block
-  // LDS reads of one region's fragment number idx (0..23: 16 A halves, then 8 W halves).
-  auto read_one = [&](uint4 (&fa)[8][2], uint4 (&fw)[4][2], const uint8_t* region, int idx)
+  // ---- fragments: 32x32x64 operands, lane row l % 32; slice h (bytes 64 h ..
+  // + 63 of the group) takes chunks 4 h + c and 4 h + 2 + c (c = l / 32) of the
+  // row, for A and W alike; rows + 32 i keep the swizzle.
+  const int r32 = lane & 31, c32 = lane >> 5;
+  int a_off[2][2], w_off[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      a_off[h][q] = swz128(wm * 128 + r32, 4 * h + 2 * q + c32);
+      w_off[h][q] = kAOp + swz128(wn * 64 + r32, 4 * h + 2 * q + c32);
+    }
+  uint4 fa0[4][2][2], fw0[2][2][2], fa1[4][2][2], fw1[2][2][2];   // [block][slice][chunk]
+  float sc0[4], sc1[4];                                          // s_a * s_w per 32-row block
+  // LDS read of one region's fragment number idx (0..23: 16 A, then 8 W).
+  auto read_one = [&](uint4 (&fa)[4][2][2], uint4 (&fw)[2][2][2], const uint8_t* region, int idx)
                       __attribute__((always_inline)) {
+    const int h = (idx >> 1) & 1, q = idx & 1;
     if (idx < 16) {
-      const int i = idx >> 1, q = idx & 1;
-      fa[i][q] = lds16(region + (q ? a_hi : a_lo) + i * 16 * kRow);
+      const int i = idx >> 2;
+      fa[i][h][q] = lds16(region + a_off[h][q] + i * 32 * kRow);
     } else {
-      const int j = (idx - 16) >> 1, q = idx & 1;
-      fw[j][q] = lds16(region + (q ? w_hi : w_lo) + j * 16 * kRow);
+      const int j = (idx - 16) >> 2;
+      fw[j][h][q] = lds16(region + w_off[h][q] + j * 32 * kRow);
     }
   };
-  auto read_scales = [&](float (&sc)[8], int slot) __attribute__((always_inline)) {
-    const float* sa = reinterpret_cast<const float*>(sa_lds + slot * kSaBytes) + wm * 128 + r16;
+  auto read_scales = [&](float (&sc)[4], int slot) __attribute__((always_inline)) {
+    const float* sa = reinterpret_cast<const float*>(sa_lds + slot * kSaBytes) + wm * 128 + r32;
     const float sw = reinterpret_cast<const float*>(sw_lds + (slot * 4 + wave) * kSwBytes)[lane];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sc[i] = sa[i * 16] * sw;
+    for (int i = 0; i < 4; ++i) sc[i] = sa[i * 32] * sw;
   };
-  auto read_all = [&](uint4 (&fa)[8][2], uint4 (&fw)[4][2], float (&sc)[8], int slot)
+  auto read_all = [&](uint4 (&fa)[4][2][2], uint4 (&fw)[2][2][2], float (&sc)[4], int slot)
                       __attribute__((always_inline)) {
 #pragma unroll
     for (int idx = 0; idx < 24; ++idx) read_one(fa, fw, smem + slot * kRegion, idx);
     read_scales(sc, slot);
   };
 
-  v4f_t acc[8][4];
+  v16f acc[4][2];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = v4f_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  };
+  // Partial products of the 32 x 32 blocks, alternating between two buffers.
+  v16f P[2];
+  // acc(block b) += P[b % 2] * s for elements 8 half .. + 7.
+  auto promote = [&](int b, int half, float s) __attribute__((always_inline)) {
+    const int i = b >> 1, j = b & 1;
+#pragma unroll
+    for (int e = 8 * half; e < 8 * half + 8; ++e) acc[i][j][e] = __builtin_fmaf(P[b & 1][e], s, acc[i][j][e]);
   };
 
-  // One region: 32 MFMAs (block (i, j) = slot 4 i + j); slot s also promotes
-  // the partial product of slot s - 2 (the MFMA result is ready by then), reads
-  // one fragment of the next region (slots 0..23) and issues one load of region
-  // lr + 3 (even slots 0..26).
-  auto region = [&](auto reads_c, const uint4 (&fa)[8][2], const uint4 (&fw)[4][2], const float (&sc)[8],
-                    uint4 (&na)[8][2], uint4 (&nw)[4][2], float (&nsc)[8], int R, int lr)
+  // One region: 16 MFMAs, block b = (i, j) = (b / 2, b % 2) takes slots 2 b
+  // (slice 0, from zero) and 2 b + 1 (slice 1, accumulating).  Block b is
+  // promoted over slots 2 b + 2 and 2 b + 3, behind the next block's MFMAs;
+  // the last block's promotion is carried into the next region's slots 0 and
+  // 1 (CARRY: with the previous region's scales, which are still in `nsc`), or
+  // done after the tile's last region (flush).  Slot s also reads fragments of
+  // the next region (A part s, and W part s for s < 8; a tile's last region
+  // reads the next tile's first one, which has landed too) and issues load
+  // part s (s < 14) of region lr + 3.
+  auto region = [&](auto carry_c, const uint4 (&fa)[4][2][2], const uint4 (&fw)[2][2][2], const float (&sc)[4],
+                    uint4 (&na)[4][2][2], uint4 (&nw)[2][2][2], float (&nsc)[4], int R, int lr)
                     __attribute__((always_inline)) {
-    constexpr bool reads = decltype(reads_c)::value;
+    constexpr bool carry = decltype(carry_c)::value;
     const uint8_t* next = smem + ((R + 1) % kSlots) * kRegion;
     const int load_slot = R % kSlots;
     int load_rg;
     const TileRsrc load_tr = region_src(lr + 3, load_rg);
-    v4f_t P[4];
 #pragma unroll
-    for (int s = 0; s < 34; ++s) {
-      if (s < 32) {
-        const int i = s >> 2, j = s & 3;
-        P[s & 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cat(fw[j][0], fw[j][1]), cat(fa[i][0], fa[i][1]),
-                                                                    v4f_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0,
-                                                                    127);
+    for (int s = 0; s < 16; ++s) {
+      const int b = s >> 1, h = s & 1, i = b >> 1, j = b & 1;
+      P[b & 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cat(fw[j][h][0], fw[j][h][1]),
+                                                                 cat(fa[i][h][0], fa[i][h][1]),
+                                                                 h ? P[b & 1] : v16f{}, 0, 0, 0, 127, 0, 127);
+      // In each slot the MFMA goes first, then the reads and the load (which
+      // cover the wait for the previous slot's result), then the FMAs.
+      __builtin_amdgcn_sched_barrier(0);
+      read_one(na, nw, next, s);
+      if (s < 8) read_one(na, nw, next, 16 + s);
+      if (s < kLoads) issue_part(load_tr, load_rg, load_slot, s);
+      __builtin_amdgcn_sched_barrier(0);
+      if (s < 2) {
+        if constexpr (carry) promote(7, s, nsc[3]);
+      } else {
+        promote((s - 2) >> 1, s & 1, sc[(s - 2) >> 2]);
       }
-      if (s >= 2) {
-        const int p = s - 2, i = p >> 2, j = p & 3;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(P[p & 3][e], sc[i], acc[i][j][e]);
-      }
-      if (reads && s < 24) read_one(na, nw, next, s);
-      if ((s & 1) == 0 && s < 2 * kLoads) issue_part(load_tr, load_rg, load_slot, s >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (reads) read_scales(nsc, (R + 1) % kSlots);
+    read_scales(nsc, (R + 1) % kSlots);
   };
   auto barrier_next = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(kLoads, 0));   // region R + 1 landed (R + 2 may be in flight)
@@ -209,71 +235,106 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- epilogue: per 16-row block i, the 4 column quads of each lane are staged
-  // in padded LDS rows, then written as whole 128-byte lines.
+  // ---- epilogue.  In block (i, j) lane (r, c) = (l % 32, l / 32) holds, per
+  // register quad rq, columns 8 rq + 4 c .. + 3 of row 32 i + r.  One
+  // v_permlane32_swap per packed dword trades quad 2 h + 1 of the lower half
+  // for quad 2 h of the upper half, after which the lane holds the 8
+  // consecutive columns 32 j + 16 h + 8 c .. + 7 (16 bytes).  Interior blocks
+  // are staged 16 rows at a time in padded LDS rows and written as whole
+  // 128-byte row segments (8 lanes per row), which keeps the number of cache
+  // lines per store instruction at 8 (the vector memory path also carries the
+  // operand stream); edge blocks (and C without 16-byte rows) store the pieces
+  // directly, masking rows past M and columns past N.
   auto epilogue = [&](int k) __attribute__((always_inline)) {
     int tm, tn;
     sched.coords(k, tm, tn);
     const int64_t m0 = (int64_t)tm * BM + wm * 128, n0 = (int64_t)tn * BN + wn * 64;
-    if constexpr (EPI) {   // N % 128 == 0, so every column exists
-      float b[4][4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint2 bw = uint2{0u, 0u};
-        if (g.bias) bw = *reinterpret_cast<const uint2*>(g.bias + n0 + j * 16 + g4 * 4);
-        b[j][0] = __uint_as_float(bw.x << 16);
-        b[j][1] = __uint_as_float(bw.x & 0xFFFF0000u);
-        b[j][2] = __uint_as_float(bw.y << 16);
-        b[j][3] = __uint_as_float(bw.y & 0xFFFF0000u);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(acc[i][j][e], g.alpha, b[j][e]);
-    }
     const bool interior = g.vec_store && m0 + 128 <= g.M && n0 + 64 <= g.N;   // wave-uniform
-    if (interior) {
-      const int rr = lane >> 3, rc = lane & 7;
-      uint8_t* wr = epi + r16 * kEpiRow + g4 * 8;
-      const uint8_t* rd = epi + rr * kEpiRow + rc * 16;
-      const uint32_t voff_c = (uint32_t)(rr * g.ldc * 2 + rc * 16);
+    const int el = fresh_lane();
+    const int fr = el & 31, fk = el >> 5;
+    const int rr = el >> 3, rc = el & 7;   // staged read-back: row rr (+ 8), 16-byte piece rc
+    const uint32_t voff_c = (uint32_t)(rr * g.ldc * 2 + rc * 16);
+    float bs[2][4][4];   // bias of the lane's columns (EPI; N % 128 == 0, so every column exists)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<uint2*>(wr + j * 32) =
-              uint2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const uint2 lo = *reinterpret_cast<const uint2*>(rd + q * 8 * kEpiRow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(rd + q * 8 * kEpiRow + 8);
-          char* base = reinterpret_cast<char*>(g.c + (m0 + i * 16 + 8 * q) * g.ldc + n0);
-          *reinterpret_cast<uint4*>(base + voff_c) = uint4{lo.x, lo.y, hi.x, hi.y};
+      for (int rq = 0; rq < 4; ++rq) {
+        uint2 bw = uint2{0u, 0u};
+        if constexpr (EPI) {
+          if (g.bias) bw = *reinterpret_cast<const uint2*>(g.bias + n0 + j * 32 + rq * 8 + fk * 4);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        bs[j][rq][0] = __uint_as_float(bw.x << 16);
+        bs[j][rq][1] = __uint_as_float(bw.x & 0xFFFF0000u);
+        bs[j][rq][2] = __uint_as_float(bw.y << 16);
+        bs[j][rq][3] = __uint_as_float(bw.y & 0xFFFF0000u);
       }
-      return;
-    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t row = m0 + i * 16 + r16;
-      if (row >= g.M) continue;
-      uint16_t* dst_row = g.c + row * g.ldc;
+    for (int i = 0; i < 4; ++i) {
+      uint4 u[2][2];   // [j][h]
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = n0 + j * 16 + g4 * 4;
-        const uint32_t lo = pack_bf16x2(acc[i][j][0], acc[i][j][1]), hi = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-        if (g.vec_store && col + 4 <= g.N) {
-          *reinterpret_cast<uint2*>(dst_row + col) = uint2{lo, hi};
-        } else {
-          const uint16_t e[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+      for (int j = 0; j < 2; ++j) {
+        float v[16];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (col + c < g.N) dst_row[col + c] = e[c];
+        for (int e = 0; e < 16; ++e)
+          v[e] = EPI ? __builtin_fmaf(acc[i][j][e], g.alpha, bs[j][e >> 2][e & 3]) : acc[i][j][e];
+        uint32_t d[4][2];
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          d[rq][0] = pack_bf16x2(v[4 * rq + 0], v[4 * rq + 1]);
+          d[rq][1] = pack_bf16x2(v[4 * rq + 2], v[4 * rq + 3]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const auto s0 = __builtin_amdgcn_permlane32_swap(d[2 * h][0], d[2 * h + 1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(d[2 * h][1], d[2 * h + 1][1], false, false);
+          u[j][h] = uint4{s0[0], s1[0], s0[1], s1[1]};
         }
       }
+      if (interior) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {   // rows 16 p .. + 15 of the block
+          if ((fr >> 4) == p) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                *reinterpret_cast<uint4*>(epi + (fr & 15) * kEpiRow + (j * 32 + h * 16 + 8 * fk) * 2) = u[j][h];
+          }
+          // The rows pass between lanes of the wave (LDS runs one wave's
+          // accesses in order): the compiler must neither reuse the previous
+          // pass's reads for lanes that did not write nor move the next pass's
+          // writes above these reads.
+          asm volatile("" ::: "memory");
+          uint4 w[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) w[q] = lds16(epi + (rr + 8 * q) * kEpiRow + rc * 16);
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            char* base = reinterpret_cast<char*>(g.c + (m0 + i * 32 + 16 * p + 8 * q) * g.ldc + n0);
+            *reinterpret_cast<uint4*>(base + voff_c) = w[q];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int64_t row = m0 + i * 32 + fr, col = n0 + j * 32 + h * 16 + 8 * fk;
+            if (row < g.M) {
+              uint16_t* dst = g.c + row * g.ldc + col;
+              if (g.vec_store && col + 8 <= g.N) {
+                *reinterpret_cast<uint4*>(dst) = u[j][h];
+              } else {
+                const uint32_t wds[4] = {u[j][h].x, u[j][h].y, u[j][h].z, u[j][h].w};
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                  if (col + c < g.N) dst[c] = (uint16_t)(wds[c >> 1] >> (16 * (c & 1)));
+              }
+            }
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one accumulator block at a time
     }
   };
 
@@ -290,36 +351,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
   __builtin_amdgcn_sched_barrier(0);
   read_all(fa0, fw0, sc0, 0);
 
-  // ---- the stream.  R counts regions over all tiles; sets 0 / 1 alternate per
-  // region (pairs of regions per loop trip; G may be odd, then the tile's last
-  // region is handled on its own).
-  using RD = std::true_type;
-  using NORD = std::false_type;
+  // ---- the stream.  R counts regions over all tiles.  A tile's first region
+  // uses register set 0 and carries nothing in; the sets then alternate (pairs
+  // of regions per loop trip), and the last block of the tile's last region is
+  // promoted after it, with that region's scales.  (The tail has no code of
+  // its own that repeats a region: identical MFMA chains on both sides of a
+  // branch get hoisted above it, all live at once.)
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   int R = 0;
   for (int k = 0; k < my_tiles; ++k) {
     zero_acc();
-    int r = 0;
-    // Regions r, r + 1 with set 0 then set 1, while at least one more follows.
-    for (; r + 2 < G; r += 2) {
+    barrier_next();
+    region(F_{}, fa0, fw0, sc0, fa1, fw1, sc1, R, 0);
+    ++R;
+    int r = 1;
+    for (; r + 1 < G; r += 2) {
       barrier_next();
-      region(RD{}, fa0, fw0, sc0, fa1, fw1, sc1, R, r);
+      region(T_{}, fa1, fw1, sc1, fa0, fw0, sc0, R, r);
       ++R;
       barrier_next();
-      region(RD{}, fa1, fw1, sc1, fa0, fw0, sc0, R, r + 1);
-      ++R;
-    }
-    if (r + 1 < G) {   // two regions left: the second ends the tile
-      barrier_next();
-      region(RD{}, fa0, fw0, sc0, fa1, fw1, sc1, R, r);
-      ++R;
-      barrier_next();
-      region(NORD{}, fa1, fw1, sc1, fa0, fw0, sc0, R, r + 1);
-      ++R;
-    } else {           // one region left
-      barrier_next();
-      region(NORD{}, fa0, fw0, sc0, fa1, fw1, sc1, R, r);
+      region(T_{}, fa0, fw0, sc0, fa1, fw1, sc1, R, r + 1);
       ++R;
     }
+    if (r < G) {   // G even: region G - 1 runs on set 1
+      barrier_next();
+      region(T_{}, fa1, fw1, sc1, fa0, fw0, sc0, R, r);
+      ++R;
+    }
+    const float s_last = (G & 1) ? sc0[3] : sc1[3];
+    promote(7, 0, s_last);
+    promote(7, 1, s_last);
     epilogue(k);
     // The next tile starts with set 0: its first region's fragments and scales
     // (complete: the last barrier waited for region R).

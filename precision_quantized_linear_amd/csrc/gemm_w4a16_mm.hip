@@ -321,6 +321,10 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
             uint2{pack_bf16x2(v[4 * rq + 0], v[4 * rq + 1]), pack_bf16x2(v[4 * rq + 2], v[4 * rq + 3])};
       }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    // Rows pass between lanes of the wave: no compiler reordering or reuse of
+    // LDS accesses across the exchange (the hardware keeps one wave's LDS
+    // accesses in order).
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint8_t* src = stg + (q * 8 + rr) * kEpiRow + rc * 16;   // 8-byte aligned (136-byte rows)
@@ -342,6 +346,7 @@ __global__ __launch_bounds__(512, 1) void k_w4a16_mm(const uint16_t* __restrict_
       }
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));   // staging block read before it is rewritten
+    asm volatile("" ::: "memory");
   }
 }
 
