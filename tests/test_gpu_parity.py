@@ -101,7 +101,7 @@ def test_quantize_bit_exact(scheme, role, rows, cols):
 
 
 @pytest.mark.parametrize("M,N,K", [(257, 388, 384), (1000, 260, 640), (512, 1024, 256), (130, 390, 384),
-                                   (2304, 4100, 256), (300, 4100, 512)])
+                                   (2304, 4100, 256), (300, 4100, 512), (200, 8300, 384), (256, 8448, 256)])
 def test_w4a16_gemm_tile_shapes(M, N, K):
     # ragged M and N tails across several 256 x 64 tiles (few tiles) and 256 x 128
     # tiles (2304 x 4100: more than 128 of them), an odd number of K-groups, and
