@@ -18,7 +18,8 @@
 // C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4] for r = 0..15: one row per
 // lane (one activation scale per 32-row block) and four quads of consecutive
 // columns; the weight scale is uniform over the tile.  Each block's 16
-// promotion FMAs run behind the next block's two 64-cycle MFMAs.
+// promotion FMAs are issued after the next block's MFMAs, by which time the
+// block's own result is complete.
 //
 // Pipeline: one 128-byte K-group per "region"; LDS holds three regions
 // (A 256 rows + W 128 rows of 128 bytes, the A scales of the group, and the W
