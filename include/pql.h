@@ -131,7 +131,10 @@ const char* pql_last_error(void);
  * W4A16).  Size outputs are host pointers; any may be NULL.
  * Errors: INVALID_ARGUMENT for negative sizes or cols / rows that the scheme
  * cannot block (cols % 32 for FP8 tensor/row, INT8_ROW and MX, cols % 128 for
- * FP8_BLOCK128 and W4A16, rows % 128 for FP8_BLOCK128 weights);
+ * FP8_BLOCK128 and W4A16, rows % 128 for FP8_BLOCK128 weights), and for
+ * cols > 2^20, rows > 2^31 - 1 or rows * cols > 2^40 (the same limits hold for
+ * every quantize and dequantize call; GEMMs take K <= 2^20, M, N <= 2^30 and
+ * at most 2^31 - 1 output tiles of 64 x 64);
  * UNSUPPORTED for W4A16 activations or an unknown scheme / role. */
 pql_status pql_quantized_sizes(int scheme, int role, int64_t rows, int64_t cols,
                                size_t* codes_bytes, size_t* scales_bytes,

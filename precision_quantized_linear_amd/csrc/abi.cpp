@@ -79,6 +79,10 @@ pql_status check_shape(int scheme, int role, int64_t rows, int64_t cols) {
     return fail(PQL_ERR_INVALID_ARGUMENT, "FP8_BLOCK128 weights need rows %% 128 == 0 (got %lld)", (long long)rows);
   if (cols > (int64_t(1) << 20)) return fail(PQL_ERR_INVALID_ARGUMENT, "cols above 2^20 is not supported");
   if (rows > (int64_t(1) << 31) - 1) return fail(PQL_ERR_INVALID_ARGUMENT, "rows above 2^31-1 is not supported");
+  // Launch grids are counted in 32-bit integers; 2^40 elements (2 TiB of bf16)
+  // is far beyond any device's memory.
+  if (rows > ((int64_t(1) << 40) / cols))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "a %lld x %lld tensor is too large", (long long)rows, (long long)cols);
   return PQL_OK;
 }
 
@@ -195,6 +199,10 @@ pql_status check_gemm_shape(int scheme, int64_t M, int64_t N, int64_t K) {
   if (K > (int64_t(1) << 20)) return fail(PQL_ERR_INVALID_ARGUMENT, "K above 2^20 is not supported");
   if (M > (int64_t(1) << 30) || N > (int64_t(1) << 30))
     return fail(PQL_ERR_INVALID_ARGUMENT, "M and N above 2^30 are not supported");
+  // The launchers count output tiles (at least 64 x 64 elements each) in 32-bit
+  // integers; an output with more tiles could not be allocated anyway.
+  if (((M + 63) / 64) * ((N + 63) / 64) > (int64_t(1) << 31) - 1)
+    return fail(PQL_ERR_INVALID_ARGUMENT, "an M x N output of %lld x %lld is too large", (long long)M, (long long)N);
   if (scheme == PQL_FP8_BLOCK128 && N % 128)
     return fail(PQL_ERR_INVALID_ARGUMENT, "FP8_BLOCK128 needs N %% 128 == 0 (got %lld)", (long long)N);
   return PQL_OK;

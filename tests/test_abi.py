@@ -59,6 +59,7 @@ def test_quantized_sizes():
     ("w4a16_asym", "weight", 4, 64),
     ("fp8_row", "activation", -1, 64),
     ("fp8_row", "activation", 4, 0),
+    ("fp8_block128", "weight", (1 << 31) - 128, 1 << 20),   # 2^51 elements
 ])
 def test_invalid_shapes_rejected(scheme, role, rows, cols):
     with pytest.raises(ValueError):
@@ -152,6 +153,7 @@ def test_qgemm_validation():
     assert g(a=_p(8)) == pql.PQL_ERR_INVALID_ARGUMENT
     assert g(scheme=11) == pql.PQL_ERR_UNSUPPORTED
     assert g(scheme=S["w4a16_asym"], wz=_p(4100)) == pql.PQL_ERR_INVALID_ARGUMENT   # misaligned zero-points
+    assert g(M=1 << 30, N=1 << 30, ldc=1 << 30) == pql.PQL_ERR_INVALID_ARGUMENT      # 2^48 output tiles
     assert g(M=0) == pql.PQL_OK
 
 
