@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpql.so")
-SOURCES = ("abi.cpp", "quant.hip", "gemm.hip", "gemm32.hip", "gemm_block.hip", "gemm_w4a16.hip",
+SOURCES = ("abi.cpp", "quant.hip", "gemm.hip", "gemm32.hip", "gemm_block.hip", "gemm_block256.hip", "gemm_w4a16.hip",
            "gemm_w4a16_mm.hip")
 ARCH = "gfx950"
 
@@ -41,7 +41,8 @@ def compile_flags():
 # Per-file code-generation options.  The block-128 GEMM promotes every matrix-core
 # partial product with VALU FMAs; taking the MFMA results in VGPRs (instead of
 # AGPRs) spares one v_accvgpr_read per element.
-EXTRA_FLAGS = {"gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"gemm_block.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "gemm_block256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -305,10 +305,10 @@ hipError_t launch_gemm(GemmKind kind, const GemmArgs& g, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-const char* gemm_kernel_name(GemmKind kind, int64_t, int64_t, int64_t K) {
+const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K) {
   switch (kind) {
     case GEMM_FP8_ROWSCALE: return "k_gemm32_fp8";
-    case GEMM_FP8_BLOCK: return "k_gemm_block";
+    case GEMM_FP8_BLOCK: return gemm_block_uses_256(M, N) ? "k_gemm_block256" : "k_gemm_block";
     case GEMM_MXFP8: return "k_gemm32<mxfp8>";
     case GEMM_MXFP4: return K % 256 == 0 ? "k_gemm32<mxfp4>" : "k_gemm<mxfp4>_256x256x256";
     case GEMM_INT8_ROW: return "k_gemm32<int8>";

@@ -1,4 +1,5 @@
-// Persistent FP8 block-128 GEMM, gfx950.
+// Persistent FP8 block-128 GEMM, gfx950.  Outputs with at least 256 tiles of
+// 256 x 256 run the 8-wave kernel of gemm_block256.hip instead.
 //
 // C[m, n] = bf16( sum_g s_a[m, g] * s_w[n / 128, g] * sum_{k in group g} qa[m, k] qw[n, k] )
 // ("[vLLM] Other quantization: FP8, ModelOpt, INC, TorchAO, Quark", section
@@ -396,6 +397,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
 }  // namespace
 
 hipError_t launch_gemm_block(const GemmArgs& g, hipStream_t st) {
+  if (gemm_block_uses_256(g.M, g.N)) return launch_gemm_block256(g, st);
   const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
   // The stream loads three regions ahead; when a tile has fewer than three
   // K-groups those loads would reach past the next tile, so short K gets one

@@ -74,6 +74,10 @@ hipError_t launch_gemm32_mx(bool fp4, const GemmArgs& g, hipStream_t st);
 hipError_t launch_gemm32_int8(const GemmArgs& g, hipStream_t st);
 // Persistent FP8 block-128 kernel (16x16x128 MFMA per K-group, FMA promotion; N % 128 == 0).
 hipError_t launch_gemm_block(const GemmArgs& g, hipStream_t st);
+// The block-128 GEMM runs 256 x 256 tiles on 8 waves when they fill at least
+// one round of the 256 CUs, else 256 x 128 tiles on 4 waves.
+inline bool gemm_block_uses_256(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256) >= 256; }
+hipError_t launch_gemm_block256(const GemmArgs& g, hipStream_t st);
 const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);
 
 // W4A16: C = A (bf16) * dequant(Wq)^T

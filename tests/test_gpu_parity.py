@@ -184,6 +184,22 @@ def test_qgemm_multi_tile_workgroups(scheme):
     assert err <= 5e-3
 
 
+# The block-128 GEMM's two kernels: 256 x 128 tiles on 4 waves (here 272 tiles,
+# so some workgroups walk two), and 256 x 256 tiles on 8 waves once those fill
+# a round of the CUs (here 289, with a ragged M tail and a last tile column
+# half past N, whose waves take the last weight-scale block).
+@pytest.mark.parametrize("M,N,K,kernel", [(4300, 2048, 640, "k_gemm_block"), (4300, 4224, 384, "k_gemm_block256"),
+                                          (4096, 4096, 128, "k_gemm_block256")])
+def test_block128_kernels(M, N, K, kernel):
+    assert pql.kernel_name("qgemm", "fp8_block128", "activation", M, N, K) == kernel
+    a = wl.small_case(7300 + M, M, K, 1.0)
+    w = wl.small_case(7400 + N, N, K, 0.02)
+    aq, wq = oracle.quantize(a, "fp8_block128", "activation"), oracle.quantize(w, "fp8_block128", "weight")
+    c = pql.qgemm(pql.from_numpy(aq, DEV), pql.from_numpy(wq, DEV))
+    err = oracle.rel_fro_error(F.bf16_to_f32(down_bf16(c)).astype(np.float64), oracle.gemm_ref(aq, wq))
+    assert err <= TOL and err <= 5e-3, f"{M}x{N}x{K}: rel err {err:.3e}"
+
+
 @pytest.mark.parametrize("M", [1, 5, 16, 33, 64, 65, 300])
 @pytest.mark.parametrize("sym", [False, True])
 def test_w4a16_gemm_matches_oracle(M, sym):
