@@ -38,4 +38,4 @@ from .formats import (  # noqa: F401
 from .quant import (  # noqa: F401
     SCHEMES, STATIC_SCHEMES, quantize, quantize_static, dequantize, dequant_exact, mx_exponent,
 )
-from .gemm import gemm_ref, gemm_ref_entries, rel_fro_error  # noqa: F401
+from .gemm import gemm_abs_ref, gemm_ref, gemm_ref_entries, rel_fro_error  # noqa: F401

@@ -70,6 +70,23 @@ def gemm_ref_entries(a, w_q: dict, rows, cols, alpha=None, bias=None) -> np.ndar
     return _epilogue(A @ W.T, alpha, bias, cols)
 
 
+def gemm_abs_ref(a, w_q: dict, alpha=None) -> np.ndarray:
+    """float64 T[M, N] = |alpha| * (|A_hat| @ |W_hat|^T): for each output, the sum of
+    the magnitudes of the K products the GEMM adds up.
+
+    Rounding-error analysis of any summation of those products is stated in
+    terms of this sum (a sum of n terms carried in a format with unit roundoff
+    u is off by at most about n * u * T), so it is what a per-element
+    tolerance on C is measured against.
+    """
+    A = np.abs(_a_hat(a))
+    W = np.abs(dequant_exact(w_q))
+    if A.shape[1] != W.shape[1]:
+        raise ValueError("K mismatch")
+    t = A @ W.T
+    return abs(float(np.float32(alpha))) * t if alpha is not None else t
+
+
 def rel_fro_error(c_test, c_ref) -> float:
     """||c_test - c_ref||_F / ||c_ref||_F in float64."""
     c_test = np.asarray(c_test, dtype=np.float64)

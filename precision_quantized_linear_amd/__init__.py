@@ -182,8 +182,11 @@ def quantize(x: torch.Tensor, scheme: str, role: str = "activation", workspace: 
     x = _as_2d_bf16(x)
     rows, cols = x.shape
     if out is not None:
+        _check_qtensor(out, "out")
         if (out.scheme, out.role, out.rows, out.cols) != (scheme, role, rows, cols):
             raise ValueError("out does not match the scheme, role and shape")
+        if out.device != x.device:
+            raise ValueError(f"out is on {out.device}, x on {x.device}")
         q = out
     else:
         q = _alloc_q(scheme, role, rows, cols, x.device)
@@ -224,10 +227,43 @@ def _bias_ptr(bias, n: int, device):
     return bias.data_ptr()
 
 
+def _check_out(out: torch.Tensor, rows: int, cols: int, device, what: str = "out") -> None:
+    """The C ABI sees only a pointer and a row stride, so the binding checks the rest:
+    a bf16 [rows, cols] view on ``device`` with unit column stride and a row stride of
+    at least ``cols`` (a view into a wider buffer is fine)."""
+    if not isinstance(out, torch.Tensor):
+        raise ValueError(f"{what} must be a torch tensor")
+    if out.dtype != torch.bfloat16:
+        raise ValueError(f"{what} must be bfloat16, not {out.dtype}")
+    if out.dim() != 2 or tuple(out.shape) != (rows, cols):
+        raise ValueError(f"{what} must have shape ({rows}, {cols}), not {tuple(out.shape)}")
+    if rows and (out.stride(1) != 1 or out.stride(0) < cols):
+        raise ValueError(f"{what} needs unit column stride and a row stride >= {cols} "
+                         f"(strides {tuple(out.stride())})")
+    if out.device != torch.device(device):
+        raise ValueError(f"{what} is on {out.device}, the operands on {device}")
+
+
+def _check_qtensor(q: QTensor, what: str) -> None:
+    if not isinstance(q, QTensor):
+        raise ValueError(f"{what} must be a QTensor")
+    bufs = [q.codes, q.scales] + ([q.zeros] if q.zeros is not None else [])
+    if any(b.device != q.codes.device for b in bufs):
+        raise ValueError(f"{what}: codes, scales and zero-points must be on one device")
+
+
+def _on_device(device) -> None:
+    if torch.device(device).type != "cuda":
+        raise ValueError(f"operands must be on a HIP device, not {device}")
+
+
 def dequantize(q: QTensor, out: torch.Tensor | None = None) -> torch.Tensor:
     """bf16 [rows, cols] = bf16(decode(code) * scale)."""
+    _check_qtensor(q, "q")
     if out is None:
         out = torch.empty((q.rows, q.cols), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, q.rows, q.cols, q.device)
+    _on_device(q.device)
     _check(lib().pql_dequantize(_scheme(q.scheme), _role(q.role), q.codes.data_ptr(), q.scales.data_ptr(),
                                 _ptr(q.zeros), q.rows, q.cols, out.data_ptr(), out.stride(0),
                                 _stream(q.device)), "dequantize")
@@ -239,15 +275,27 @@ def qgemm(a, w: QTensor, out: torch.Tensor | None = None, alpha: float = 1.0,
     """C[M, N] = alpha * (A_hat * W_hat^T) + bias on quantized operands (W4A16: ``a`` is the
     bf16 activation).  ``alpha`` and ``bias`` (bf16 [N]) are the fused epilogue of the FP8
     and int8 schemes."""
+    _check_qtensor(w, "w")
     if w.role != "weight":
         raise ValueError("the second operand must be a quantized weight")
     if isinstance(a, QTensor):
+        _check_qtensor(a, "a")
+        if a.role != "activation":
+            raise ValueError("the first operand must be a quantized activation")
         if a.scheme != w.scheme:
             raise ValueError("activation and weight schemes differ")
+        if w.scheme.startswith("w4a16"):
+            raise ValueError("W4A16 takes the bf16 activation itself, not a quantized one")
+        if a.device != w.device:
+            raise ValueError(f"activation on {a.device}, weight on {w.device}")
         M, K = a.rows, a.cols
         a_ptr, as_ptr = a.codes.data_ptr(), a.scales.data_ptr()
     else:
+        if not w.scheme.startswith("w4a16"):
+            raise ValueError(f"{w.scheme} needs a quantized activation (pql.quantize(x, scheme, 'activation'))")
         a = _as_2d_bf16(a)
+        if a.device != w.device:
+            raise ValueError(f"activation on {a.device}, weight on {w.device}")
         if a.stride(0) != a.shape[1]:
             a = a.contiguous()
         M, K = a.shape
@@ -256,6 +304,8 @@ def qgemm(a, w: QTensor, out: torch.Tensor | None = None, alpha: float = 1.0,
         raise ValueError(f"K mismatch: {K} vs {w.cols}")
     if out is None:
         out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=w.device)
+    _check_out(out, M, w.rows, w.device)
+    _on_device(w.device)
     _check(lib().pql_qgemm_ex(_scheme(w.scheme), a_ptr, as_ptr, w.codes.data_ptr(), w.scales.data_ptr(),
                               _ptr(w.zeros), M, w.rows, K, float(alpha), _bias_ptr(bias, w.rows, w.device),
                               out.data_ptr(), out.stride(0), _stream(w.device)), "qgemm")
@@ -267,9 +317,12 @@ def qlinear(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None,
             act_scales: torch.Tensor | None = None) -> torch.Tensor:
     """The quantized linear layer's forward: flatten x[..., K] to 2-D, quantize it with the
     weight's scheme (activation rule), GEMM against ``w``, restore the leading shape.
+    ``out``, if given, is the 2-D [M, N] bf16 output (a view with a wider row stride is
+    accepted).
     ``alpha`` / ``bias`` are the fused epilogue; ``act_scales`` (fp32, the scheme's
     activation scale layout) makes the activation scales static (fp8_tensor and
     fp8_block128)."""
+    _check_qtensor(w, "w")
     if w.role != "weight":
         raise ValueError("w must be a quantized weight")
     lead = x.shape[:-1]
@@ -280,18 +333,30 @@ def qlinear(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None,
     M, K = x2.shape
     if K != w.cols:
         raise ValueError(f"K mismatch: {K} vs {w.cols}")
+    if x2.device != w.device:
+        raise ValueError(f"input on {x2.device}, weight on {w.device}")
     if out is None:
         out = torch.empty((M, w.rows), dtype=torch.bfloat16, device=x.device)
+    _check_out(out, M, w.rows, w.device)
+    if act_scales is not None:
+        if w.scheme not in STATIC_SCHEMES:
+            raise NotImplementedError(f"static activation scales are defined for {STATIC_SCHEMES} only")
+        want = 1 if w.scheme == "fp8_tensor" else M * (K // 128)
+        if (act_scales.dtype != torch.float32 or not act_scales.is_contiguous()
+                or act_scales.device != x2.device):
+            raise ValueError("act_scales must be a contiguous float32 tensor on the input's device")
+        if act_scales.numel() != want:
+            raise ValueError(f"{w.scheme} takes {want} activation scales, got {act_scales.numel()}")
     wsb = workspace_size("qlinear", w.scheme, "activation", M, w.rows, K)
     if wsb and workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
-    if act_scales is not None and (act_scales.dtype != torch.float32 or not act_scales.is_contiguous()
-                                   or act_scales.device != x.device):
-        raise ValueError("act_scales must be a contiguous float32 tensor on the input's device")
+    if workspace is not None and (workspace.device != x2.device or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on the input's device")
+    _on_device(w.device)
     _check(lib().pql_qlinear_ex(_scheme(w.scheme), x2.data_ptr(), M, K, x2.stride(0), _ptr(act_scales),
                                 w.codes.data_ptr(), w.scales.data_ptr(), _ptr(w.zeros), w.rows, float(alpha),
                                 _bias_ptr(bias, w.rows, x.device), out.data_ptr(), out.stride(0),
-                                _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
                                 _stream(x.device)), "qlinear")
     return out.reshape(*lead, w.rows)
 

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block(GemmArgs g) {
     const int el = fresh_lane();
     const int fr = el & 31, fk = el >> 5;
     const int rr = el >> 3, rc = el & 7;   // staged read-back: row rr (+ 8), 16-byte piece rc
-    const uint32_t voff_c = (uint32_t)(rr * g.ldc * 2 + rc * 16);
+    const int64_t voff_c = (int64_t)rr * g.ldc * 2 + rc * 16;   // bytes; 64-bit for any ldc
     float bs[2][4][4];   // bias of the lane's columns (EPI; N % 128 == 0, so every column exists)
 #pragma unroll
     for (int j = 0; j < 2; ++j)

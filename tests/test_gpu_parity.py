@@ -4,10 +4,15 @@
 * Dequantized bf16 must match bit for bit.
 * GEMM outputs, given identical quantized inputs, must satisfy
   ||C_gpu - C_oracle||_F / ||C_oracle||_F <= 1e-2 (the tolerance the
-  quantized-linear target states); the oracle is the exact float64 product.
+  quantized-linear target states) and, element by element, the bound of
+  tests/gemm_check.py (bf16 output rounding plus the worst case of fp32
+  accumulation); the oracle is the exact float64 product.  The operands are
+  scaled by powers of two per row / K-block / weight block so that a scale
+  taken from a neighbouring block is off by at least 2x.
 Small cases span several 256x256 tiles with ragged M / N tails; the full-size
 workloads (the shapes the benchmark times) are checked on sampled rows and
-sampled output entries, which the oracle computes one by one.
+columns covering every 256 x 256 output tile, which the oracle computes one
+by one.  tests/test_gpu_exact.py adds bit-exact GEMM checks of every element.
 """
 import numpy as np
 import pytest
@@ -16,6 +21,7 @@ import torch
 import oracle
 import precision_quantized_linear_amd as pql
 import workloads as wl
+from gemm_check import assert_gemm, check_gemm, tile_sample, w4a16_terms
 from oracle import formats as F
 
 pytestmark = pytest.mark.gpu
@@ -110,13 +116,11 @@ def test_w4a16_gemm_tile_shapes(M, N, K):
     if N % 4 == 0:
         assert pql.kernel_name("qgemm", "w4a16_asym", "activation", M, N, K) == \
             ("k_w4a16_mm_256x64x64" if narrow else "k_w4a16_mm_256x128x64")
-    a = wl.small_case(5000 + M, M, K, 1.0)
-    w = wl.small_case(6000 + N, N, K, 0.02)
+    a = wl.pow2_blocks(wl.small_case(5000 + M, M, K, 1.0), M, 1, 128)
+    w = wl.pow2_blocks(wl.small_case(6000 + N, N, K, 0.02), N, 1, 128)
     wq = oracle.quantize(w, "w4a16_asym", "weight")
     c = pql.qgemm(up(a), pql.from_numpy(wq, DEV))
-    err = oracle.rel_fro_error(F.bf16_to_f32(down_bf16(c)), oracle.gemm_ref(a, wq))
-    assert err <= TOL, f"{M}x{N}x{K}: rel err {err:.3e}"
-    assert err <= 5e-3
+    assert_gemm(down_bf16(c), a, wq, f"{M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("scheme", FP_SCHEMES + ("w4a16_asym",))
@@ -154,17 +158,20 @@ def test_dequantize_bit_exact(scheme, role):
 GEMM_SHAPES = [(1, 256, 128), (77, 384, 256), (256, 256, 640), (300, 640, 1152), (513, 128, 384)]
 
 
+def _gemm_operands(scheme, M, N, K, seed):
+    """Seeded operands, scaled by powers of two per row and 32-block (activation) and
+    per 128 x 128 block (weight), quantized by the oracle."""
+    a = wl.pow2_blocks(wl.small_case(seed + M, M, K, 1.0), seed, 1, 32)
+    w = wl.pow2_blocks(wl.small_case(seed + 1 + N, N, K, 0.02), seed + 1, 128 if scheme == "fp8_block128" else 1, 128)
+    return oracle.quantize(a, scheme, "activation"), oracle.quantize(w, scheme, "weight")
+
+
 @pytest.mark.parametrize("scheme", FP_SCHEMES)
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 def test_qgemm_matches_oracle(scheme, M, N, K):
-    a = wl.small_case(1000 + M, M, K, 1.0)
-    w = wl.small_case(2000 + N, N, K, 0.02)
-    aq, wq = oracle.quantize(a, scheme, "activation"), oracle.quantize(w, scheme, "weight")
+    aq, wq = _gemm_operands(scheme, M, N, K, 1000)
     c = pql.qgemm(pql.from_numpy(aq, DEV), pql.from_numpy(wq, DEV))
-    c_gpu = F.bf16_to_f32(down_bf16(c)).astype(np.float64)
-    err = oracle.rel_fro_error(c_gpu, oracle.gemm_ref(aq, wq))
-    assert err <= TOL, f"{scheme} {M}x{N}x{K}: rel err {err:.3e}"
-    assert err <= 5e-3   # expected ~2^-9 from the bf16 output rounding; flags a drift early
+    assert_gemm(down_bf16(c), aq, wq, f"{scheme} {M}x{N}x{K}")
 
 
 # More output tiles than the 256 persistent workgroups, so some workgroups walk
@@ -173,15 +180,10 @@ def test_qgemm_matches_oracle(scheme, M, N, K):
 # a multiple of 256 so MXFP4 runs its region-pipelined kernel too.
 @pytest.mark.parametrize("scheme", FP_SCHEMES)
 def test_qgemm_multi_tile_workgroups(scheme):
-    M, N, K = 4300, 4200, 512
-    a = wl.small_case(7100, M, K, 1.0)
-    w = wl.small_case(7200, N if scheme != "fp8_block128" else 4224, K, 0.02)
-    aq, wq = oracle.quantize(a, scheme, "activation"), oracle.quantize(w, scheme, "weight")
+    M, N, K = 4300, 4200 if scheme != "fp8_block128" else 4224, 512
+    aq, wq = _gemm_operands(scheme, M, N, K, 7100)
     c = pql.qgemm(pql.from_numpy(aq, DEV), pql.from_numpy(wq, DEV))
-    c_gpu = F.bf16_to_f32(down_bf16(c)).astype(np.float64)
-    err = oracle.rel_fro_error(c_gpu, oracle.gemm_ref(aq, wq))
-    assert err <= TOL, f"{scheme}: rel err {err:.3e}"
-    assert err <= 5e-3
+    assert_gemm(down_bf16(c), aq, wq, f"{scheme} {M}x{N}x{K}")
 
 
 # The block-128 GEMM's two kernels: 256 x 128 tiles on 4 waves (here 272 tiles,
@@ -192,24 +194,20 @@ def test_qgemm_multi_tile_workgroups(scheme):
                                           (4096, 4096, 128, "k_gemm_block256")])
 def test_block128_kernels(M, N, K, kernel):
     assert pql.kernel_name("qgemm", "fp8_block128", "activation", M, N, K) == kernel
-    a = wl.small_case(7300 + M, M, K, 1.0)
-    w = wl.small_case(7400 + N, N, K, 0.02)
-    aq, wq = oracle.quantize(a, "fp8_block128", "activation"), oracle.quantize(w, "fp8_block128", "weight")
+    aq, wq = _gemm_operands("fp8_block128", M, N, K, 7300)
     c = pql.qgemm(pql.from_numpy(aq, DEV), pql.from_numpy(wq, DEV))
-    err = oracle.rel_fro_error(F.bf16_to_f32(down_bf16(c)).astype(np.float64), oracle.gemm_ref(aq, wq))
-    assert err <= TOL and err <= 5e-3, f"{M}x{N}x{K}: rel err {err:.3e}"
+    assert_gemm(down_bf16(c), aq, wq, f"{M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("M", [1, 5, 16, 33, 64, 65, 300])
 @pytest.mark.parametrize("sym", [False, True])
 def test_w4a16_gemm_matches_oracle(M, sym):
     N, K = 384, 1152
-    a = wl.small_case(3000 + M, M, K, 1.0)
-    w = wl.small_case(4000, N, K, 0.02)
+    a = wl.pow2_blocks(wl.small_case(3000 + M, M, K, 1.0), M, 1, 128)
+    w = wl.pow2_blocks(wl.small_case(4000, N, K, 0.02), 7, 1, 128)
     wq = oracle.quantize(w, "w4a16_sym" if sym else "w4a16_asym", "weight")
     c = pql.qgemm(up(a), pql.from_numpy(wq, DEV))
-    err = oracle.rel_fro_error(F.bf16_to_f32(down_bf16(c)), oracle.gemm_ref(a, wq))
-    assert err <= TOL, f"M={M}: rel err {err:.3e}"
+    assert_gemm(down_bf16(c), a, wq, f"M={M}")
 
 
 @pytest.mark.parametrize("scheme", FP_SCHEMES + ("w4a16_asym",))
@@ -261,14 +259,6 @@ def _take(q_np: dict, rows: np.ndarray, role: str) -> dict:
     return out
 
 
-def _expand_block_rows(q: dict) -> dict:
-    """A row subset of a 128x128-block weight as a dict the oracle can dequantize:
-    repeat the block scale per row and relabel it as a per-(row, group) scale."""
-    q = dict(q)
-    q["role"] = "activation"
-    return q
-
-
 def _check_rows(xbits, q_gpu_np, scheme, role, rows):
     if scheme == "fp8_block128" and role == "weight":
         blocks = np.unique(rows // 128)
@@ -283,14 +273,25 @@ def _check_rows(xbits, q_gpu_np, scheme, role, rows):
     assert_q_equal(_take(q_gpu_np, rows, role), ref, "sampled rows")
 
 
-def _gemm_sample_ref(aq_rows: dict, wq_rows: dict, scheme):
-    if scheme == "fp8_block128":
-        # expand the weight's block scales to per-(row, group) so the sampled rows stand alone
-        w = dict(wq_rows)
-        w["scales"] = np.asarray(wq_rows["scales"], np.float32)
-        w["role"] = "activation"
-        return oracle.gemm_ref(aq_rows, w)
-    return oracle.gemm_ref(aq_rows, wq_rows)
+def _sample_check(c_bits, a_rows, w_rows, K, what, a_bits_rows=None):
+    """Per-element check of sampled outputs; a_rows / w_rows are row subsets (for a
+    128x128-block weight, its rows with the block scale repeated per row)."""
+    if a_bits_rows is not None:       # W4A16: the activation is bf16 itself
+        c64 = oracle.gemm_ref(a_bits_rows, w_rows)
+        t = oracle.gemm_abs_ref(a_bits_rows, w_rows)
+        wr, t_off = w4a16_terms(a_bits_rows, w_rows)
+        return check_gemm(c_bits, c64, t, K, what, weight_round=wr, t_acc=t_off)
+    c64 = oracle.gemm_ref(a_rows, w_rows)
+    t = oracle.gemm_abs_ref(a_rows, w_rows)
+    return check_gemm(c_bits, c64, t, K, what)
+
+
+def _block_weight_rows(wq_np: dict, rw: np.ndarray) -> dict:
+    """Rows of a 128x128-block weight as a per-(row, 128-group) scaled operand."""
+    w = _take(wq_np, rw, "weight")
+    w["scales"] = np.asarray(wq_np["scales"], np.float32)[rw // 128]
+    w["role"] = "activation"
+    return w
 
 
 @pytest.mark.parametrize("name,scheme", [("fp8_tensor_small", "fp8_tensor"), ("fp8_row_dit", "fp8_row"),
@@ -309,21 +310,17 @@ def test_full_size_workload(name, scheme):
     if scheme == "fp8_tensor":
         assert_q_equal(aq_np, oracle.quantize(a_bits, scheme, "activation"), "A")
         assert_q_equal(wq_np, oracle.quantize(w_bits, scheme, "weight"), "W")
-        err = oracle.rel_fro_error(F.bf16_to_f32(down_bf16(c)), oracle.gemm_ref(aq_np, wq_np))
-        assert err <= TOL
+        assert_gemm(down_bf16(c), aq_np, wq_np, name)
         return
-    ra = _sample_rows(w_.M, 96, 11, extra=range(w_.M - 40, w_.M))    # includes the ragged tail
-    rw = _sample_rows(w_.N, 96, 12, extra=range(w_.N - 8, w_.N))
-    _check_rows(a_bits, aq_np, scheme, "activation", ra)
-    _check_rows(w_bits, wq_np, scheme, "weight", rw)
+    # every 256 x 256 output tile: its first and last rows and columns plus two random
+    # ones each, and the ragged tail rows
+    ra = tile_sample(w_.M, 11, extra=range(w_.M - 24, w_.M))
+    rw = tile_sample(w_.N, 12)
+    _check_rows(a_bits, aq_np, scheme, "activation", ra[::3])
+    _check_rows(w_bits, wq_np, scheme, "weight", rw[::3])
     a_rows = _take(aq_np, ra, "activation")
-    w_rows = _take(wq_np, rw, "weight")
-    if scheme == "fp8_block128":
-        w_rows["scales"] = np.repeat(wq_np["scales"][rw // 128][:, None, :], 1, axis=1).reshape(len(rw), -1)
-    ref = _gemm_sample_ref(a_rows, w_rows, scheme)
-    got = F.bf16_to_f32(down_bf16(c)[np.ix_(ra, rw)])
-    err = oracle.rel_fro_error(got, ref)
-    assert err <= TOL, f"{name}/{scheme}: rel err {err:.3e}"
+    w_rows = _block_weight_rows(wq_np, rw) if scheme == "fp8_block128" else _take(wq_np, rw, "weight")
+    _sample_check(down_bf16(c)[np.ix_(ra, rw)], a_rows, w_rows, w_.K, f"{name}/{scheme}")
 
 
 @pytest.mark.parametrize("M", [1, 16, 256, 4096])
@@ -335,14 +332,12 @@ def test_full_size_w4a16(M):
     wq = pql.from_numpy(wq_np, DEV)
     a_bits = wl.activation(w_, M)
     c = pql.qlinear(up(a_bits), wq)
-    ra = _sample_rows(M, 48, 13)
-    rw = _sample_rows(w_.N, 128, 14, extra=range(w_.N - 4, w_.N))
+    ra = tile_sample(M, 13)
+    rw = tile_sample(w_.N, 14, tile=128, per_tile=1)
     w_rows = {k: (v[rw] if isinstance(v, np.ndarray) else v) for k, v in wq_np.items()}
     w_rows["rows"] = len(rw)
-    ref = oracle.gemm_ref(np.ascontiguousarray(a_bits[ra]), w_rows)
-    got = F.bf16_to_f32(down_bf16(c)[np.ix_(ra, rw)])
-    err = oracle.rel_fro_error(got, ref)
-    assert err <= TOL, f"M={M}: rel err {err:.3e}"
+    _sample_check(down_bf16(c)[np.ix_(ra, rw)], None, w_rows, w_.K, f"M={M}",
+                  a_bits_rows=np.ascontiguousarray(a_bits[ra]))
 
 
 def test_full_size_int4_weight_quantizer():

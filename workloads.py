@@ -131,3 +131,17 @@ def pack_int4_codes(codes: np.ndarray) -> np.ndarray:
 def small_case(seed: int, rows: int, cols: int, std: float = 1.0) -> np.ndarray:
     """A small seeded bf16 tensor for parity cases that span several tiles."""
     return normal_bf16(seed, rows, cols, std)
+
+
+def pow2_blocks(bits: np.ndarray, seed: int, row_block: int, col_block: int) -> np.ndarray:
+    """Multiply a bf16 tensor by 2^(e_i + f_j), e per block of ``row_block`` rows and f per
+    block of ``col_block`` columns, each cycling through 0, 1, 2 (offset by ``seed``), so
+    that neighbouring blocks differ in magnitude by 2x or 4x.  Power-of-two scaling of
+    bf16 values is exact.  Parity cases use it so that a scale taken from a
+    neighbouring row, K-group or block is off by at least a factor of 2."""
+    b = np.asarray(bits, dtype=np.uint16)
+    rows, cols = b.shape
+    e = (np.arange(rows) // row_block + seed) % 3
+    f = (2 * (np.arange(cols) // col_block) + seed) % 3
+    x = bf16_bits_to_f32(b) * np.ldexp(np.float32(1.0), (e[:, None] + f[None, :])).astype(np.float32)
+    return f32_to_bf16_bits(x)
