@@ -17,7 +17,8 @@
  *   - All pointers except the size outputs are DEVICE pointers on the current
  *     HIP device.  The caller allocates and owns every buffer, including
  *     workspace; the library allocates no device memory and keeps no state
- *     besides a per-device property cache and a thread-local error message.
+ *     besides a per-device property cache, a thread-local error message and
+ *     the static device buffer of pql_qlinear_noalloc (see there).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
  *     and the call returns without synchronizing.  Calls are re-entrant.
  *   - Every argument check runs before anything is enqueued; on any error
@@ -225,6 +226,27 @@ pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64
                           const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
                           const void* bias, void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/* pql_qlinear_ex for callers that cannot allocate device memory at call
+ * time -- code being captured into a HIP graph, tight serving loops, harnesses
+ * that forbid allocation -- and so cannot hand over a workspace.  Arguments,
+ * results and errors are those of pql_qlinear_ex without the workspace: the
+ * activation's codes and scales go to a static device buffer of the library
+ * (pql_noalloc_scratch_bytes(), 64 MiB, held on every device the library runs
+ * on until the process ends).  Nothing is allocated or freed, by the library
+ * or anything it calls.  An activation whose codes and scales need more than
+ * that (pql_workspace_size(PQL_OP_QLINEAR, ...) > pql_noalloc_scratch_bytes())
+ * is rejected with PQL_ERR_WORKSPACE before anything is enqueued.  Every call
+ * on one device shares that device's buffer and leaves its contents behind
+ * (nothing in it needs to start at zero): calls that overlap in time on one
+ * device -- on different streams, or from different threads without ordering
+ * -- race and give undefined results.  W4A16 uses no buffer. */
+pql_status pql_qlinear_noalloc(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
+                               const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
+                               const void* bias, void* c, int64_t ldc, void* stream);
+
+/* Size in bytes of pql_qlinear_noalloc's static device buffer. */
+size_t pql_noalloc_scratch_bytes(void);
 
 /* Name of the kernel that `op` would launch for these sizes (for "no silent
  * fallback" checks); "" if the combination is invalid.  Static string. */

@@ -60,8 +60,11 @@ def lib() -> ctypes.CDLL:
         L.pql_quantize_static.argtypes = [ci, ci, vp, i64, i64, i64, vp, vp, vp]
         L.pql_qgemm_ex.argtypes = [ci, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp, vp, i64, vp]
         L.pql_qlinear_ex.argtypes = [ci, vp, i64, i64, i64, vp, vp, vp, vp, i64, f32, vp, vp, i64, vp, sz, vp]
+        L.pql_qlinear_noalloc.argtypes = [ci, vp, i64, i64, i64, vp, vp, vp, vp, i64, f32, vp, vp, i64, vp]
+        L.pql_noalloc_scratch_bytes.restype = sz
         for f in ("pql_quantized_sizes", "pql_workspace_size", "pql_quantize", "pql_dequantize",
-                  "pql_qgemm", "pql_qlinear", "pql_quantize_static", "pql_qgemm_ex", "pql_qlinear_ex"):
+                  "pql_qgemm", "pql_qlinear", "pql_quantize_static", "pql_qgemm_ex", "pql_qlinear_ex",
+                  "pql_qlinear_noalloc"):
             getattr(L, f).restype = ci
         _lib = L
     return _lib
@@ -428,3 +431,37 @@ def to_numpy(q: QTensor) -> dict:
         out["scales_packed"] = scales
         out["scales"] = unpack_mx_scales(scales, q.cols // 32)
     return out
+
+
+def qlinear_noalloc(x: torch.Tensor, w: QTensor, out: torch.Tensor, alpha: float = 1.0,
+                    bias: torch.Tensor | None = None, act_scales: torch.Tensor | None = None) -> torch.Tensor:
+    """``qlinear`` that allocates nothing, for code under HIP graph capture or loops that must
+    not allocate: x is a 2-D bf16 [M, K] tensor (W4A16: contiguous), ``out`` the caller's bf16
+    [M, N] output.  The activation's codes and scales live in the library's static device
+    buffer (``noalloc_scratch_bytes()``); calls overlapping in time on one device race."""
+    _check_qtensor(w, "w")
+    if w.role != "weight":
+        raise ValueError("w must be a quantized weight")
+    x = _as_2d_bf16(x)
+    M, K = x.shape
+    if K != w.cols:
+        raise ValueError(f"K mismatch: {K} vs {w.cols}")
+    if x.device != w.device:
+        raise ValueError(f"input on {x.device}, weight on {w.device}")
+    _check_out(out, M, w.rows, w.device)
+    if act_scales is not None:
+        if w.scheme not in STATIC_SCHEMES:
+            raise NotImplementedError(f"static activation scales are defined for {STATIC_SCHEMES} only")
+        want = 1 if w.scheme == "fp8_tensor" else M * (K // 128)
+        if act_scales.dtype != torch.float32 or not act_scales.is_contiguous() or act_scales.device != x.device \
+                or act_scales.numel() != want:
+            raise ValueError(f"act_scales must be {want} contiguous float32 values on the input's device")
+    _check(lib().pql_qlinear_noalloc(_scheme(w.scheme), x.data_ptr(), M, K, x.stride(0), _ptr(act_scales),
+                                     w.codes.data_ptr(), w.scales.data_ptr(), _ptr(w.zeros), w.rows, float(alpha),
+                                     _bias_ptr(bias, w.rows, x.device), out.data_ptr(), out.stride(0),
+                                     _stream(x.device)), "qlinear_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().pql_noalloc_scratch_bytes())

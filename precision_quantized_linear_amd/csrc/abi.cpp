@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -374,10 +375,14 @@ pql_status pql_qgemm(int scheme, const void* a, const void* a_scales, const void
   return pql_qgemm_ex(scheme, a, a_scales, w_codes, w_scales, w_zeros, M, N, K, 1.0f, nullptr, c, ldc, stream);
 }
 
-pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
-                          const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
-                          const void* bias, void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of qlinear (both entry points) that precede the workspace check.
+pql_status check_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
+                         const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
+                         const void* bias, const void* c, int64_t ldc) {
   if (!valid_scheme(scheme)) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
   pql_status st = check_gemm_shape(scheme, M, N, K);
   if (st != PQL_OK) return st;
@@ -394,14 +399,13 @@ pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64
   if (!aligned16(a) || !aligned16(w_codes) || !aligned16(w_scales) || (a_static_scales && !aligned16(a_static_scales)) ||
       (w_zeros && !aligned16(w_zeros)))
     return fail(PQL_ERR_INVALID_ARGUMENT, "operands, scales and zero-points must be 16-byte aligned");
-  if (!is_w4a16(scheme)) {
-    const size_t need = qlinear_ws_bytes(scheme, M, K);
-    if (!workspace || workspace_bytes < need)
-      return fail(PQL_ERR_WORKSPACE, "qlinear needs a %zu-byte workspace (got %zu)", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned16(workspace)) return fail(PQL_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
-  }
-  if ((st = check_device()) != PQL_OK) return st;
+  return PQL_OK;
+}
+
+// qlinear's launches, after every check (the workspace holds at least qlinear_ws_bytes).
+pql_status run_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
+                       const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
+                       const void* bias, void* c, int64_t ldc, void* workspace, void* stream) {
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (is_w4a16(scheme))
     return launched(do_qgemm(scheme, a, nullptr, w_codes, w_scales, w_zeros, M, N, K, 1.0f, nullptr, c, ldc, hs),
@@ -422,6 +426,74 @@ pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64
   if (e != hipSuccess) return launched(e, "qlinear activation quantize");
   return launched(do_qgemm(scheme, a_codes, a_scales, w_codes, w_scales, w_zeros, M, N, K, alpha, bias, c, ldc, hs),
                   "qlinear gemm");
+}
+
+// ---- the entry point that allocates nothing: its activation codes and scales
+// live in this file-scope device array.  The host-side name `scratch` is only a
+// stand-in: kernels get the per-device address from hipGetSymbolAddress.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];   // per device, filled on the device's first call
+
+pql_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PQL_ERR_HIP, "no usable HIP device: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(PQL_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(PQL_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PQL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
+                          const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
+                          const void* bias, void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  pql_status st = check_qlinear(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha, bias,
+                                c, ldc);
+  if (st != PQL_OK || M == 0) return st == PQL_OK ? ok() : st;
+  if (!is_w4a16(scheme)) {
+    const size_t need = qlinear_ws_bytes(scheme, M, K);
+    if (!workspace || workspace_bytes < need)
+      return fail(PQL_ERR_WORKSPACE, "qlinear needs a %zu-byte workspace (got %zu)", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PQL_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  }
+  if ((st = check_device()) != PQL_OK) return st;
+  return run_qlinear(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha, bias, c, ldc,
+                     workspace, stream);
+}
+
+size_t pql_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+pql_status pql_qlinear_noalloc(int scheme, const void* a, int64_t M, int64_t K, int64_t lda,
+                               const void* a_static_scales, const void* w_codes, const void* w_scales,
+                               const void* w_zeros, int64_t N, float alpha, const void* bias, void* c, int64_t ldc,
+                               void* stream) {
+  pql_status st = check_qlinear(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha, bias,
+                                c, ldc);
+  if (st != PQL_OK || M == 0) return st == PQL_OK ? ok() : st;
+  const size_t need = is_w4a16(scheme) ? 0 : qlinear_ws_bytes(scheme, M, K);
+  if (need > kScratchBytes)
+    return fail(PQL_ERR_WORKSPACE, "the activation's codes and scales need %zu bytes, more than the %zu-byte "
+                "static scratch of pql_qlinear_noalloc; use pql_qlinear_ex with a workspace", need, kScratchBytes);
+  if ((st = check_device()) != PQL_OK) return st;
+  void* ws = nullptr;
+  if (need && (st = scratch_address(&ws)) != PQL_OK) return st;
+  return run_qlinear(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha, bias, c, ldc, ws,
+                     stream);
 }
 
 pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* w_codes,

@@ -226,3 +226,18 @@ def test_qgemm_ex_validation():
     assert q(scheme=S["int8_row"]) == pql.PQL_ERR_UNSUPPORTED
     assert q(st=_p(516)) == pql.PQL_ERR_INVALID_ARGUMENT
     assert q(scheme=S["w4a16_asym"], st=None, alpha=3.0) == pql.PQL_ERR_UNSUPPORTED
+
+
+def test_qlinear_noalloc_limit_is_checked_before_any_device_call():
+    """An activation whose codes and scales exceed the static buffer is refused by
+    argument checks alone (no device is touched; the pointers are never read)."""
+    L = pql.lib()
+    cap = L.pql_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    K, N = 4096, 128
+    M = cap // K + 1
+    fake = 1 << 20                           # 16-byte aligned, never dereferenced on this path
+    st = L.pql_qlinear_noalloc(S["fp8_row"], fake, M, K, K, None, fake, fake, None, N, ctypes.c_float(1.0), None,
+                               fake, N, None)
+    assert st == pql.PQL_ERR_WORKSPACE
+    assert b"static scratch" in L.pql_last_error()
