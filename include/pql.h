@@ -27,8 +27,9 @@
  *     (ldx, ldy, lda, ldc) are in elements.  Device pointers must be 16-byte
  *     aligned and leading dimensions multiples of 8 elements.
  *
- * Canonical layouts (per scheme; rows = M for activations, N for weights,
- * cols = K):
+ * Packed layouts: what every call below except pql_repack produces and
+ * consumes, laid out for the GEMM kernels (per scheme; rows = M for
+ * activations, N for weights, cols = K):
  *   FP8_TENSOR    codes u8 e4m3fn [rows, cols]          scales f32 [1]
  *   FP8_ROW       codes u8 e4m3fn [rows, cols]          scales f32 [rows]
  *   FP8_BLOCK128  codes u8 e4m3fn [rows, cols]          scales f32 [rows, cols/128] (activation)
@@ -51,6 +52,12 @@
  * r's 32-element block c g + b (K-elements 32 (c g + b) .. + 31); bytes past
  * the row's last block are 127.  A chunk covers 128 bytes of codes, so the
  * exponents one GEMM step needs for consecutive rows are consecutive bytes.
+ *
+ * Canonical layouts (PQL_LAYOUT_CANONICAL): the same codes, with the scales
+ * and zero-points of every row together: MX exponents u8 [rows, cols/32],
+ * W4A16 scales bf16 [rows, cols/128] and zero-points u8 [rows, cols/128]; for
+ * every other scheme the canonical and packed layouts are the same bytes.
+ * pql_repack converts between the two on the device.
  */
 #ifndef PQL_H
 #define PQL_H
@@ -113,6 +120,8 @@ typedef enum pql_scheme {
 
 typedef enum pql_role { PQL_ACTIVATION = 0, PQL_WEIGHT = 1 } pql_role;
 
+typedef enum pql_layout { PQL_LAYOUT_CANONICAL = 0, PQL_LAYOUT_PACKED = 1 } pql_layout;
+
 typedef enum pql_op {
   PQL_OP_QUANTIZE = 0,
   PQL_OP_DEQUANTIZE = 1,
@@ -140,6 +149,30 @@ const char* pql_last_error(void);
 pql_status pql_quantized_sizes(int scheme, int role, int64_t rows, int64_t cols,
                                size_t* codes_bytes, size_t* scales_bytes,
                                size_t* zeros_bytes);
+
+/* pql_quantized_sizes for either layout (PQL_LAYOUT_PACKED gives the same
+ * sizes as pql_quantized_sizes; canonical MX scales take rows * cols / 32
+ * bytes, without the packed layout's padding).  Same errors, plus
+ * INVALID_ARGUMENT for an unknown layout. */
+pql_status pql_layout_sizes(int scheme, int role, int layout, int64_t rows, int64_t cols, size_t* codes_bytes,
+                            size_t* scales_bytes, size_t* zeros_bytes);
+
+/* Convert a quantized tensor's scales (and W4A16 zero-points) from one layout
+ * to the other on the device ("vLLM-Omni Online Quantization complete
+ * guide", section "How online quantization works underneath", step 2: online
+ * weights are brought into the layout the GEMM consumes, with the scales
+ * rearranged to match).  Codes are the same bytes in both layouts and are not
+ * touched.  scales_in / zeros_in are in `from_layout`, scales_out /
+ * zeros_out (caller-allocated, pql_layout_sizes(to_layout) bytes) receive
+ * `to_layout`; zeros are required for W4A16 and ignored otherwise.  When the
+ * two layouts are the same bytes (the layouts are equal, or the scheme has
+ * one layout) this is a device copy, nothing if input and output coincide;
+ * otherwise input and output must be distinct buffers.  Errors: as
+ * pql_quantize's shape checks, INVALID_ARGUMENT for an unknown layout, NULL
+ * buffers or overlapping buffers of a transposing repack. */
+pql_status pql_repack(int scheme, int role, int from_layout, int to_layout, const void* scales_in,
+                      const void* zeros_in, void* scales_out, void* zeros_out, int64_t rows, int64_t cols,
+                      void* stream);
 
 /* Workspace bytes a call needs (host output).  op = PQL_OP_QUANTIZE: the
  * per-tensor scheme needs a small partial-maximum buffer, the others 0.

@@ -60,11 +60,13 @@ def lib() -> ctypes.CDLL:
         L.pql_quantize_static.argtypes = [ci, ci, vp, i64, i64, i64, vp, vp, vp]
         L.pql_qgemm_ex.argtypes = [ci, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp, vp, i64, vp]
         L.pql_qlinear_ex.argtypes = [ci, vp, i64, i64, i64, vp, vp, vp, vp, i64, f32, vp, vp, i64, vp, sz, vp]
+        L.pql_layout_sizes.argtypes = [ci, ci, ci, i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
+        L.pql_repack.argtypes = [ci, ci, ci, ci, vp, vp, vp, vp, i64, i64, vp]
         L.pql_qlinear_noalloc.argtypes = [ci, vp, i64, i64, i64, vp, vp, vp, vp, i64, f32, vp, vp, i64, vp]
         L.pql_noalloc_scratch_bytes.restype = sz
         for f in ("pql_quantized_sizes", "pql_workspace_size", "pql_quantize", "pql_dequantize",
                   "pql_qgemm", "pql_qlinear", "pql_quantize_static", "pql_qgemm_ex", "pql_qlinear_ex",
-                  "pql_qlinear_noalloc"):
+                  "pql_qlinear_noalloc", "pql_layout_sizes", "pql_repack"):
             getattr(L, f).restype = ci
         _lib = L
     return _lib
@@ -364,72 +366,98 @@ def qlinear(x: torch.Tensor, w: QTensor, out: torch.Tensor | None = None,
     return out.reshape(*lead, w.rows)
 
 
-def pack_mx_scales(scales, chunk: int):
-    """Row-major e8m0 exponents [rows, nblk] (NumPy) -> the library's packed layout
-    [ceil(nblk / chunk), rows, chunk], bytes past a row's last block 127."""
-    import numpy as np
-    s = np.asarray(scales, np.uint8)
-    rows, nblk = s.shape
-    g = -(-nblk // chunk)
-    padded = np.full((rows, g * chunk), 127, np.uint8)
-    padded[:, :nblk] = s
-    return np.ascontiguousarray(padded.reshape(rows, g, chunk).transpose(1, 0, 2))
+LAYOUTS = {"canonical": 0, "packed": 1}
 
 
-def unpack_mx_scales(packed, nblk: int):
-    """Inverse of pack_mx_scales: [G, rows, chunk] -> [rows, nblk]."""
-    import numpy as np
-    p = np.asarray(packed, np.uint8)
-    g, rows, chunk = p.shape
-    return np.ascontiguousarray(p.transpose(1, 0, 2).reshape(rows, g * chunk)[:, :nblk])
+def layout_sizes(scheme, role, layout, rows: int, cols: int):
+    c, s, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().pql_layout_sizes(_scheme(scheme), _role(role), LAYOUTS[layout], rows, cols,
+                                  ctypes.byref(c), ctypes.byref(s), ctypes.byref(z)), "layout_sizes")
+    return c.value, s.value, z.value
+
+
+def _canonical_shapes(scheme, role, rows, cols):
+    """(scales dtype, scales shape, zeros shape or None) of the canonical layout."""
+    if scheme in MX_CHUNK:
+        return torch.uint8, (rows, cols // 32), None
+    if scheme.startswith("w4a16"):
+        return torch.bfloat16, (rows, cols // 128), (rows, cols // 128)
+    return None, None, None     # the same bytes as the packed layout
+
+
+def _repack(scheme, role, rows, cols, frm, to, scales_in, zeros_in, scales_out, zeros_out, device):
+    _check(lib().pql_repack(_scheme(scheme), _role(role), LAYOUTS[frm], LAYOUTS[to], scales_in.data_ptr(),
+                            _ptr(zeros_in), scales_out.data_ptr(), _ptr(zeros_out), rows, cols, _stream(device)),
+           "repack")
+
+
+def to_canonical(q: QTensor):
+    """(codes, scales, zeros) of ``q`` in the canonical layout, as device tensors; the
+    scales (and W4A16 zero-points) are rearranged on the device by pql_repack."""
+    _check_qtensor(q, "q")
+    _on_device(q.device)
+    dt, shape, zshape = _canonical_shapes(q.scheme, q.role, q.rows, q.cols)
+    if dt is None:
+        return q.codes, q.scales, q.zeros
+    scales = torch.empty(shape, dtype=dt, device=q.device)
+    zeros = torch.empty(zshape, dtype=torch.uint8, device=q.device) if zshape else None
+    _repack(q.scheme, q.role, q.rows, q.cols, "packed", "canonical", q.scales, q.zeros, scales, zeros, q.device)
+    return q.codes, scales, zeros
+
+
+def from_canonical(scheme: str, role: str, rows: int, cols: int, codes: torch.Tensor, scales: torch.Tensor,
+                   zeros: torch.Tensor | None = None) -> QTensor:
+    """A QTensor (packed layout) from device tensors in the canonical layout; codes are
+    used as they are, scales (and W4A16 zero-points) are rearranged on the device."""
+    _on_device(codes.device)
+    q = _alloc_q(scheme, role, rows, cols, codes.device)
+    cb, sb, zb = layout_sizes(scheme, role, "canonical", rows, cols)
+    for t, nb, what in ((codes, cb, "codes"), (scales, sb, "scales"), (zeros, zb, "zeros")):
+        if t is None:
+            if nb:
+                raise ValueError(f"{scheme} needs {what}")
+            continue
+        if t.device != codes.device or not t.is_contiguous() or t.numel() * t.element_size() != nb:
+            raise ValueError(f"{what} must be a contiguous tensor of {nb} bytes on {codes.device}")
+    q.codes = codes.view(q.codes.dtype).reshape(q.codes.shape)
+    _repack(scheme, role, rows, cols, "canonical", "packed", scales, zeros, q.scales, q.zeros, codes.device)
+    return q
 
 
 def from_numpy(q: dict, device) -> QTensor:
     """Upload a quantized tensor given as NumPy arrays in the canonical layout (MX
-    exponents row-major [rows, cols / 32], W4A16 scales and zero-points [rows,
-    cols / 128]; both go up in the device layout)."""
+    exponents [rows, cols / 32], W4A16 scales and zero-points [rows, cols / 128]); the
+    arrays go up as they are and pql_repack rearranges them into the packed layout on
+    the device."""
     import numpy as np
     scheme = q["scheme"]
 
-    def up(a, dtype):
-        t = torch.from_numpy(np.ascontiguousarray(a))
-        if dtype is not None:
-            t = t.view(dtype)
-        return t.to(device)
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
-    if scheme.startswith("w4a16"):   # scales / zero-points go up group-major
-        codes = up(q["codes"].view("int32"), None)
-        scales = up(np.ascontiguousarray(np.asarray(q["scales"]).T).view("int16"), torch.bfloat16)
-        zeros = up(np.ascontiguousarray(np.asarray(q["zeros"]).T), None)
-    else:
-        codes = up(q["codes"], None)
-        sc = q["scales"]
-        if scheme in MX_CHUNK:
-            sc = pack_mx_scales(sc, MX_CHUNK[scheme])
-        scales = up(sc, None)
-        zeros = None
-    return QTensor(scheme, q["role"], q["rows"], q["cols"], codes, scales, zeros)
+    codes = up(np.asarray(q["codes"]).view(np.uint8))
+    scales = up(np.asarray(q["scales"]).view(np.uint8))
+    zeros = up(np.asarray(q["zeros"]).view(np.uint8)) if q.get("zeros") is not None else None
+    return from_canonical(scheme, q["role"], q["rows"], q["cols"], codes, scales, zeros)
 
 
 def to_numpy(q: QTensor) -> dict:
-    """Download a quantized tensor into NumPy arrays in the canonical layout (MX
-    exponents unpacked to row-major [rows, cols / 32], the packed bytes as they are
-    in device memory under "scales_packed"; W4A16 scales and zero-points as
-    [rows, cols / 128])."""
+    """Download a quantized tensor into NumPy arrays in the canonical layout: pql_repack
+    rearranges the scales (and W4A16 zero-points) on the device, then the bytes come down
+    as they are.  The packed device bytes of MX exponents are also returned, under
+    "scales_packed"."""
     import numpy as np
-    codes = q.codes.cpu().numpy()
-    if q.scheme.startswith("w4a16"):   # group-major on the device, [rows, groups] here
-        codes = codes.view(np.uint32)
-        scales = np.ascontiguousarray(q.scales.view(torch.int16).cpu().numpy().view(np.uint16).T)
-        zeros = np.ascontiguousarray(q.zeros.cpu().numpy().T)
-    else:
-        scales = q.scales.cpu().numpy()
-        zeros = None
+    codes, scales, zeros = to_canonical(q)
+    np_dtype = {torch.uint8: np.uint8, torch.int8: np.int8, torch.int32: np.uint32, torch.float32: np.float32,
+                torch.bfloat16: np.uint16}
+
+    def down(t):
+        return t.contiguous().view(torch.uint8).cpu().numpy().view(np_dtype[t.dtype]).reshape(t.shape)
+
     out = {"scheme": q.scheme, "role": q.role, "rows": q.rows, "cols": q.cols,
-           "codes": codes, "scales": scales, "zeros": zeros}
+           "codes": down(codes), "scales": down(scales), "zeros": None if zeros is None else down(zeros)}
     if q.scheme in MX_CHUNK:
-        out["scales_packed"] = scales
-        out["scales"] = unpack_mx_scales(scales, q.cols // 32)
+        out["scales_packed"] = down(q.scales)
     return out
 
 

@@ -503,6 +503,54 @@ pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t 
                         workspace, workspace_bytes, stream);
 }
 
+pql_status pql_layout_sizes(int scheme, int role, int layout, int64_t rows, int64_t cols, size_t* codes_bytes,
+                            size_t* scales_bytes, size_t* zeros_bytes) {
+  if (layout != PQL_LAYOUT_CANONICAL && layout != PQL_LAYOUT_PACKED)
+    return fail(PQL_ERR_INVALID_ARGUMENT, "unknown layout %d", layout);
+  pql_status st = pql_quantized_sizes(scheme, role, rows, cols, codes_bytes, scales_bytes, zeros_bytes);
+  if (st != PQL_OK || layout == PQL_LAYOUT_PACKED) return st;
+  if (is_mx(scheme) && scales_bytes) *scales_bytes = (size_t)rows * (size_t)(cols / 32);   // u8 [rows, cols / 32]
+  return ok();
+}
+
+pql_status pql_repack(int scheme, int role, int from_layout, int to_layout, const void* scales_in,
+                      const void* zeros_in, void* scales_out, void* zeros_out, int64_t rows, int64_t cols,
+                      void* stream) {
+  pql_status st = check_scheme_role(scheme, role);
+  if (st != PQL_OK) return st;
+  if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
+  for (int l : {from_layout, to_layout})
+    if (l != PQL_LAYOUT_CANONICAL && l != PQL_LAYOUT_PACKED)
+      return fail(PQL_ERR_INVALID_ARGUMENT, "unknown layout %d", l);
+  if (rows == 0) return ok();
+  if (!scales_in || !scales_out) return fail(PQL_ERR_INVALID_ARGUMENT, "scales_in and scales_out must be non-NULL");
+  if (is_w4a16(scheme) && (!zeros_in || !zeros_out))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "W4A16 needs zeros_in and zeros_out");
+  const bool differs = from_layout != to_layout && (is_mx(scheme) || is_w4a16(scheme));
+  if (differs && (scales_in == scales_out || (zeros_in && zeros_in == zeros_out)))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "%s scales change layout; input and output must be distinct buffers",
+                scheme_name(scheme));
+  if ((st = check_device()) != PQL_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool to_packed = to_layout == PQL_LAYOUT_PACKED;
+  if (differs && is_mx(scheme))
+    return launched(pql::launch_mx_repack(to_packed, scheme == PQL_MXFP4, static_cast<const uint8_t*>(scales_in),
+                                          rows, cols, static_cast<uint8_t*>(scales_out), hs),
+                    "repack launch");
+  if (differs)
+    return launched(pql::launch_group_repack(to_packed, static_cast<const uint16_t*>(scales_in),
+                                             static_cast<const uint8_t*>(zeros_in), rows, cols / 128,
+                                             static_cast<uint16_t*>(scales_out), static_cast<uint8_t*>(zeros_out), hs),
+                    "repack launch");
+  // the same layout: a copy (nothing to do in place)
+  const Sizes sz = sizes_of(scheme, role, rows, cols);
+  hipError_t e = hipSuccess;
+  if (scales_in != scales_out) e = hipMemcpyAsync(scales_out, scales_in, sz.scales, hipMemcpyDeviceToDevice, hs);
+  if (e == hipSuccess && zeros_in && zeros_out && zeros_in != zeros_out)
+    e = hipMemcpyAsync(zeros_out, zeros_in, sz.zeros, hipMemcpyDeviceToDevice, hs);
+  return launched(e, "repack copy");
+}
+
 const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, int64_t K) {
   if (!valid_scheme(scheme)) return "";
   switch (op) {

@@ -47,6 +47,14 @@ hipError_t launch_quant_int4(bool sym, const uint16_t* x, int64_t rows, int64_t 
 hipError_t launch_dequant(int kind, const void* codes, const void* scales, const uint8_t* zeros,
                           int64_t rows, int64_t cols, uint16_t* y, int64_t ldy, hipStream_t st);
 
+// ---------------------------------------------------------------- layouts
+// MX exponents: canonical [rows, cols / 32] <-> packed [G, rows, c] (to_packed picks the direction).
+hipError_t launch_mx_repack(bool to_packed, bool fp4, const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,
+                            hipStream_t st);
+// W4A16 scales (and zero-points, if zeros_in is non-null): canonical [rows, groups] <-> group-major [groups, rows].
+hipError_t launch_group_repack(bool to_packed, const uint16_t* scales_in, const uint8_t* zeros_in, int64_t rows,
+                               int64_t groups, uint16_t* scales_out, uint8_t* zeros_out, hipStream_t st);
+
 // ---------------------------------------------------------------- GEMM
 enum GemmKind { GEMM_FP8_ROWSCALE = 0, GEMM_FP8_BLOCK = 1, GEMM_MXFP8 = 2, GEMM_MXFP4 = 3, GEMM_INT8_ROW = 4 };
 

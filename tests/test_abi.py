@@ -241,3 +241,29 @@ def test_qlinear_noalloc_limit_is_checked_before_any_device_call():
                                fake, N, None)
     assert st == pql.PQL_ERR_WORKSPACE
     assert b"static scratch" in L.pql_last_error()
+
+
+def test_layout_sizes():
+    L = pql.lib()
+    c, sc, z = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    for scheme, rows, cols, canon, packed in (("mxfp8", 3, 96, 3 * 3, 3 * 4), ("mxfp4", 5, 384, 5 * 12, 5 * 16),
+                                              ("w4a16_asym", 4, 256, 2 * 4 * 2, 2 * 4 * 2),
+                                              ("fp8_row", 7, 64, 7 * 4, 7 * 4)):
+        for layout, want in ((0, canon), (1, packed)):
+            assert L.pql_layout_sizes(S[scheme], W, layout, rows, cols, ctypes.byref(c), ctypes.byref(sc),
+                                      ctypes.byref(z)) == pql.PQL_OK
+            assert sc.value == want, (scheme, layout)
+    assert L.pql_layout_sizes(S["mxfp8"], W, 2, 4, 64, None, None, None) == pql.PQL_ERR_INVALID_ARGUMENT
+
+
+def test_repack_validation():
+    L = pql.lib()
+    fake = 1 << 20
+    # unknown layout, NULL buffers, a transposing repack in place: refused before any device call
+    assert L.pql_repack(S["mxfp8"], W, 0, 3, fake, None, fake + 4096, None, 4, 64, None) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert L.pql_repack(S["mxfp8"], W, 0, 1, None, None, fake, None, 4, 64, None) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert L.pql_repack(S["mxfp4"], W, 0, 1, fake, None, fake, None, 4, 64, None) == pql.PQL_ERR_INVALID_ARGUMENT
+    assert L.pql_repack(S["w4a16_asym"], W, 1, 0, fake, None, fake + 4096, fake + 8192, 4, 128, None) \
+        == pql.PQL_ERR_INVALID_ARGUMENT
+    assert L.pql_repack(S["w4a16_asym"], A, 1, 0, fake, fake, fake, fake, 4, 128, None) == pql.PQL_ERR_UNSUPPORTED
+    assert L.pql_repack(S["mxfp8"], W, 0, 1, fake, None, fake + 4096, None, 4, 48, None) == pql.PQL_ERR_INVALID_ARGUMENT

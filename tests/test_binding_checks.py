@@ -6,18 +6,15 @@ operands in the wrong role, and mismatched devices: otherwise a kernel would
 write past a buffer or store bf16 into a float32 tensor.  Every case below
 raises ValueError from the binding itself (CPU tensors never reach the
 library)."""
-import numpy as np
 import pytest
 import torch
 
-import oracle
 import precision_quantized_linear_amd as pql
-import workloads as wl
 
 
 def _cpu_q(scheme, role, rows, cols, seed):
-    bits = wl.small_case(seed, rows, cols, 1.0 if role == "activation" else 0.02)
-    return pql.from_numpy(oracle.quantize(bits, scheme, role), "cpu")
+    """A QTensor with buffers of the right shapes on the CPU (contents irrelevant here)."""
+    return pql._alloc_q(scheme, role, rows, cols, "cpu")
 
 
 @pytest.fixture(scope="module")
@@ -100,3 +97,11 @@ def test_wide_row_stride_out_is_accepted_until_the_device_check(ops):
     wide = torch.empty((16, 48), dtype=torch.bfloat16)[:, 8:40]    # [16, 32] view, row stride 48
     with pytest.raises(ValueError, match="HIP device"):            # shape and strides passed
         pql.qgemm(a, w, out=wide)
+
+
+def test_from_numpy_needs_a_device():
+    import oracle
+    import workloads as wl
+    q = oracle.quantize(wl.small_case(1, 4, 64), "mxfp8", "activation")
+    with pytest.raises(ValueError, match="HIP device"):
+        pql.from_numpy(q, "cpu")

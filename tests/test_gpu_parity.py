@@ -106,6 +106,35 @@ def test_quantize_bit_exact(scheme, role, rows, cols):
         assert np.array_equal(q.zeros.cpu().numpy(), ref["zeros"].T)
 
 
+REPACK_CASES = [("mxfp8", "activation", 37, 384), ("mxfp8", "weight", 5, 96), ("mxfp4", "weight", 300, 1152),
+                ("mxfp4", "activation", 1, 64), ("w4a16_asym", "weight", 300, 1152), ("w4a16_sym", "weight", 7, 128),
+                ("w4a16_asym", "weight", 33, 4096), ("fp8_block128", "activation", 9, 256),
+                ("fp8_block128", "weight", 128, 384), ("fp8_row", "weight", 3, 64), ("int8_row", "activation", 6, 640)]
+
+
+def _bytes(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy().reshape(-1)
+
+
+@pytest.mark.parametrize("scheme,role,rows,cols", REPACK_CASES)
+def test_repack_canonical_bytes_on_device(scheme, role, rows, cols):
+    """The device repack (pql_repack) turns the packed scales of a GPU quantization into
+    the canonical layout bit for bit against the oracle, and back into the same packed
+    bytes (MX pad bytes included); no host-side permutation is involved."""
+    x = hard_input(rows * 3 + cols, rows, cols, 0.02 if role == "weight" else 1.0)
+    ref = oracle.quantize(x, scheme, role)                       # canonical by definition
+    q = pql.quantize(up(x), scheme, role)                       # packed device layout
+    codes, scales, zeros = pql.to_canonical(q)
+    assert np.array_equal(_bytes(codes), np.ascontiguousarray(ref["codes"]).view(np.uint8).reshape(-1))
+    assert np.array_equal(_bytes(scales), np.ascontiguousarray(ref["scales"]).view(np.uint8).reshape(-1))
+    if ref["zeros"] is not None:
+        assert np.array_equal(_bytes(zeros), np.ascontiguousarray(ref["zeros"]).view(np.uint8).reshape(-1))
+    back = pql.from_canonical(scheme, role, rows, cols, codes, scales, zeros)
+    assert np.array_equal(_bytes(back.scales), _bytes(q.scales))
+    if q.zeros is not None:
+        assert np.array_equal(_bytes(back.zeros), _bytes(q.zeros))
+
+
 @pytest.mark.parametrize("M,N,K", [(257, 388, 384), (1000, 260, 640), (512, 1024, 256), (130, 390, 384),
                                    (2304, 4100, 256), (300, 4100, 512), (200, 8300, 384), (256, 8448, 256)])
 def test_w4a16_gemm_tile_shapes(M, N, K):
