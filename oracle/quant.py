@@ -13,6 +13,8 @@ fp8_block128   u8 e4m3fn [rows, cols]        act f32 [rows, cols/128];
                                              wt  f32 [rows/128, cols/128]
 mxfp8          u8 e4m3fn [rows, cols]        u8 e8m0 [rows, cols/32]
 mxfp4          u8 two e2m1 [rows, cols/2]    u8 e8m0 [rows, cols/32]
+mxfp4_dual     u8 two e2m1 [rows, cols/2]    u8 e8m0 [rows, cols/32] (fine),
+                                             f32 [rows, cols/512] ("coarse")
 w4a16_asym     u32 eight int4 [rows, cols/8] bf16 [rows, cols/128]
                                              (u8 zero-points [rows, cols/128])
 w4a16_sym      as w4a16_asym, zero-point fixed at 8
@@ -46,6 +48,17 @@ Readings where the pages are silent (all listed in the design notes):
 * MX shared exponent X = clamp(floor(log2 amax) - emax, -127, 127), emax = 8
   for e4m3 and 2 for e2m1; the element is rounded from x * 2^-X; amax = 0
   gives X = -127 (code 0).
+* Dual-scale MXFP4 (two online scale levels, fine per 32 and coarse per 512
+  K-elements, with the calibrated multiplier of offline checkpoints replaced
+  by ones; "vLLM-Omni Online Quantization complete guide", sections "How
+  online quantization works underneath" and "Key parameters in detail"): the
+  page names the levels but not their formats.  Read as: a coarse fp32 scale
+  per (row, 512-block) s_c = fp32(amax_512 / 6), 1 if that is 0; the
+  quotient v = fp32(x / s_c) (correctly rounded, formed first, as for FP8);
+  then plain MX on v: a fine e8m0 exponent per 32-block
+  X = clamp(floor(log2 max|v|) - 2, -127, 127) and q = RNE_sat_e2m1(v * 2^-X).
+  A unit multiplier leaves x unchanged.  K must be a multiple of 512.
+  Dequantized: decode(q) * 2^X * s_c.
 * int4 round-to-nearest: range [min(0, min x), max(0, max x)],
   s = bf16(fp32(fp32(xmax - xmin) / 15)), z = clamp(rne(fp32(-xmin / s)), 0, 15),
   q = clamp(rne(fp32(x / s)) + z, 0, 15).  Symmetric: z = 8,
@@ -63,7 +76,7 @@ from .formats import (
 )
 
 SCHEMES = ("fp8_tensor", "fp8_row", "fp8_block128", "mxfp8", "mxfp4",
-           "w4a16_asym", "w4a16_sym", "int8_row")
+           "w4a16_asym", "w4a16_sym", "int8_row", "mxfp4_dual")
 STATIC_SCHEMES = ("fp8_tensor", "fp8_block128")
 ROLES = ("activation", "weight")
 
@@ -83,6 +96,8 @@ def _check(x_bits, scheme, role):
         raise ValueError("W4A16 quantizes weights only")
     if scheme in ("mxfp8", "mxfp4") and cols % 32:
         raise ValueError("MX schemes need K % 32 == 0")
+    if scheme == "mxfp4_dual" and cols % 512:
+        raise ValueError("dual-scale MXFP4 needs K % 512 == 0")
     if (scheme == "fp8_block128" or scheme.startswith("w4a16")) and cols % 128:
         raise ValueError("block-128 / group-128 schemes need K % 128 == 0")
     if scheme == "fp8_block128" and role == "weight" and rows % 128:
@@ -155,6 +170,23 @@ def _quant_mx(x, fmt):
     return codes, (X + 127).astype(np.uint8)
 
 
+def _quant_mx4_dual(x):
+    """Two scale levels: coarse fp32 s_c per 512-block, then MX (e2m1, emax 2) on the
+    quotients v = fp32(x / s_c)."""
+    rows, cols = x.shape
+    nb = cols // 512
+    xc = x.reshape(rows, nb, 512)
+    amax = np.max(np.abs(xc), axis=2) if rows else np.zeros((0, nb), _F32)
+    s_c = (amax.astype(_F32) / _F32(E2M1_MAX)).astype(_F32)
+    s_c = np.where(s_c == 0, _F32(1.0), s_c).astype(_F32)              # [rows, cols/512]
+    v = (xc / s_c[:, :, None]).astype(_F32)                             # fp32 quotient, RNE
+    vb = v.reshape(rows, cols // 32, 32).astype(np.float64)
+    vmax = np.max(np.abs(vb), axis=2) if rows else np.zeros((0, cols // 32))
+    X = mx_exponent(vmax, 2)                                            # fine exponents [rows, cols/32]
+    codes = pack_fp4(e2m1_encode(vb * np.ldexp(1.0, -X)[:, :, None]).reshape(rows, cols))
+    return codes, (X + 127).astype(np.uint8), s_c
+
+
 # ---------------------------------------------------------------- int4 RTN
 def _rne_int(v_f32):
     return np.rint(v_f32.astype(np.float64))                   # half to even
@@ -216,6 +248,10 @@ def quantize(x_bits, scheme: str, role: str = "activation") -> dict:
         codes, scales = _quant_mx(x, scheme)
     elif scheme == "int8_row":
         codes, scales = _quant_int8_row(x)
+    elif scheme == "mxfp4_dual":
+        codes, scales, coarse = _quant_mx4_dual(x)
+        return {"scheme": scheme, "role": role, "rows": rows, "cols": cols,
+                "codes": codes, "scales": scales, "coarse": coarse, "zeros": None}
     else:
         codes, scales, zeros = _quant_int4(x, scheme == "w4a16_sym")
     return {"scheme": scheme, "role": role, "rows": rows, "cols": cols,
@@ -273,9 +309,12 @@ def _decoded(q):
         return e4m3_decode(q["codes"]), _expand_scale_f32(q).astype(np.float64)
     if scheme == "int8_row":
         return np.asarray(q["codes"], dtype=np.int8).astype(np.float64), _expand_scale_f32(q).astype(np.float64)
-    if scheme in ("mxfp8", "mxfp4"):
+    if scheme in ("mxfp8", "mxfp4", "mxfp4_dual"):
         vals = e4m3_decode(q["codes"]) if scheme == "mxfp8" else e2m1_decode(unpack_fp4(q["codes"]))
         sc = np.repeat(e8m0_decode(q["scales"]).reshape(rows, cols // 32), 32, axis=1)
+        if scheme == "mxfp4_dual":   # 2^X (exact) times the coarse fp32 scale (exact in float64)
+            sc = sc * np.repeat(np.asarray(q["coarse"], np.float32).astype(np.float64).reshape(rows, cols // 512),
+                                512, axis=1)
         return vals, sc
     codes = unpack_int4(q["codes"]).astype(np.float64)
     z = np.repeat(np.asarray(q["zeros"], dtype=np.float64).reshape(rows, cols // 128), 128, axis=1)
@@ -290,7 +329,16 @@ def dequant_exact(q) -> np.ndarray:
 
 
 def dequantize(q) -> np.ndarray:
-    """bf16 bits of bf16_RNE(fp32(decode(q) * scale)) (int4: (q - z) * s)."""
+    """bf16 bits of bf16_RNE(fp32(decode(q) * scale)) (int4: (q - z) * s; dual-scale
+    MXFP4: fp32(decode(q) * 2^X) is exact, then one rounding of its product with the
+    coarse fp32 scale)."""
+    if q["scheme"] == "mxfp4_dual":
+        rows, cols = q["rows"], q["cols"]
+        fine = (e2m1_decode(unpack_fp4(q["codes"]))
+                * np.repeat(e8m0_decode(q["scales"]).reshape(rows, cols // 32), 32, axis=1)).astype(_F32)
+        coarse = np.repeat(np.asarray(q["coarse"], _F32).reshape(rows, cols // 512), 512, axis=1)
+        with np.errstate(over="ignore"):
+            return f32_to_bf16_rne((fine * coarse).astype(_F32))
     vals, sc = _decoded(q)
     prod = (vals.astype(_F32) * sc.astype(_F32)).astype(_F32)   # one fp32 rounding
     with np.errstate(over="ignore"):

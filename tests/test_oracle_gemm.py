@@ -97,7 +97,7 @@ def _frac_dequant(q):
                 byte = int(np.asarray(q["codes"]).view(np.uint8)[r, k])
                 v = Fraction(byte - 256 if byte > 127 else byte)       # two's complement by hand
                 out[r][k] = v * Fraction(float(q["scales"][r]))
-            elif scheme in ("mxfp8", "mxfp4"):
+            elif scheme in ("mxfp8", "mxfp4", "mxfp4_dual"):
                 if scheme == "mxfp8":
                     c = q["codes"][r, k]
                     v = Fraction(float(F.e4m3_decode(np.array([c], np.uint8))[0]))
@@ -107,6 +107,8 @@ def _frac_dequant(q):
                     v = Fraction(float(F.e2m1_decode(np.array([nib]))[0]))
                 X = int(q["scales"][r, k // 32]) - 127
                 out[r][k] = v * (Fraction(2) ** X)
+                if scheme == "mxfp4_dual":     # times the coarse fp32 scale of the 512-block
+                    out[r][k] *= Fraction(float(np.float32(q["coarse"][r, k // 512])))
             else:
                 word = int(q["codes"][r, k // 8])
                 code = (word >> (4 * (k % 8))) & 0xF
@@ -117,12 +119,14 @@ def _frac_dequant(q):
 
 
 @pytest.mark.parametrize("scheme", ["fp8_tensor", "fp8_row", "fp8_block128", "mxfp8", "mxfp4",
-                                    "w4a16_asym", "int8_row"])
+                                    "w4a16_asym", "int8_row", "mxfp4_dual"])
 def test_random_tiny_gemm_against_exact_rationals(scheme):
     rng = np.random.default_rng(7 + len(scheme) * 31 + ord(scheme[-1]))
     for trial in range(3):
         M, N = int(rng.integers(1, 4)), int(rng.integers(1, 4))
         K = int(rng.choice([128, 256])) if scheme in ("fp8_block128", "w4a16_asym") else int(rng.choice([32, 64, 128, 256]))
+        if scheme == "mxfp4_dual":
+            K = int(rng.choice([512, 1024]))
         Nw = 128 if scheme == "fp8_block128" else N
         a_bits = small_case(1000 + trial, M, K, 1.0)
         w_bits = small_case(2000 + trial, Nw, K, 0.02)
@@ -208,3 +212,14 @@ def test_random_tiny_epilogue_against_exact_rationals(scheme):
             exact = Fraction(float(alpha)) * sum(terms, Fraction(0)) + bias_f[n]
             bound = 4 * K * 2.0 ** -53 * (float(alpha) * float(sum(abs(t) for t in terms)) + abs(float(bias_f[n])))
             assert abs(c[m, n] - float(exact)) <= bound + 1e-300, (m, n)
+
+
+def test_mxfp4_dual_two_coarse_blocks_scale_separately():
+    """K = 1024: coarse block 0 all codes 1.0 (0x2) with s_c 2 (A) and 3 (W); block 1 all
+    codes 2.0 (0x4) with s_c 0.5 and 0.25; fine exponents 0.  C = 2*3*512*1 + 0.5*0.25*512*4 = 3328."""
+    nib = np.concatenate([np.full(512, 0x2), np.full(512, 0x4)]).astype(np.uint8)[None, :]
+    fine = np.full((1, 32), 127, np.uint8)
+    a = {"scheme": "mxfp4_dual", "role": "activation", "rows": 1, "cols": 1024, "codes": F.pack_fp4(nib),
+         "scales": fine, "coarse": np.array([[2.0, 0.5]], np.float32), "zeros": None}
+    w = dict(a, role="weight", coarse=np.array([[3.0, 0.25]], np.float32))
+    assert oracle.gemm_ref(a, w).tolist() == [[3328.0]]

@@ -21,6 +21,7 @@ import oracle
 from oracle import formats as F
 from golden_io import keyed, parse_floats, parse_hex
 from workloads import f32_to_bf16_bits, small_case
+import workloads as wl
 
 
 def bf16(vals):
@@ -484,3 +485,87 @@ def test_int8_dequantize_rounds_once():
     y = F.bf16_to_f32(oracle.dequantize(q))
     prod = (q["codes"].astype(np.float32) * q["scales"][:, None]).astype(np.float32)
     assert np.array_equal(y, F.bf16_to_f32(F.f32_to_bf16_rne(prod)))
+
+
+# ----------------------------------------------------------------- dual-scale MXFP4
+def test_mxfp4_dual_worked_example():
+    """tests/golden/mxfp4_dual_worked_example.txt: coarse fp32 scale, fine exponents and
+    codes worked by hand (every element not listed is 0 with code 0; unlisted blocks
+    are all-zero, fine code 0)."""
+    from golden_io import keyed
+    d = keyed("mxfp4_dual_worked_example.txt")
+    x = np.zeros((2, 512), np.float32)
+    for r, k, v in d["x"]:
+        x[int(r), int(k)] = np.float32(float(v))
+    q = oracle.quantize(wl.f32_to_bf16_bits(x), "mxfp4_dual", "activation")
+    coarse = np.asarray(q["coarse"], np.float32).view(np.uint32)
+    for r, h in d["coarse"]:
+        assert coarse[int(r), 0] == int(h, 16)
+    fine = np.zeros((2, 16), np.uint8)
+    for r, b, c in d["fine"]:
+        fine[int(r), int(b)] = int(c)
+    assert np.array_equal(q["scales"], fine)
+    codes = np.zeros((2, 512), np.uint8)
+    for r, k, c in d["code"]:
+        codes[int(r), int(k)] = int(c, 16)
+    assert np.array_equal(F.unpack_fp4(q["codes"]), codes)
+
+
+@pytest.mark.parametrize("coarse_mant", [1.0, 1.5])
+def test_mxfp4_dual_exact_reproduction(coarse_mant):
+    """Values e2m1 * 2^X * s_c with s_c = m 2^j (m = 1 or 1.5, exact in bf16 together with
+    any e2m1 value) and one element of each 512-block at 6 * s_c: the coarse scale, fine
+    exponents and codes come back exactly, including a non-power-of-two coarse scale."""
+    rng = np.random.default_rng(int(coarse_mant * 10))
+    rows, cols = 6, 1024
+    nib = rng.integers(0, 16, (rows, cols)).astype(np.uint8)
+    X = rng.integers(-6, 1, (rows, cols // 32))
+    X[:, ::16] = 0                                     # the block holding the 6 keeps X = 0
+    nib[:, ::512] = 0x7                                # +6 in every 512-block's first element
+    j = rng.integers(-4, 5, (rows, cols // 512))
+    s_c = (coarse_mant * np.ldexp(1.0, j)).astype(np.float32)
+    # every 32-block needs a magnitude-6 element for its X to be recovered exactly
+    nib[:, 5::32] = 0xF
+    vals = F.e2m1_decode(nib) * np.repeat(np.ldexp(1.0, X), 32, axis=1) * np.repeat(s_c, 512, axis=1)
+    bits = wl.f32_to_bf16_bits(vals.astype(np.float32))
+    assert np.array_equal(F.bf16_to_f32(bits).astype(np.float64), vals)       # representable
+    q = oracle.quantize(bits, "mxfp4_dual", "weight")
+    assert np.array_equal(np.asarray(q["coarse"], np.float32), s_c)
+    assert np.array_equal(q["scales"].astype(np.int64) - 127, X)
+    # the sign of zero is kept, so compare values (and codes away from zero)
+    got = F.unpack_fp4(q["codes"])
+    assert np.array_equal(F.e2m1_decode(got), F.e2m1_decode(nib))
+    assert np.array_equal(oracle.dequant_exact(q), vals)
+
+
+def test_mxfp4_dual_error_bound_and_zero_blocks():
+    x = wl.small_case(77, 16, 2048).copy()
+    x[3, 512:1024] = 0                                   # an all-zero coarse block
+    x[5, :32] = 0                                        # an all-zero fine block
+    q = oracle.quantize(x, "mxfp4_dual", "activation")
+    xf = F.bf16_to_f32(x).astype(np.float64)
+    assert q["coarse"][3, 1] == 1.0 and np.all(F.unpack_fp4(q["codes"])[3, 512:1024] & 7 == 0)
+    assert q["scales"][5, 0] == 0
+    s_c = np.repeat(np.asarray(q["coarse"], np.float64), 512, axis=1)
+    X = np.repeat(q["scales"].astype(np.int64) - 127, 32, axis=1)
+    v = (xf / s_c).astype(np.float32).astype(np.float64) * np.ldexp(1.0, -X)     # the grid value
+    dq = oracle.dequant_exact(q)
+    sat = np.abs(v) > 6
+    # half an e2m1 ulp at the element's binade (0.5 below 1, then 0.5, 0.5, 1, 1, 2 ...)
+    e = np.maximum(np.floor(np.log2(np.maximum(np.abs(v), 1e-300))), 0)
+    half_ulp = np.ldexp(0.25, e.astype(np.int64))
+    bound = half_ulp * np.ldexp(1.0, X) * s_c + np.abs(xf) * 2.0 ** -23
+    assert np.all(np.abs(xf - dq)[~sat] <= bound[~sat])
+    assert np.all(np.abs(dq[sat]) == 6 * np.ldexp(1.0, X[sat]) * s_c[sat])
+
+
+def test_mxfp4_dual_dequantize_rounds_once():
+    x = wl.small_case(78, 8, 512)
+    q = oracle.quantize(x, "mxfp4_dual", "activation")
+    want = F.f32_to_bf16_rne(oracle.dequant_exact(q).astype(np.float32))   # exact value, one rounding
+    assert np.array_equal(oracle.dequantize(q), want)
+
+
+def test_mxfp4_dual_rejects_k_not_multiple_of_512():
+    with pytest.raises(ValueError):
+        oracle.quantize(wl.small_case(1, 2, 256), "mxfp4_dual", "activation")
