@@ -42,6 +42,9 @@
  *   W4A16_SYM     as W4A16_ASYM with every zero-point 8
  *   INT8_ROW      codes i8 [rows, cols] (two's         scales f32 [rows]
  *                 complement)
+ *   MXFP4_DUAL    codes as MXFP4                       scales: fine e8m0 packed [G, rows, 8], then
+ *                                                       from the next 256-byte boundary coarse
+ *                                                       f32 [cols/512, rows] (group-major)
  * All codes are K-contiguous, which is the operand order the matrix cores
  * consume, so weights need no re-layout after quantization.
  * W4A16 scales and zero-points are group-major ([group, row]): one K-group's
@@ -55,8 +58,10 @@
  *
  * Canonical layouts (PQL_LAYOUT_CANONICAL): the same codes, with the scales
  * and zero-points of every row together: MX exponents u8 [rows, cols/32],
- * W4A16 scales bf16 [rows, cols/128] and zero-points u8 [rows, cols/128]; for
- * every other scheme the canonical and packed layouts are the same bytes.
+ * W4A16 scales bf16 [rows, cols/128] and zero-points u8 [rows, cols/128],
+ * MXFP4_DUAL fine exponents u8 [rows, cols/32] then (from the next 256-byte
+ * boundary, as packed) coarse f32 [rows, cols/512]; for every other scheme the
+ * canonical and packed layouts are the same bytes.
  * pql_repack converts between the two on the device.
  */
 #ifndef PQL_H
@@ -106,6 +111,15 @@ typedef enum pql_status {
  *     online path quantizes weights with weight scales; its activation
  *     scales are dynamic, a static activation scheme is an error).
  *     s = fp32(amax / 127) (1 if that is 0); code = clamp(rne(fp32(x / s)), -128, 127).
+ *   MXFP4_DUAL: MXFP4 with two online scale levels, a coarse fp32 scale per
+ *     512 K-elements and a fine e8m0 exponent per 32 ("vLLM-Omni Online
+ *     Quantization complete guide", section "How online quantization works
+ *     underneath", MXFP4 paragraph; the calibrated multiplier of offline
+ *     checkpoints is all ones online and leaves x unchanged).  K % 512 == 0.
+ *     s_c = fp32(amax_512 / 6) (1 if 0); v = fp32(x / s_c) (correctly
+ *     rounded); X = clamp(floor(log2 max|v|) - 2, -127, 127) per 32-block;
+ *     code = RNE_sat_e2m1(v * 2^-X).  Dequantized: fp32(decode * 2^X) * s_c.
+ *     No fused alpha / bias epilogue.
  */
 typedef enum pql_scheme {
   PQL_FP8_TENSOR = 0,
@@ -115,7 +129,8 @@ typedef enum pql_scheme {
   PQL_MXFP4 = 4,
   PQL_W4A16_ASYM = 5,
   PQL_W4A16_SYM = 6,
-  PQL_INT8_ROW = 7
+  PQL_INT8_ROW = 7,
+  PQL_MXFP4_DUAL = 8
 } pql_scheme;
 
 typedef enum pql_role { PQL_ACTIVATION = 0, PQL_WEIGHT = 1 } pql_role;

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(_PKG, "libpql.so")
 MX_CHUNK = {"mxfp8": 4, "mxfp4": 8}
 
 SCHEMES = {"fp8_tensor": 0, "fp8_row": 1, "fp8_block128": 2, "mxfp8": 3, "mxfp4": 4,
-           "w4a16_asym": 5, "w4a16_sym": 6, "int8_row": 7}
+           "w4a16_asym": 5, "w4a16_sym": 6, "int8_row": 7, "mxfp4_dual": 8}
 STATIC_SCHEMES = ("fp8_tensor", "fp8_block128")
 ROLES = {"activation": 0, "weight": 1}
 OPS = {"quantize": 0, "dequantize": 1, "qgemm": 2, "qlinear": 3}
@@ -151,6 +151,10 @@ def _alloc_q(scheme: str, role: str, rows: int, cols: int, device) -> QTensor:
     elif scheme == "int8_row":
         codes = torch.empty((rows, cols), dtype=torch.int8, device=device)
         scales = torch.empty((rows,), dtype=torch.float32, device=device)
+        zeros = None
+    elif scheme == "mxfp4_dual":   # fine exponents, then coarse fp32 scales, in one byte buffer
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=device)
+        scales = torch.empty((sb,), dtype=torch.uint8, device=device)
         zeros = None
     else:
         codes = torch.empty((rows, cols if scheme != "mxfp4" else cols // 2), dtype=torch.uint8, device=device)
@@ -376,8 +380,14 @@ def layout_sizes(scheme, role, layout, rows: int, cols: int):
     return c.value, s.value, z.value
 
 
+def _dual_coarse_offset(rows, cols):
+    return (rows * (cols // 32) + 255) // 256 * 256
+
+
 def _canonical_shapes(scheme, role, rows, cols):
     """(scales dtype, scales shape, zeros shape or None) of the canonical layout."""
+    if scheme == "mxfp4_dual":
+        return torch.uint8, (_dual_coarse_offset(rows, cols) + 4 * rows * (cols // 512),), None
     if scheme in MX_CHUNK:
         return torch.uint8, (rows, cols // 32), None
     if scheme.startswith("w4a16"):
@@ -436,7 +446,15 @@ def from_numpy(q: dict, device) -> QTensor:
         return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
     codes = up(np.asarray(q["codes"]).view(np.uint8))
-    scales = up(np.asarray(q["scales"]).view(np.uint8))
+    if scheme == "mxfp4_dual":      # one canonical buffer: fine [rows, cols/32], then coarse [rows, cols/512]
+        off = _dual_coarse_offset(q["rows"], q["cols"])
+        buf = np.zeros(off + 4 * q["rows"] * (q["cols"] // 512), np.uint8)
+        fine = np.ascontiguousarray(q["scales"], np.uint8).reshape(-1)
+        buf[:fine.size] = fine
+        buf[off:] = np.ascontiguousarray(q["coarse"], np.float32).reshape(-1).view(np.uint8)
+        scales = up(buf)
+    else:
+        scales = up(np.asarray(q["scales"]).view(np.uint8))
     zeros = up(np.asarray(q["zeros"]).view(np.uint8)) if q.get("zeros") is not None else None
     return from_canonical(scheme, q["role"], q["rows"], q["cols"], codes, scales, zeros)
 
@@ -457,6 +475,11 @@ def to_numpy(q: QTensor) -> dict:
     out = {"scheme": q.scheme, "role": q.role, "rows": q.rows, "cols": q.cols,
            "codes": down(codes), "scales": down(scales), "zeros": None if zeros is None else down(zeros)}
     if q.scheme in MX_CHUNK:
+        out["scales_packed"] = down(q.scales)
+    if q.scheme == "mxfp4_dual":    # split the canonical buffer into its two levels
+        buf, off = out["scales"], _dual_coarse_offset(q.rows, q.cols)
+        out["scales"] = buf[:q.rows * (q.cols // 32)].reshape(q.rows, q.cols // 32).copy()
+        out["coarse"] = buf[off:].view(np.float32).reshape(q.rows, q.cols // 512).copy()
         out["scales_packed"] = down(q.scales)
     return out
 

@@ -47,19 +47,27 @@ const char* scheme_name(int s) {
     case PQL_W4A16_ASYM: return "W4A16_ASYM";
     case PQL_W4A16_SYM: return "W4A16_SYM";
     case PQL_INT8_ROW: return "INT8_ROW";
+    case PQL_MXFP4_DUAL: return "MXFP4_DUAL";
   }
   return "?";
 }
 
 bool is_w4a16(int s) { return s == PQL_W4A16_ASYM || s == PQL_W4A16_SYM; }
 bool is_mx(int s) { return s == PQL_MXFP8 || s == PQL_MXFP4; }
-bool valid_scheme(int s) { return s >= PQL_FP8_TENSOR && s <= PQL_INT8_ROW; }
+bool valid_scheme(int s) { return s >= PQL_FP8_TENSOR && s <= PQL_MXFP4_DUAL; }
 // Schemes whose GEMM takes the fused epilogue alpha * (A W^T) + bias.
 bool has_epilogue(int s) { return s == PQL_FP8_TENSOR || s == PQL_FP8_ROW || s == PQL_FP8_BLOCK128 || s == PQL_INT8_ROW; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
-int64_t k_granule(int scheme) { return (scheme == PQL_FP8_BLOCK128 || is_w4a16(scheme)) ? 128 : 32; }
+int64_t k_granule(int scheme) {
+  return scheme == PQL_MXFP4_DUAL ? 512 : (scheme == PQL_FP8_BLOCK128 || is_w4a16(scheme)) ? 128 : 32;
+}
+
+// Dual-scale MXFP4 keeps both scale levels in its scales buffer: the fine e8m0
+// exponents (rows * cols / 32 bytes), then, from the next 256-byte boundary,
+// the coarse fp32 scales (rows * cols / 512 of them).
+size_t dual_coarse_offset(int64_t rows, int64_t cols) { return ((size_t)rows * (size_t)(cols / 32) + 255) & ~size_t(255); }
 
 pql_status check_scheme_role(int scheme, int role) {
   if (!valid_scheme(scheme)) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
@@ -102,6 +110,7 @@ Sizes sizes_of(int scheme, int role, int64_t rows, int64_t cols) {
       break;
     case PQL_MXFP8: s.codes = R * C; s.scales = R * pql::mx_packed_row_bytes(C, false); break;
     case PQL_MXFP4: s.codes = R * C / 2; s.scales = R * pql::mx_packed_row_bytes(C, true); break;
+    case PQL_MXFP4_DUAL: s.codes = R * C / 2; s.scales = dual_coarse_offset(rows, cols) + 4 * R * (C / 512); break;
     default: s.codes = R * C / 2; s.scales = 2 * R * (C / 128); s.zeros = R * (C / 128); break;
   }
   return s;
@@ -153,6 +162,11 @@ hipError_t do_quantize(int scheme, int role, const void* x, int64_t rows, int64_
     case PQL_MXFP8:
     case PQL_MXFP4:
       return pql::launch_quant_mx(scheme == PQL_MXFP4, xb, rows, cols, ldx, cb, static_cast<uint8_t*>(scales), st);
+    case PQL_MXFP4_DUAL:
+      return pql::launch_quant_mx4_dual(xb, rows, cols, ldx, cb, static_cast<uint8_t*>(scales),
+                                        reinterpret_cast<float*>(static_cast<uint8_t*>(scales) +
+                                                                 dual_coarse_offset(rows, cols)),
+                                        st);
     default:
       return pql::launch_quant_int4(scheme == PQL_W4A16_SYM, xb, rows, cols, ldx, static_cast<uint32_t*>(codes),
                                     static_cast<uint16_t*>(scales), static_cast<uint8_t*>(zeros), st);
@@ -170,6 +184,23 @@ pql::GemmKind gemm_kind(int scheme) {
 hipError_t do_qgemm(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
                     const void* w_zeros, int64_t M, int64_t N, int64_t K, float alpha, const void* bias, void* c,
                     int64_t ldc, hipStream_t st) {
+  if (scheme == PQL_MXFP4_DUAL) {   // alpha = 1 and no bias here (checked by the callers)
+    pql::GemmArgs g{};
+    g.a = static_cast<const uint8_t*>(a);
+    g.w = static_cast<const uint8_t*>(w_codes);
+    g.a_scales = a_scales;
+    g.w_scales = w_scales;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = static_cast<uint16_t*>(c);
+    g.ldc = ldc;
+    g.vec_store = aligned16(c) && ldc % 8 == 0;
+    g.alpha = 1.0f;
+    const float* ac = reinterpret_cast<const float*>(static_cast<const uint8_t*>(a_scales) + dual_coarse_offset(M, K));
+    const float* wc = reinterpret_cast<const float*>(static_cast<const uint8_t*>(w_scales) + dual_coarse_offset(N, K));
+    return pql::launch_gemm_mx4_dual(g, ac, wc, st);
+  }
   if (is_w4a16(scheme))   // alpha = 1 and no bias here (checked by the callers)
     return pql::launch_gemm_w4a16(static_cast<const uint16_t*>(a), static_cast<const uint32_t*>(w_codes),
                                   static_cast<const uint16_t*>(w_scales), static_cast<const uint8_t*>(w_zeros), M, N,
@@ -206,6 +237,8 @@ pql_status check_gemm_shape(int scheme, int64_t M, int64_t N, int64_t K) {
     return fail(PQL_ERR_INVALID_ARGUMENT, "an M x N output of %lld x %lld is too large", (long long)M, (long long)N);
   if (scheme == PQL_FP8_BLOCK128 && N % 128)
     return fail(PQL_ERR_INVALID_ARGUMENT, "FP8_BLOCK128 needs N %% 128 == 0 (got %lld)", (long long)N);
+  if (scheme == PQL_MXFP4_DUAL && K % 512)
+    return fail(PQL_ERR_INVALID_ARGUMENT, "MXFP4_DUAL needs K %% 512 == 0 (got %lld)", (long long)K);
   return PQL_OK;
 }
 
@@ -296,8 +329,11 @@ pql_status pql_dequantize(int scheme, int role, const void* codes, const void* s
     case PQL_MXFP8: kind = 4; break;
     case PQL_MXFP4: kind = 5; break;
     case PQL_INT8_ROW: kind = 7; break;
+    case PQL_MXFP4_DUAL: kind = 8; break;
     default: kind = 6; break;
   }
+  if (scheme == PQL_MXFP4_DUAL)   // the coarse scales follow the fine exponents in the scales buffer
+    zeros = static_cast<const uint8_t*>(scales) + dual_coarse_offset(rows, cols);
   return launched(pql::launch_dequant(kind, codes, scales, static_cast<const uint8_t*>(zeros), rows, cols,
                                       static_cast<uint16_t*>(y), ldy, static_cast<hipStream_t>(stream)),
                   "dequantize launch");
@@ -526,13 +562,24 @@ pql_status pql_repack(int scheme, int role, int from_layout, int to_layout, cons
   if (!scales_in || !scales_out) return fail(PQL_ERR_INVALID_ARGUMENT, "scales_in and scales_out must be non-NULL");
   if (is_w4a16(scheme) && (!zeros_in || !zeros_out))
     return fail(PQL_ERR_INVALID_ARGUMENT, "W4A16 needs zeros_in and zeros_out");
-  const bool differs = from_layout != to_layout && (is_mx(scheme) || is_w4a16(scheme));
+  const bool differs = from_layout != to_layout && (is_mx(scheme) || is_w4a16(scheme) || scheme == PQL_MXFP4_DUAL);
   if (differs && (scales_in == scales_out || (zeros_in && zeros_in == zeros_out)))
     return fail(PQL_ERR_INVALID_ARGUMENT, "%s scales change layout; input and output must be distinct buffers",
                 scheme_name(scheme));
   if ((st = check_device()) != PQL_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool to_packed = to_layout == PQL_LAYOUT_PACKED;
+  if (differs && scheme == PQL_MXFP4_DUAL) {   // fine exponents as MXFP4, coarse scales transposed
+    const size_t off = dual_coarse_offset(rows, cols);
+    const uint8_t* in = static_cast<const uint8_t*>(scales_in);
+    uint8_t* out = static_cast<uint8_t*>(scales_out);
+    hipError_t e = pql::launch_mx_repack(to_packed, true, in, rows, cols, out, hs);
+    // canonical coarse [rows, cols / 512], packed group-major [cols / 512, rows]
+    if (e == hipSuccess)
+      e = pql::launch_transpose_f32(reinterpret_cast<const float*>(in + off), to_packed ? rows : cols / 512,
+                                    to_packed ? cols / 512 : rows, reinterpret_cast<float*>(out + off), hs);
+    return launched(e, "repack launch");
+  }
   if (differs && is_mx(scheme))
     return launched(pql::launch_mx_repack(to_packed, scheme == PQL_MXFP4, static_cast<const uint8_t*>(scales_in),
                                           rows, cols, static_cast<uint8_t*>(scales_out), hs),
@@ -563,12 +610,14 @@ const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, 
         case PQL_FP8_BLOCK128: return role == PQL_ACTIVATION ? "k_fp8_block_act" : "k_fp8_block_wt";
         case PQL_MXFP8: return "k_mx<e4m3>";
         case PQL_MXFP4: return "k_mx<e2m1>";
+        case PQL_MXFP4_DUAL: return "k_mx4_dual";
         default: return scheme == PQL_W4A16_SYM ? "k_int4<sym>" : "k_int4<asym>";
       }
     case PQL_OP_DEQUANTIZE: return "k_dequant";
     case PQL_OP_QGEMM:
     case PQL_OP_QLINEAR:
       if (is_w4a16(scheme)) return pql::gemm_w4a16_kernel_name(M, N, K);
+      if (scheme == PQL_MXFP4_DUAL) return "k_gemm_mx4_dual";
       return pql::gemm_kernel_name(gemm_kind(scheme), M, N, K);
   }
   return "";

@@ -100,6 +100,10 @@ hipError_t launch_mx_repack(bool to_packed, bool fp4, const uint8_t* in, int64_t
   return hipGetLastError();
 }
 
+hipError_t launch_transpose_f32(const float* in, int64_t R, int64_t C, float* out, hipStream_t st) {
+  return transpose<uint32_t>(in, R, C, out, st);
+}
+
 hipError_t launch_group_repack(bool to_packed, const uint16_t* scales_in, const uint8_t* zeros_in, int64_t rows,
                                int64_t groups, uint16_t* scales_out, uint8_t* zeros_out, hipStream_t st) {
   // canonical [rows, groups] -> packed [groups, rows] and back: a transpose either way

@@ -38,12 +38,16 @@ hipError_t launch_quant_fp8_block_wt(const uint16_t* x, int64_t rows, int64_t co
                                      uint8_t* codes, float* scales, hipStream_t st);
 hipError_t launch_quant_mx(bool fp4, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                            uint8_t* codes, uint8_t* scales, hipStream_t st);
+// Dual-scale MXFP4 (K % 512 == 0): codes [rows, K/2], fine exponents packed [K/256, rows, 8],
+// coarse fp32 scales group-major [K/512, rows].
+hipError_t launch_quant_mx4_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                                uint8_t* fine, float* coarse, hipStream_t st);
 hipError_t launch_quant_int4(bool sym, const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
                              uint32_t* codes, uint16_t* scales, uint8_t* zeros, hipStream_t st);
 
 // ---------------------------------------------------------------- dequantize
 // kind: 0 fp8 tensor, 1 fp8 row, 2 fp8 block act, 3 fp8 block weight, 4 mxfp8,
-//       5 mxfp4, 6 int4, 7 int8 row
+//       5 mxfp4, 6 int4, 7 int8 row, 8 dual-scale mxfp4 (zeros = its coarse fp32 scales)
 hipError_t launch_dequant(int kind, const void* codes, const void* scales, const uint8_t* zeros,
                           int64_t rows, int64_t cols, uint16_t* y, int64_t ldy, hipStream_t st);
 
@@ -52,6 +56,8 @@ hipError_t launch_dequant(int kind, const void* codes, const void* scales, const
 hipError_t launch_mx_repack(bool to_packed, bool fp4, const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,
                             hipStream_t st);
 // W4A16 scales (and zero-points, if zeros_in is non-null): canonical [rows, groups] <-> group-major [groups, rows].
+// fp32 [R, C] -> [C, R] (dual-scale MXFP4 coarse scales between canonical and group-major).
+hipError_t launch_transpose_f32(const float* in, int64_t R, int64_t C, float* out, hipStream_t st);
 hipError_t launch_group_repack(bool to_packed, const uint16_t* scales_in, const uint8_t* zeros_in, int64_t rows,
                                int64_t groups, uint16_t* scales_out, uint8_t* zeros_out, hipStream_t st);
 
@@ -87,6 +93,9 @@ hipError_t launch_gemm_block(const GemmArgs& g, hipStream_t st);
 inline bool gemm_block_uses_256(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256) >= 256; }
 hipError_t launch_gemm_block256(const GemmArgs& g, hipStream_t st);
 const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);
+// Dual-scale MXFP4 (K % 512 == 0): g's a_scales / w_scales are the fine exponents (packed
+// MXFP4 layout), a_coarse / w_coarse the coarse fp32 scales, group-major [K / 512, rows].
+hipError_t launch_gemm_mx4_dual(const GemmArgs& g, const float* a_coarse, const float* w_coarse, hipStream_t st);
 
 // W4A16: C = A (bf16) * dequant(Wq)^T
 // W4A16, M > 64: pipelined 256 x 128 tile kernel (N % 4 == 0, K % 128 == 0).

@@ -368,6 +368,67 @@ __global__ __launch_bounds__(256) void k_mx(const uint16_t* __restrict__ x, int6
   }
 }
 
+// ---------------------------------------------------------------- dual-scale MXFP4
+// Two online scale levels: a coarse fp32 scale per 512 K-elements and a fine
+// e8m0 exponent per 32 ("vLLM-Omni Online Quantization complete guide",
+// section "How online quantization works underneath", MXFP4 paragraph; the
+// calibrated multiplier of offline checkpoints is all ones online, so x is
+// used as it is).  s_c = fp32(amax_512 / 6) (1 if 0); v = fp32(x / s_c),
+// correctly rounded like the FP8 quotient; then MX on v: X = floor(log2
+// max|v|) - 2 per 32-block, code = e2m1 RNE_sat(v * 2^-X).
+// Row segments: with K % 512 == 0 a lane slice of 64 chunks is exactly one
+// coarse block, so its amax is a wave reduction (every lane of a wave shares
+// the row and the slice); a fine block is a DPP quad.  Fine exponents go to the
+// packed MXFP4 layout [G, rows, 8] (K % 512 == 0: no pad bytes), coarse scales
+// group-major [K / 512, rows].
+__global__ __launch_bounds__(256) void k_mx4_dual(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                  int64_t ldx, uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ fine, float* __restrict__ coarse) {
+  const Seg g;
+  if (g.row >= rows) return;   // wave-uniform: a wave is one row
+  const int64_t cpr = cols >> 3;
+  const uint16_t* xr = x + g.row * ldx;
+  const int64_t slice0 = g.c0 - g.lane;   // first chunk of the wave's first slice
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) {
+    if (slice0 + 64 * u >= cpr) break;    // wave-uniform (cpr is a multiple of 64)
+    const int64_t c = g.c0 + 64 * u;
+    const uint4 v = ldg16(xr + c * 8);
+    const float amax = wave_max(chunk_absmax(v));
+    float sc = __fdiv_rn(amax, 6.0f);
+    sc = sc == 0.0f ? 1.0f : sc;
+    const int64_t cb = (slice0 + 64 * u) >> 6;   // coarse block of this slice
+    if (g.lane == 0) coarse[cb * rows + g.row] = sc;
+    float f[8];
+    chunk_to_f32(v, f);
+    if (sc >= kSmallestFastScale) {
+      const float rcp = __fdiv_rn(1.0f, sc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = quot<true>(f[j], sc, rcp);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = quot<false>(f[j], sc, 0.0f);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, __builtin_fabsf(f[j]));
+    const int X = mx_shared_exponent(group4_max(m), 2);
+    if ((c & 3) == 0) {
+      const int64_t b = c >> 2;
+      fine[((b >> 3) * rows + g.row) * 8 + (b & 7)] = (uint8_t)(X + 127);
+    }
+    const float inv = exp2i(-X);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f[j] *= inv;
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0], f[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], 1.0f, 3);
+    *reinterpret_cast<uint32_t*>(codes + g.row * (cols >> 1) + c * 4) = w;
+  }
+}
+
 // ---------------------------------------------------------------- int4 round-to-nearest
 // Row segments; a 128-group is a 16-lane DPP row.  One chunk = one u32 of codes.
 template <bool SYM>
@@ -471,13 +532,18 @@ __global__ __launch_bounds__(256) void k_dequant(int kind, const uint8_t* __rest
     const int64_t c = g.c0 + 64 * u;
     if (c >= cpr) continue;
     float v[8];
-    if (kind <= 5) {
-      if (kind == 5) {
+    if (kind <= 5 || kind == 8) {
+      if (kind == 5 || kind == 8) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (cols >> 1) + c * 4);
         const int64_t b = c >> 2;
         const float sc = e8m0_value(static_cast<const uint8_t*>(scales)[((b >> 3) * rows + r) * 8 + (b & 7)]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((w >> (4 * j)) & 0xF) * sc;
+        for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((w >> (4 * j)) & 0xF) * sc;   // exact
+        if (kind == 8) {   // dual-scale: times the coarse scale (group-major [K/512, rows]), one rounding
+          const float cs = reinterpret_cast<const float*>(zeros)[(c >> 6) * rows + r];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] *= cs;
+        }
       } else {
         const uint2 w = *reinterpret_cast<const uint2*>(codes + r * cols + c * 8);
         float sc;
@@ -580,6 +646,12 @@ hipError_t launch_quant_mx(bool fp4, const uint16_t* x, int64_t rows, int64_t co
   const dim3 grid = seg_grid(rows, cols), block(256);
   if (fp4) hipLaunchKernelGGL(k_mx<true>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
   else hipLaunchKernelGGL(k_mx<false>, grid, block, 0, st, x, rows, cols, ldx, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx4_dual(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                                uint8_t* fine, float* coarse, hipStream_t st) {
+  hipLaunchKernelGGL(k_mx4_dual, seg_grid(rows, cols), dim3(256), 0, st, x, rows, cols, ldx, codes, fine, coarse);
   return hipGetLastError();
 }
 

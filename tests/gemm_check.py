@@ -150,11 +150,17 @@ def exact_operand(scheme: str, role: str, rows: int, cols: int, seed: int) -> di
         q["scales"] = np.ldexp(1.0, (br + 2 * g + seed) % 3 - 1).astype(np.float32)
     if scheme == "int8_row":
         q["codes"] = rng.integers(-16, 17, (rows, cols)).astype(np.int8)
-    if scheme in ("mxfp8", "mxfp4"):
-        if scheme == "mxfp4":
+    if scheme in ("mxfp8", "mxfp4", "mxfp4_dual"):
+        if scheme != "mxfp8":
             q["codes"] = F.pack_fp4(rng.integers(0, 16, (rows, cols)).astype(np.uint8))
         b = np.arange(cols // 32)[None, :]
-        q["scales"] = ((r + 2 * b + seed) % 3 - 1 + 127).astype(np.uint8)
+        if scheme == "mxfp4_dual":   # two levels multiply: exponents -1 / 0, alternating along rows and K
+            q["scales"] = ((r + b + seed) % 2 - 1 + 127).astype(np.uint8)
+        else:
+            q["scales"] = ((r + 2 * b + seed) % 3 - 1 + 127).astype(np.uint8)
+    if scheme == "mxfp4_dual":   # coarse scales: powers of two per (row, 512-block), neighbours 2x apart
+        cb = np.arange(cols // 512)[None, :]
+        q["coarse"] = np.ldexp(1.0, (r + cb + seed) % 2 - 1).astype(np.float32)
     if scheme.startswith("w4a16"):
         q["codes"] = F.pack_int4(rng.integers(0, 16, (rows, cols)).astype(np.uint8))
         g = np.arange(cols // 128)[None, :]

@@ -49,6 +49,9 @@ def test_quantized_sizes():
     assert _sizes("w4a16_asym", "weight", 12288, 3072) == (12288 * 1536, 2 * 12288 * 24, 12288 * 24)
     assert _sizes("int8_row", "activation", 4096, 3072) == (4096 * 3072, 4 * 4096, 0)
     assert _sizes("int8_row", "weight", 12288, 3072) == (12288 * 3072, 4 * 12288, 0)
+    # dual-scale MXFP4: fine exponents, then (256-byte aligned) the coarse fp32 scales
+    assert _sizes("mxfp4_dual", "activation", 20280, 5120) == (20280 * 2560, 20280 * 160 + 4 * 20280 * 10, 0)
+    assert _sizes("mxfp4_dual", "weight", 3, 512) == (3 * 256, 256 + 4 * 3, 0)
 
 
 @pytest.mark.parametrize("scheme,role,rows,cols", [
@@ -58,6 +61,7 @@ def test_quantized_sizes():
     ("fp8_block128", "weight", 64, 128),      # weight rows not a multiple of 128
     ("w4a16_asym", "weight", 4, 64),
     ("fp8_row", "activation", -1, 64),
+    ("mxfp4_dual", "activation", 4, 256),     # K not a multiple of 512
     ("fp8_row", "activation", 4, 0),
     ("fp8_block128", "weight", (1 << 31) - 128, 1 << 20),   # 2^51 elements
 ])
@@ -70,7 +74,7 @@ def test_unsupported_combinations():
     with pytest.raises(NotImplementedError):
         _sizes("w4a16_asym", "activation", 4, 128)
     with pytest.raises(NotImplementedError):
-        _sizes(8, "activation", 4, 128)
+        _sizes(9, "activation", 4, 128)
     with pytest.raises(NotImplementedError):
         _sizes("fp8_row", 2, 4, 128)
 

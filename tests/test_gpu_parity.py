@@ -109,7 +109,8 @@ def test_quantize_bit_exact(scheme, role, rows, cols):
 REPACK_CASES = [("mxfp8", "activation", 37, 384), ("mxfp8", "weight", 5, 96), ("mxfp4", "weight", 300, 1152),
                 ("mxfp4", "activation", 1, 64), ("w4a16_asym", "weight", 300, 1152), ("w4a16_sym", "weight", 7, 128),
                 ("w4a16_asym", "weight", 33, 4096), ("fp8_block128", "activation", 9, 256),
-                ("fp8_block128", "weight", 128, 384), ("fp8_row", "weight", 3, 64), ("int8_row", "activation", 6, 640)]
+                ("fp8_block128", "weight", 128, 384), ("fp8_row", "weight", 3, 64), ("int8_row", "activation", 6, 640),
+                ("mxfp4_dual", "activation", 37, 1024), ("mxfp4_dual", "weight", 300, 2048)]
 
 
 def _bytes(t):
@@ -126,11 +127,21 @@ def test_repack_canonical_bytes_on_device(scheme, role, rows, cols):
     q = pql.quantize(up(x), scheme, role)                       # packed device layout
     codes, scales, zeros = pql.to_canonical(q)
     assert np.array_equal(_bytes(codes), np.ascontiguousarray(ref["codes"]).view(np.uint8).reshape(-1))
-    assert np.array_equal(_bytes(scales), np.ascontiguousarray(ref["scales"]).view(np.uint8).reshape(-1))
+    want = np.ascontiguousarray(ref["scales"]).view(np.uint8).reshape(-1)
+    got = _bytes(scales)
+    if scheme == "mxfp4_dual":   # fine exponents, then the coarse scales from the next 256-byte boundary
+        off = -(-want.size // 256) * 256
+        assert np.array_equal(got[off:], np.ascontiguousarray(ref["coarse"], np.float32).view(np.uint8).reshape(-1))
+        got = got[:want.size]
+    assert np.array_equal(got, want)
     if ref["zeros"] is not None:
         assert np.array_equal(_bytes(zeros), np.ascontiguousarray(ref["zeros"]).view(np.uint8).reshape(-1))
     back = pql.from_canonical(scheme, role, rows, cols, codes, scales, zeros)
-    assert np.array_equal(_bytes(back.scales), _bytes(q.scales))
+    b, p = _bytes(back.scales), _bytes(q.scales)
+    if scheme == "mxfp4_dual":   # the bytes between the two levels are padding, not part of either
+        assert np.array_equal(b[:want.size], p[:want.size]) and np.array_equal(b[off:], p[off:])
+    else:
+        assert np.array_equal(b, p)
     if q.zeros is not None:
         assert np.array_equal(_bytes(back.zeros), _bytes(q.zeros))
 
