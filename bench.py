@@ -37,7 +37,7 @@ PEAK_HBM_GBS = 8000.0
 HEADLINE = ("fp8_block_dit", "fp8_block128")
 # every workload, the headline last (the largest GEMM: 1.16 TFLOP)
 RUNS = (("fp8_tensor_small", "fp8_tensor"), ("fp8_row_dit", "fp8_row"), ("mx_video_dit", "mxfp8"),
-        ("mx_video_dit", "mxfp4"), ("w4a16_dit", "w4a16_asym"), HEADLINE)
+        ("mx_video_dit", "mxfp4"), ("mx_video_dit", "mxfp4_dual"), ("w4a16_dit", "w4a16_asym"), HEADLINE)
 DESCRIPTION = {
     "fp8_tensor_small": "FP8 e4m3 per-tensor dynamic scales, M=256 K=512 N=512",
     "fp8_row_dit": "FP8 e4m3 per-token activation x per-channel weight scales, M=4096 K=3072 N=12288, "
@@ -54,7 +54,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--only", default=None, help="time only this workload (its line is then the last)")
+    p.add_argument("--only", default=None, help="time only this workload (NAME or NAME:SCHEME; its line is then "
+                                                "the last)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) three times, the "
@@ -166,7 +167,7 @@ def run_quantized(torch, pql, name, scheme, steps, warmup):
     ms = ev.ms()
     q_ms, g_ms = ms[0::2], ms[1::2]
     flops = 2.0 * M * N * K
-    peak = PEAK_TFLOPS["fp4" if scheme == "mxfp4" else "fp8"]
+    peak = PEAK_TFLOPS["fp4" if scheme.startswith("mxfp4") else "fp8"]
     ba, bw = quant_bytes(pql, scheme, "activation", M, K), quant_bytes(pql, scheme, "weight", N, K)
     qa, qw, gg = stats_us(q_ms), stats_us(evw.ms()), stats_us(g_ms)
     step_ms = total_ms / steps
@@ -326,7 +327,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    runs = [r for r in RUNS if args.only is None or r[0] == args.only]
+    runs = [r for r in RUNS if args.only is None or args.only in (r[0], f"{r[0]}:{r[1]}")]
     if not runs:
         print(f"unknown workload {args.only!r}", file=sys.stderr)
         sys.exit(2)
@@ -348,7 +349,7 @@ def main():
     g = head["gemm"]
     flops = 2 * head["M"] * head["N"] * head["K"]
     step_ms = head["step_us"] * 1e-3
-    is_mx4 = scheme == "mxfp4"
+    is_mx4 = scheme.startswith("mxfp4")
     result = {
         "metric": "qlinear TFLOP/s & quantize GB/s on 1 MI355X, % of MFMA/HBM peak",
         "value": round(flops / (step_ms * 1e-3) / 1e12, 2),

@@ -34,22 +34,21 @@ prefix key matches a layer when the layer equals it or continues it at a dot.
 The method names map to this library's schemes as: fp8 -> fp8_row (dynamic
 per-token activations, per-channel weights; fp8_tensor / fp8_block128 are
 selected with ``"scheme"``), int8 -> int8_row, mxfp8 -> mxfp8, mxfp4 ->
-mxfp4, auto_round / inc -> w4a16_asym.  Dual-scale MXFP4 has no kernel here:
-it resolves (so its routing can be checked) but ``scheme_for`` raises
-``NotImplementedError`` for the layers it would quantize.
+mxfp4, mxfp4_dualscale -> mxfp4_dual (online: the calibrated multiplier is
+all ones), auto_round / inc -> w4a16_asym.
 """
 from __future__ import annotations
 
 import re
 from dataclasses import dataclass, field
 
-# canonical method name -> default library scheme (None: routing only, no kernel)
+# canonical method name -> default library scheme
 METHODS = {
     "fp8": "fp8_row",
     "int8": "int8_row",
     "mxfp8": "mxfp8",
     "mxfp4": "mxfp4",
-    "mxfp4_dualscale": None,
+    "mxfp4_dualscale": "mxfp4_dual",
     "auto_round": "w4a16_asym",
     "inc": "w4a16_asym",
 }
@@ -59,7 +58,7 @@ SCHEME_CHOICES = {
     "int8": ("int8_row",),
     "mxfp8": ("mxfp8",),
     "mxfp4": ("mxfp4",),
-    "mxfp4_dualscale": (),
+    "mxfp4_dualscale": ("mxfp4_dual",),
     "auto_round": ("w4a16_asym", "w4a16_sym"),
     "inc": ("w4a16_asym", "w4a16_sym"),
 }
@@ -121,7 +120,6 @@ class MethodConfig:
             m = _BLOCK_RE.match(prefix)
             if m and int(m.group(1)) < self.num_bf16_fallback_layers:
                 return None
-            raise NotImplementedError(f"dual-scale MXFP4 (layer {prefix!r}) has no kernel in this library")
         return self.scheme
 
 

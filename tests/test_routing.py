@@ -76,13 +76,10 @@ def test_dualscale_fallback_priority():
     assert c.num_bf16_fallback_layers == 5                               # the default
     assert all(c.scheme_for(f"blocks.{i}.attn.to_q") is None for i in range(5))   # rule 2
     assert c.scheme_for("blocks.7.ffn.net.0") is None                    # rule 1, anywhere
-    with pytest.raises(NotImplementedError):                             # rule 3: dual-scale kernel
-        c.scheme_for("blocks.5.attn.to_q")
-    with pytest.raises(NotImplementedError):                             # outside blocks.N: quantized
-        c.scheme_for("condition_embedder.linear_1")
+    assert c.scheme_for("blocks.5.attn.to_q") == "mxfp4_dual"           # rule 3: the dual-scale kernel
+    assert c.scheme_for("condition_embedder.linear_1") == "mxfp4_dual"  # outside blocks.N: quantized
     c0 = R.build_quant_config({"method": "mxfp4_dualscale", "num_bf16_fallback_layers": 0})
-    with pytest.raises(NotImplementedError):
-        c0.scheme_for("blocks.0.attn.to_q")
+    assert c0.scheme_for("blocks.0.attn.to_q") == "mxfp4_dual"
     with pytest.raises(ValueError):
         R.build_quant_config({"method": "mxfp4_dualscale", "num_bf16_fallback_layers": -1})
 
