@@ -190,7 +190,7 @@ def exact_precondition(a, wq: dict, alpha=None, bias=None):
     (at most T, plus the bias) stays below 2^(24 - p); the check asks for 2^(21 - p),
     which also holds a matrix-core dot product that keeps two or three bits fewer.  For W4A16 the integer-code
     kernel also sums a (128 + q) and a (128 + z) per K-group, which must stay below
-    2^24 as integers (the activation is integer-valued here)."""
+    2^21 as integers (the activation is integer-valued here)."""
     from oracle.gemm import _a_hat   # the oracle's own dequantized operand
     A = _a_hat(a)
     W = oracle.dequant_exact(wq)
@@ -203,7 +203,8 @@ def exact_precondition(a, wq: dict, alpha=None, bias=None):
     assert float(t.max(initial=0.0)) * 2.0 ** p < 2.0 ** 21, "partial sums could exceed the exact range"
     if wq["scheme"].startswith("w4a16"):
         assert _grid_bits(A) == 0
-        assert float(np.abs(A).sum(axis=1).max(initial=0.0)) * 2 * 143 < 2.0 ** 21
+        per_group = np.abs(A).reshape(A.shape[0], -1, 128).sum(axis=2)   # the integer sums run per K-group
+        assert float(per_group.max(initial=0.0)) * 2 * 143 < 2.0 ** 21
 
 
 def assert_gemm(c_bits, a, wq: dict, what="", alpha=None, bias=None, flag=True):
