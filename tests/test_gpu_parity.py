@@ -264,6 +264,21 @@ def test_qlinear_equals_quantize_then_qgemm(scheme):
     assert torch.equal(y.reshape(M, N).view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("M,N,K", [(4300, 4224, 384), (4096, 4096, 1024)])
+def test_block128_qlinear_group_major_scales(M, N, K):
+    """qlinear's own block-128 quantize writes its scales group-major for the 256 x 256
+    kernel; the result equals quantize (canonical scales) + qgemm bit for bit, with and
+    without the alpha / bias epilogue."""
+    assert pql.kernel_name("qgemm", "fp8_block128", "activation", M, N, K) == "k_gemm_block256"
+    a = up(wl.small_case(31, M, K))
+    wq = pql.quantize(up(wl.small_case(32, N, K, 0.02)), "fp8_block128", "weight")
+    aq = pql.quantize(a, "fp8_block128", "activation")
+    assert torch.equal(pql.qlinear(a, wq).view(torch.int16), pql.qgemm(aq, wq).view(torch.int16))
+    bias = up(wl.small_case(33, 1, N, 0.5)[0])
+    assert torch.equal(pql.qlinear(a, wq, alpha=0.75, bias=bias).view(torch.int16),
+                       pql.qgemm(aq, wq, alpha=0.75, bias=bias).view(torch.int16))
+
+
 def test_schemes_give_different_outputs():
     """The pages' no-silent-fallback check: each scheme is a real, different computation."""
     M, N, K = 256, 256, 512
