@@ -227,7 +227,15 @@ pql_status pql_qgemm(int scheme, const void* a, const void* a_scales, const void
 /* The linear layer's forward: quantize the bf16 activation a[M, K] (row
  * stride lda) with the scheme's activation rule into `workspace`, then
  * qgemm against the quantized weight.  W4A16 uses a as-is (lda must equal K)
- * and needs no workspace.  C as for pql_qgemm. */
+ * and needs no workspace.  C as for pql_qgemm.
+ * A few tokens (1 <= M <= 16) under FP8_TENSOR, FP8_ROW, FP8_BLOCK128 or
+ * INT8_ROW take one fused launch instead ("vLLM-Omni Online Quantization
+ * complete guide", section "How online quantization works underneath": the
+ * activation quantize fused into the GEMM): each workgroup recomputes the
+ * activation's scales and codes on chip, with the same rule and the same
+ * codes as pql_quantize, and the workspace is neither needed nor touched
+ * (pql_workspace_size gives 0 for these shapes).  The result differs from
+ * quantize + qgemm only in the order of the fp32 partial sums. */
 pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda,
                        const void* w_codes, const void* w_scales, const void* w_zeros,
                        int64_t N, void* c, int64_t ldc, void* workspace,

@@ -58,12 +58,13 @@ def similarity(cand, ref) -> dict:
     else:
         rel = l2 / nr if nr > 0 else math.inf
     peak = float(np.max(r) - np.min(r))
+    ratio = peak * peak / mse if mse != 0.0 else math.inf
     if mse == 0.0:
         psnr = math.inf
-    elif peak == 0.0:
-        psnr = -math.inf
+    elif not ratio > 0.0:     # a zero range, or an infinite error: no signal above the noise
+        psnr = -math.inf if ratio == 0.0 or ratio != ratio else math.nan
     else:
-        psnr = 10.0 * math.log10(peak * peak / mse)
+        psnr = 10.0 * math.log10(ratio)
     return {"cosine_similarity": cosine_similarity(c, r), "mae": float(np.mean(ad)), "mse": mse,
             "rmse": math.sqrt(mse), "max_abs": float(np.max(ad)), "l2": l2, "relative_l2": rel,
             "psnr_db": psnr}

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpql.so")
-SOURCES = ("abi.cpp", "quant.hip", "layout.hip", "gemm.hip", "gemm32.hip", "gemm_block.hip", "gemm_block256.hip", "gemm_w4a16.hip", "gemm_dual.hip",
+SOURCES = ("abi.cpp", "quant.hip", "layout.hip", "gemm.hip", "gemm32.hip", "gemm_block.hip", "gemm_block256.hip", "gemm_w4a16.hip", "gemm_dual.hip", "qlinear_small.hip",
            "gemm_w4a16_mm.hip")
 ARCH = "gfx950"
 

@@ -242,6 +242,24 @@ pql_status check_gemm_shape(int scheme, int64_t M, int64_t N, int64_t K) {
   return PQL_OK;
 }
 
+// The fused small-M kernel's kind for a scheme, or -1 when it does not apply.
+int small_kind(int scheme, int64_t M, int64_t K) {
+  if (!pql::qlinear_small_applies(M, K)) return -1;
+  switch (scheme) {
+    case PQL_FP8_TENSOR: return pql::SMALL_TENSOR;
+    case PQL_FP8_ROW: return pql::SMALL_ROW;
+    case PQL_INT8_ROW: return pql::SMALL_INT8;
+    case PQL_FP8_BLOCK128: return pql::SMALL_BLOCK;
+  }
+  return -1;
+}
+
+size_t qlinear_ws_bytes(int scheme, int64_t M, int64_t K) {
+  if (small_kind(scheme, M, K) >= 0) return 0;   // the fused kernel keeps the quantized activation on chip
+  const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
+  return round256(s.codes) + round256(s.scales) + (scheme == PQL_FP8_TENSOR ? kTensorWs : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -276,9 +294,7 @@ pql_status pql_workspace_size(int op, int scheme, int role, int64_t M, int64_t N
     if (!valid_scheme(scheme)) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
     pql_status st = check_gemm_shape(scheme, M, N, K);
     if (st != PQL_OK) return st;
-    if (is_w4a16(scheme)) return ok();
-    const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
-    *bytes = round256(s.codes) + round256(s.scales) + (scheme == PQL_FP8_TENSOR ? kTensorWs : 0);
+    if (!is_w4a16(scheme)) *bytes = qlinear_ws_bytes(scheme, M, K);
     return ok();
   }
   return ok();
@@ -352,11 +368,6 @@ pql_status check_epilogue(int scheme, int64_t N, float alpha, const void* bias) 
   if (bias && !aligned16(bias)) return fail(PQL_ERR_INVALID_ARGUMENT, "bias must be 16-byte aligned");
   if (bias && N % 2) return fail(PQL_ERR_INVALID_ARGUMENT, "a bias needs an even N (got %lld)", (long long)N);
   return PQL_OK;
-}
-
-size_t qlinear_ws_bytes(int scheme, int64_t M, int64_t K) {
-  const Sizes s = sizes_of(scheme, PQL_ACTIVATION, M, K);
-  return round256(s.codes) + round256(s.scales) + (scheme == PQL_FP8_TENSOR ? kTensorWs : 0);
 }
 
 }  // namespace
@@ -443,6 +454,23 @@ pql_status run_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t 
                        const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
                        const void* bias, void* c, int64_t ldc, void* workspace, void* stream) {
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int sk = small_kind(scheme, M, K);
+  if (sk >= 0) {   // a few tokens: quantize inside the GEMM, one launch, no workspace traffic
+    pql::SmallArgs s;
+    s.a = static_cast<const uint16_t*>(a);
+    s.M = M;
+    s.K = K;
+    s.lda = lda;
+    s.a_static = static_cast<const float*>(a_static_scales);
+    s.w = static_cast<const uint8_t*>(w_codes);
+    s.w_scales = static_cast<const float*>(w_scales);
+    s.N = N;
+    s.alpha = alpha;
+    s.bias = static_cast<const uint16_t*>(bias);
+    s.c = static_cast<uint16_t*>(c);
+    s.ldc = ldc;
+    return launched(pql::launch_qlinear_small(sk, s, hs), "qlinear launch");
+  }
   if (is_w4a16(scheme))
     return launched(do_qgemm(scheme, a, nullptr, w_codes, w_scales, w_zeros, M, N, K, 1.0f, nullptr, c, ldc, hs),
                     "qlinear launch");
@@ -614,8 +642,15 @@ const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, 
         default: return scheme == PQL_W4A16_SYM ? "k_int4<sym>" : "k_int4<asym>";
       }
     case PQL_OP_DEQUANTIZE: return "k_dequant";
-    case PQL_OP_QGEMM:
     case PQL_OP_QLINEAR:
+      switch (small_kind(scheme, M, K)) {
+        case pql::SMALL_TENSOR: return "k_qlinear_small<fp8_tensor>";
+        case pql::SMALL_ROW: return "k_qlinear_small<fp8_row>";
+        case pql::SMALL_INT8: return "k_qlinear_small<int8_row>";
+        case pql::SMALL_BLOCK: return "k_qlinear_small<fp8_block128>";
+      }
+      [[fallthrough]];
+    case PQL_OP_QGEMM:
       if (is_w4a16(scheme)) return pql::gemm_w4a16_kernel_name(M, N, K);
       if (scheme == PQL_MXFP4_DUAL) return "k_gemm_mx4_dual";
       return pql::gemm_kernel_name(gemm_kind(scheme), M, N, K);

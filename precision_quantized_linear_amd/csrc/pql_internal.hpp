@@ -97,6 +97,24 @@ const char* gemm_kernel_name(GemmKind kind, int64_t M, int64_t N, int64_t K);
 // MXFP4 layout), a_coarse / w_coarse the coarse fp32 scales, group-major [K / 512, rows].
 hipError_t launch_gemm_mx4_dual(const GemmArgs& g, const float* a_coarse, const float* w_coarse, hipStream_t st);
 
+// Fused quantize + GEMM for M <= 16 tokens (qlinear only): the activation is quantized
+// inside the GEMM with the scheme's activation rule.
+enum SmallKindId { SMALL_TENSOR = 0, SMALL_ROW = 1, SMALL_INT8 = 2, SMALL_BLOCK = 3 };
+struct SmallArgs {
+  const uint16_t* a;        // bf16 [M, lda]
+  int64_t M, K, lda;
+  const float* a_static;    // static activation scales (TENSOR: [1], BLOCK: [M, K/128]) or null
+  const uint8_t* w;         // weight codes [N, K]
+  const float* w_scales;    // the weight's scales in its scheme's layout
+  int64_t N;
+  float alpha;
+  const uint16_t* bias;     // bf16 [N] or null
+  uint16_t* c;
+  int64_t ldc;
+};
+inline bool qlinear_small_applies(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K % 128 == 0; }
+hipError_t launch_qlinear_small(int kind, const SmallArgs& s, hipStream_t st);
+
 // W4A16: C = A (bf16) * dequant(Wq)^T
 // W4A16, M > 64: pipelined 256 x 128 tile kernel (N % 4 == 0, K % 128 == 0).
 bool w4a16_mm_supported(int64_t M, int64_t N, int64_t K);

@@ -1,0 +1,243 @@
+// Fused quantize + GEMM for a few tokens (M <= 16), gfx950.
+//
+// For one or a few tokens the separate activation quantize is pure overhead
+// ("vLLM-Omni Online Quantization complete guide", section "How online
+// quantization works underneath": the activation-quantize prologue fusion;
+// per-call quantize and dequant overhead dominating single requests on the
+// quantization page for diffusion transformers) and a 256 x 256 output tile
+// leaves most CUs idle.  This kernel streams the weight like a GEMV and
+// quantizes the activation inside: every workgroup owns 32 output columns and
+// all M <= 16 rows, reads the bf16 activation itself (it is tiny and stays in
+// L2), quantizes each K-chunk with the scheme's activation rule exactly as the
+// quantize kernels do (same scales, same codes) and feeds the codes straight
+// to the matrix core.  Schemes:
+//   TENSOR  FP8, one scale for the whole activation (max over its M rows)
+//   ROW     FP8, one scale per token
+//   INT8    int8 W8A8, one scale per token, int32 sums
+//   BLOCK   FP8, one scale per (token, 128-wide K-group), computed per chunk
+// with static (supplied) activation scales for TENSOR and BLOCK.  The weight
+// keeps its own layout and scales (per tensor, per channel, per 128 x 128
+// block) and the epilogue is the GEMMs' alpha * (...) + bias.
+//
+// Matrix core: v_mfma_scale_f32_16x16x128_f8f6f4 with unit scales (int8:
+// v_mfma_i32_16x16x64_i8 twice).  Lane l feeds row l % 16 with, for g = l / 16,
+// the 16 K-elements 16 g .. + 15 of a 128-element chunk in bytes 0-15 and
+// 64 + 16 g .. + 15 in bytes 16-31, for the activation and the weight alike
+// (so each K-element meets its partner whatever order the sums run in); lane l
+// then holds C[4 g + r][l % 16], r = 0..3.  The 4 waves take the K-chunks
+// round-robin and add their sums in LDS at the end.
+#include <algorithm>
+
+#include "gemm_common.hpp"
+#include "pql_device.hpp"
+#include "pql_internal.hpp"
+#include "quant_common.hpp"
+
+namespace pql {
+
+namespace {
+
+constexpr int kWaves = 4, kThreads = 64 * kWaves;
+constexpr int kCols = 32;   // output columns per workgroup (two blocks of 16)
+
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+
+template <int KIND>
+struct SmallKind {
+  static constexpr bool kInt8 = KIND == SMALL_INT8;
+  static constexpr bool kBlock = KIND == SMALL_BLOCK;
+  static constexpr bool kTensor = KIND == SMALL_TENSOR;
+};
+
+// 32 bf16 of the lane's row for one chunk -> 32 codes (FP8 or int8), in MFMA byte order.
+template <int KIND, bool STATIC>
+__device__ __forceinline__ void cast_chunk(const uint4 (&x)[4], float s, uint32_t (&q)[8]) {
+  const bool fast = s >= kSmallestFastScale;
+  const float rcp = fast ? __fdiv_rn(1.0f, s) : 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint2 v;
+    if constexpr (KIND == SMALL_INT8) v = fast ? int8_chunk<true>(x[i], s, rcp) : int8_chunk<false>(x[i], s, rcp);
+    else if constexpr (STATIC) v = fast ? fp8_chunk_sat<true>(x[i], s, rcp) : fp8_chunk_sat<false>(x[i], s, rcp);
+    else v = fast ? fp8_chunk<true>(x[i], s, rcp) : fp8_chunk<false>(x[i], s, rcp);
+    q[2 * i] = v.x;
+    q[2 * i + 1] = v.y;
+  }
+}
+
+template <int KIND, bool STATIC, bool EPI>
+__global__ __launch_bounds__(kThreads) void k_qlinear_small(const uint16_t* __restrict__ a, int64_t M, int64_t K,
+                                                          int64_t lda, const float* __restrict__ a_static,
+                                                          const uint8_t* __restrict__ w,
+                                                          const float* __restrict__ w_scales, int64_t N, float alpha,
+                                                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ c,
+                                                          int64_t ldc) {
+  using T = SmallKind<KIND>;
+  __shared__ float red[kWaves][16];
+  __shared__ float s_row[16];
+  __shared__ float part[kWaves][16][kCols + 1];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * kCols;
+  const int nk = (int)(K / 128);
+  const bool row_valid = r16 < M;
+  const uint16_t* arow = a + (int64_t)std::min<int64_t>(r16, M - 1) * lda;
+
+  // ---- per-token (or per-tensor) scales: the max of |x| over each row, from all threads
+  if constexpr (!T::kBlock) {
+    if constexpr (STATIC) {
+      if (t < 16) s_row[t] = a_static[0];
+    } else {
+      float pm[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        pm[m] = 0.0f;
+        if (m < M)
+          for (int64_t ch = t; ch < K / 8; ch += kThreads)
+            pm[m] = fmaxf(pm[m], chunk_absmax(ldg16(a + (int64_t)m * lda + ch * 8)));
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const float v = wave_max(pm[m]);
+        if (lane == 0) red[wave][m] = v;
+      }
+      __syncthreads();
+      if (t < 16) {
+        float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+        if constexpr (T::kTensor) {   // one scale: the max over every row
+          amax = 0.0f;
+          for (int m = 0; m < M; ++m) amax = fmaxf(amax, fmaxf(fmaxf(red[0][m], red[1][m]), fmaxf(red[2][m], red[3][m])));
+        }
+        s_row[t] = T::kInt8 ? int8_scale(amax) : fp8_scale(amax);
+      }
+    }
+    __syncthreads();
+  }
+  const float s_lane = T::kBlock ? 1.0f : s_row[r16];   // the lane's own row's scale
+
+  const uint8_t* wrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wrow[j] = w + std::min<int64_t>(n0 + 16 * j + r16, N - 1) * K;
+  const int64_t nblk = n0 / 128;   // block-128: the 32 columns lie in one weight block (N % 128 == 0)
+
+  v4f_t acc[2] = {v4f_t{0.f, 0.f, 0.f, 0.f}, v4f_t{0.f, 0.f, 0.f, 0.f}};
+  v4i acci[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+  for (int ck = wave; ck < nk; ck += kWaves) {
+    const int64_t k0 = (int64_t)ck * 128;
+    uint4 x[4] = {uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}};
+    if (row_valid) {
+      x[0] = ldg16(arow + k0 + 16 * g);
+      x[1] = ldg16(arow + k0 + 16 * g + 8);
+      x[2] = ldg16(arow + k0 + 64 + 16 * g);
+      x[3] = ldg16(arow + k0 + 64 + 16 * g + 8);
+    }
+    uint4 wv[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      wv[j][0] = ldg16_nt(wrow[j] + k0 + 16 * g);
+      wv[j][1] = ldg16_nt(wrow[j] + k0 + 64 + 16 * g);
+    }
+    float s = s_lane;
+    if constexpr (T::kBlock) {
+      if constexpr (STATIC) {
+        s = a_static[(int64_t)std::min<int64_t>(r16, M - 1) * nk + ck];
+      } else {   // the chunk is the row's K-group ck: its 128 elements are spread over lanes r16 + 16 g'
+        float m = fmaxf(fmaxf(chunk_absmax(x[0]), chunk_absmax(x[1])), fmaxf(chunk_absmax(x[2]), chunk_absmax(x[3])));
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        s = fp8_scale(m);
+      }
+    }
+    uint32_t q[8];
+    cast_chunk<KIND, STATIC>(x, s, q);
+    if constexpr (T::kInt8) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acci[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]},
+                                                        __builtin_bit_cast(v4i, wv[j][0]), acci[j], 0, 0, 0);
+        acci[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(v4i{(int)q[4], (int)q[5], (int)q[6], (int)q[7]},
+                                                        __builtin_bit_cast(v4i, wv[j][1]), acci[j], 0, 0, 0);
+      }
+    } else {
+      const v8i qa = v8i{(int)q[0], (int)q[1], (int)q[2], (int)q[3], (int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+      if constexpr (T::kBlock) {
+        // this chunk's partial sums, promoted with s_a[m, ck] s_w[block, ck]; the lane's
+        // outputs are rows 4 g + r, whose scales sit in lanes 4 g + r
+        float sr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sr[r] = __shfl(s, 4 * g + r);
+        const float sw = w_scales[nblk * nk + ck];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const v4f_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, gemm::cat(wv[j][0], wv[j][1]),
+                                                                          v4f_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0,
+                                                                          127);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(P[r], sr[r] * sw, acc[j][r]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, gemm::cat(wv[j][0], wv[j][1]), acc[j], 0, 0, 0, 127,
+                                                                    0, 127);
+      }
+    }
+  }
+
+  // ---- sums of the 4 waves, then the epilogue (the scales of the row / column GEMMs)
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      part[wave][4 * g + r][16 * j + r16] = T::kInt8 ? __int_as_float(acci[j][r]) : acc[j][r];
+  __syncthreads();
+  for (int e = t; e < 16 * kCols; e += kThreads) {
+    const int m = e / kCols, col = e - m * kCols;
+    const int64_t n = n0 + col;
+    if (m >= M || n >= N) continue;
+    float v;
+    if constexpr (T::kInt8) {
+      const int si = __float_as_int(part[0][m][col]) + __float_as_int(part[1][m][col]) +
+                     __float_as_int(part[2][m][col]) + __float_as_int(part[3][m][col]);
+      v = (float)si;
+    } else {
+      v = (part[0][m][col] + part[1][m][col]) + (part[2][m][col] + part[3][m][col]);
+    }
+    float out;
+    if constexpr (T::kBlock) {
+      out = EPI ? __builtin_fmaf(v, alpha, bias ? __uint_as_float((uint32_t)bias[n] << 16) : 0.0f) : v;
+    } else {
+      const float rs = alpha * s_row[m];
+      const float cs = T::kTensor ? w_scales[0] : w_scales[n];
+      out = EPI ? __builtin_fmaf(v * rs, cs, bias ? __uint_as_float((uint32_t)bias[n] << 16) : 0.0f) : v * rs * cs;
+    }
+    c[(int64_t)m * ldc + n] = (uint16_t)(gemm::pack_bf16x2(out, 0.0f) & 0xFFFFu);
+  }
+}
+
+template <int KIND, bool STATIC>
+hipError_t launch_kind(const SmallArgs& s, hipStream_t st) {
+  const dim3 grid((unsigned)((s.N + kCols - 1) / kCols)), block(kThreads);
+  if (s.alpha != 1.0f || s.bias)
+    hipLaunchKernelGGL((k_qlinear_small<KIND, STATIC, true>), grid, block, 0, st, s.a, s.M, s.K, s.lda, s.a_static,
+                       s.w, s.w_scales, s.N, s.alpha, s.bias, s.c, s.ldc);
+  else
+    hipLaunchKernelGGL((k_qlinear_small<KIND, STATIC, false>), grid, block, 0, st, s.a, s.M, s.K, s.lda, s.a_static,
+                       s.w, s.w_scales, s.N, s.alpha, s.bias, s.c, s.ldc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qlinear_small(int kind, const SmallArgs& s, hipStream_t st) {
+  const bool stat = s.a_static != nullptr;
+  switch (kind) {
+    case SMALL_TENSOR: return stat ? launch_kind<SMALL_TENSOR, true>(s, st) : launch_kind<SMALL_TENSOR, false>(s, st);
+    case SMALL_ROW: return launch_kind<SMALL_ROW, false>(s, st);
+    case SMALL_INT8: return launch_kind<SMALL_INT8, false>(s, st);
+    case SMALL_BLOCK: return stat ? launch_kind<SMALL_BLOCK, true>(s, st) : launch_kind<SMALL_BLOCK, false>(s, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pql

@@ -217,3 +217,36 @@ def assert_gemm(c_bits, a, wq: dict, what="", alpha=None, bias=None, flag=True):
     if wq["scheme"].startswith("w4a16"):
         wr, t_off = w4a16_terms(a, wq)
     return check_gemm(c_bits, c64, t, K, what, weight_round=wr, t_acc=t_off, flag=flag)
+
+
+def fused_exact_activation(scheme: str, M: int, K: int, seed: int) -> np.ndarray:
+    """bf16 bits of an activation whose quantization is exact: values on the code grid
+    times a power of two per scale unit (tensor, row, or (row, 128-group)), with one
+    element per unit at the format's largest code, so that every scale comes out a power
+    of two and every code reproduces its value.  The GEMM on the result is then exact
+    (``exact_precondition``), which lets the fused quantize + GEMM be checked bit for bit."""
+    rng = np.random.default_rng(seed)
+    if scheme == "int8_row":
+        vals, top, j0 = rng.integers(-16, 17, (M, K)).astype(np.float64), 127.0, -1
+    else:
+        # multiples of 32 up to 448 (all e4m3 codes): products then span few bits, so that
+        # the matrix core's dot product (which aligns its products to the largest one in a
+        # window narrower than fp32) adds them exactly
+        vals = 32.0 * rng.integers(-14, 15, (M, K)).astype(np.float64)
+        top, j0 = 448.0, -3
+    if scheme == "fp8_tensor":
+        j = np.full((M, K), float(rng.integers(-1, 1) + j0))
+        vals[int(rng.integers(0, M)), int(rng.integers(0, K))] = top * (1 if rng.integers(0, 2) else -1)
+    elif scheme in ("fp8_row", "int8_row"):
+        j = np.repeat(((np.arange(M) + seed) % 2 - 1 + j0)[:, None].astype(np.float64), K, axis=1)
+        vals[np.arange(M), rng.integers(0, K, M)] = top
+    else:   # fp8_block128: a power of two and a planted maximum per (row, 128-group)
+        G = K // 128
+        jg = (np.arange(M)[:, None] + np.arange(G)[None, :] + seed) % 2 - 1 + j0
+        j = np.repeat(jg.astype(np.float64), 128, axis=1)
+        for g in range(G):
+            vals[np.arange(M), 128 * g + rng.integers(0, 128, M)] = -top
+    x = vals * np.ldexp(1.0, j.astype(np.int64))
+    bits = F.f32_to_bf16_rne(x.astype(np.float32))
+    assert np.array_equal(F.bf16_to_f32(bits).astype(np.float64), x)
+    return bits

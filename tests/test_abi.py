@@ -85,6 +85,21 @@ def test_workspace_sizes():
     ws = pql.workspace_size("qlinear", "mxfp8", "activation", 20280, 5120, 5120)
     assert ws == 20280 * 5120 + ((20280 * 160 + 255) // 256) * 256
     assert pql.workspace_size("qlinear", "w4a16_asym", "activation", 16, 12288, 3072) == 0
+    # a few tokens under the FP8 / int8 schemes: the fused kernel needs no workspace
+    for s in ("fp8_tensor", "fp8_row", "fp8_block128", "int8_row"):
+        assert pql.workspace_size("qlinear", s, "activation", 16, 12288, 3072) == 0
+        assert pql.workspace_size("qlinear", s, "activation", 17, 12288, 3072) >= 17 * 3072
+    assert pql.workspace_size("qlinear", "mxfp8", "activation", 1, 12288, 3072) > 3072
+
+
+def test_small_m_qlinear_runs_the_fused_kernel():
+    for s in ("fp8_tensor", "fp8_row", "fp8_block128", "int8_row"):
+        for M in (1, 16):
+            assert pql.kernel_name("qlinear", s, "activation", M, 3072, 3072) == f"k_qlinear_small<{s}>"
+            assert pql.kernel_name("qgemm", s, "activation", M, 3072, 3072) != f"k_qlinear_small<{s}>"
+        assert not pql.kernel_name("qlinear", s, "activation", 17, 3072, 3072).startswith("k_qlinear_small")
+    for s in ("mxfp8", "mxfp4", "mxfp4_dual", "w4a16_asym"):
+        assert not pql.kernel_name("qlinear", s, "activation", 1, 3072, 3072).startswith("k_qlinear_small")
     with pytest.raises(ValueError):
         pql.workspace_size("qlinear", "fp8_row", "activation", 16, 128, 100)
 
