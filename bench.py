@@ -34,10 +34,16 @@ import numpy as np
 
 PEAK_TFLOPS = {"fp8": 5000.0, "fp4": 10100.0, "bf16": 2500.0, "int8": 5000.0}   # MI355X dense matrix peaks
 PEAK_HBM_GBS = 8000.0
+CPU_GEMM_ROWS = 512                   # rows of the headline GEMM the CPU oracle recomputes
 HEADLINE = ("fp8_block_dit", "fp8_block128")
 # every workload, the headline last (the largest GEMM: 1.16 TFLOP)
 RUNS = (("fp8_tensor_small", "fp8_tensor"), ("fp8_row_dit", "fp8_row"), ("mx_video_dit", "mxfp8"),
-        ("mx_video_dit", "mxfp4"), ("mx_video_dit", "mxfp4_dual"), ("w4a16_dit", "w4a16_asym"), HEADLINE)
+        ("mx_video_dit", "mxfp4"), ("mx_video_dit", "mxfp4_dual"), ("w4a16_dit", "w4a16_asym"),
+        ("fp8_decode", "fused"), HEADLINE)
+# --all adds the NEXT variants before the headline: int8 W8A8, the alpha / bias epilogue, static FP8 scales
+EXTRA = (("fp8_row_dit", "int8_row"), ("fp8_row_dit", "fp8_row+epilogue"), ("fp8_row_dit", "int8_row+epilogue"),
+         ("fp8_block_dit", "fp8_block128+epilogue"), ("fp8_block_dit", "fp8_block128+static"),
+         ("fp8_tensor_small", "fp8_tensor+static"))
 DESCRIPTION = {
     "fp8_tensor_small": "FP8 e4m3 per-tensor dynamic scales, M=256 K=512 N=512",
     "fp8_row_dit": "FP8 e4m3 per-token activation x per-channel weight scales, M=4096 K=3072 N=12288, "
@@ -46,6 +52,8 @@ DESCRIPTION = {
                      "M=8192 K=5120 N=13824",
     "mx_video_dit": "OCP MX (E8M0 per 32 K), M=20280 K=5120 N=5120, 0.5% K-channel outliers x50",
     "w4a16_dit": "W4A16 int4 group-128 asymmetric, K=3072 N=12288",
+    "fp8_decode": "FP8 per-token / block-128 qlinear for 1 and 16 tokens (fused activation quantize + GEMM), "
+                  "K=3072 N=12288",
 }
 
 
@@ -57,6 +65,8 @@ def parse():
     p.add_argument("--only", default=None, help="time only this workload (NAME or NAME:SCHEME; its line is then "
                                                 "the last)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--all", action="store_true", help="also time int8 W8A8, the alpha / bias epilogue and static "
+                                                      "FP8 scales (before the headline)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) three times, the "
                         "reference dispatch that scales FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -135,7 +145,11 @@ def _rate(x, unit_scale):
 
 # ----------------------------------------------------------------------------- one FP8 / MX workload
 def run_quantized(torch, pql, name, scheme, steps, warmup):
+    """One FP8 / MX / int8 workload.  ``scheme`` may carry a variant: "+epilogue" (the GEMM
+    with alpha = 0.5 and a bf16 bias), "+static" (the activation quantized with supplied
+    scales: the dynamic scales of the same input, as a calibrated scale would be)."""
     import workloads as wl
+    scheme, _, variant = scheme.partition("+")
     w = wl.WORKLOADS[name]
     M, N, K = w.M, w.N, w.K
     a_bits, w_bits = wl.activation(w), wl.weight(w)
@@ -146,6 +160,9 @@ def run_quantized(torch, pql, name, scheme, steps, warmup):
     wq = pql.quantize(w0, scheme, "weight", workspace=qws)
     aq = pql.quantize(a0, scheme, "activation", workspace=qws)
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    static = aq.scales.clone() if variant == "static" else None
+    bias = up(torch, wl.small_case(7, 1, N, 0.5)[0]) if variant == "epilogue" else None
+    alpha = 0.5 if variant == "epilogue" else 1.0
 
     # weight quantize (done once at load in a layer; timed here for its bandwidth)
     def wstep(i, ev):
@@ -155,8 +172,11 @@ def run_quantized(torch, pql, name, scheme, steps, warmup):
 
     # the step: quantize A, then the GEMM
     def step(i, ev):
-        fq = lambda: pql.quantize(acts[i % len(acts)], scheme, "activation", workspace=qws, out=aq)
-        fg = lambda: pql.qgemm(aq, wq, out=out)
+        if static is None:
+            fq = lambda: pql.quantize(acts[i % len(acts)], scheme, "activation", workspace=qws, out=aq)
+        else:
+            fq = lambda: pql.quantize_static(acts[i % len(acts)], scheme, "activation", static, out=aq)
+        fg = lambda: pql.qgemm(aq, wq, out=out, alpha=alpha, bias=bias)
         if ev:
             ev(fq)
             ev(fg)
@@ -167,19 +187,21 @@ def run_quantized(torch, pql, name, scheme, steps, warmup):
     ms = ev.ms()
     q_ms, g_ms = ms[0::2], ms[1::2]
     flops = 2.0 * M * N * K
-    peak = PEAK_TFLOPS["fp4" if scheme.startswith("mxfp4") else "fp8"]
+    peak = PEAK_TFLOPS["fp4" if scheme.startswith("mxfp4") else "int8" if scheme == "int8_row" else "fp8"]
     ba, bw = quant_bytes(pql, scheme, "activation", M, K), quant_bytes(pql, scheme, "weight", N, K)
     qa, qw, gg = stats_us(q_ms), stats_us(evw.ms()), stats_us(g_ms)
     step_ms = total_ms / steps
     line = {
-        "kind": "workload", "workload": name, "scheme": scheme, "M": M, "N": N, "K": K,
+        "kind": "workload", "workload": name, "scheme": scheme + (f"+{variant}" if variant else ""),
+        "M": M, "N": N, "K": K,
         "step_us": round(step_ms * 1e3, 2), "step_tflops": round(flops / (step_ms * 1e-3) / 1e12, 1),
-        "gemm": {"kernel": pql.kernel_name("qgemm", scheme, "activation", M, N, K),
+        "gemm": {"kernel": pql.kernel_name("qgemm", scheme, "activation", M, N, K) + ("+epilogue" if bias is not None else ""),
                  **{k: round(v, 2) for k, v in gg.items()},
                  "tflops": round(flops / (gg["mean_us"] * 1e-6) / 1e12, 1),
                  "mfma_frac": round(flops / (gg["mean_us"] * 1e-6) / 1e12 / peak, 4),
                  "mfma_frac_median": round(flops / (gg["median_us"] * 1e-6) / 1e12 / peak, 4), "peak_tflops": peak},
-        "quant_a": {"kernel": pql.kernel_name("quantize", scheme, "activation", M, N, K),
+        "quant_a": {"kernel": pql.kernel_name("quantize", scheme, "activation", M, N, K) if static is None
+                    else "k_fp8_static",
                     **{k: round(v, 2) for k, v in qa.items()}, "bytes": ba,
                     "gbs_median": round(ba / (qa["median_us"] * 1e-6) / 1e9, 1),
                     "hbm_frac_median": round(ba / (qa["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
@@ -188,8 +210,11 @@ def run_quantized(torch, pql, name, scheme, steps, warmup):
                     "gbs_median": round(bw / (qw["median_us"] * 1e-6) / 1e9, 1),
                     "hbm_frac_median": round(bw / (qw["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
     }
-    keep = {"a_bits": a_bits, "w_bits": w_bits} if (name, scheme) == HEADLINE else {}
-    del acts, wts, aq, wq, out
+    keep = {}
+    if (name, scheme) == HEADLINE and not variant:   # the output rows the CPU oracle leg recomputes (every copy of A is equal)
+        keep = {"a_bits": a_bits, "w_bits": w_bits,
+                "c_rows": out[:CPU_GEMM_ROWS].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)}
+    del acts, wts, aq, wq, out, static, bias
     torch.cuda.empty_cache()
     return line, keep
 
@@ -231,6 +256,44 @@ def run_w4a16(torch, pql, steps, warmup):
     return lines
 
 
+# ----------------------------------------------------------------------------- few-token qlinear
+def run_decode(torch, pql, steps, warmup):
+    """qlinear for 1 and 16 tokens on the per-token FP8 workload's weight (N=12288, K=3072):
+    one fused launch that quantizes the activation inside the GEMM.  Weight copies rotate
+    (>= 1 GiB) so every call streams the weight from HBM; timed per call with HIP events."""
+    import workloads as wl
+    w = wl.WORKLOADS["fp8_row_dit"]
+    w0 = up(torch, wl.weight(w))
+    lines = []
+    for scheme in ("fp8_row", "fp8_block128"):
+        wq = pql.quantize(w0, scheme, "weight")
+        wbytes = wq.codes.numel() * wq.codes.element_size() + wq.scales.numel() * 4
+        copies = [wq] + [pql.QTensor(wq.scheme, wq.role, wq.rows, wq.cols, wq.codes.clone(), wq.scales.clone(),
+                                     None) for _ in range(copies_for(wbytes) - 1)]
+        for M in (1, 16):
+            a0 = up(torch, wl.activation(w, M))
+            out = torch.empty((M, w.N), dtype=torch.bfloat16, device="cuda")
+
+            def step(i, ev):
+                f = lambda: pql.qlinear(a0, copies[i % len(copies)], out=out)
+                ev(f) if ev else f()
+            total_ms, ev = timed(torch, step, steps, warmup)
+            gg = stats_us(ev.ms())
+            byts = wbytes + 2 * M * w.K + 2 * M * w.N
+            lines.append({"kind": "workload", "workload": "fp8_decode", "scheme": scheme, "M": M, "N": w.N,
+                          "K": w.K, "step_us": round(total_ms / steps * 1e3, 2),
+                          "gemm": {"kernel": pql.kernel_name("qlinear", scheme, "activation", M, w.N, w.K),
+                                   **{k: round(v, 2) for k, v in gg.items()},
+                                   "gbs_median": round(byts / (gg["median_us"] * 1e-6) / 1e9, 1),
+                                   "hbm_frac_median": round(byts / (gg["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                                   "bytes": byts}})
+            del a0, out
+        del copies, wq
+    del w0
+    torch.cuda.empty_cache()
+    return lines
+
+
 # ----------------------------------------------------------------------------- CPU oracle
 def host_info():
     model = platform.processor() or "unknown"
@@ -253,12 +316,16 @@ def host_info():
     return model, blas, threads, len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(a_bits, w_bits, name, scheme, gemm_rows=512):
+def cpu_baseline(a_bits, w_bits, name, scheme, c_rows=None, gemm_rows=None):
     """The oracle, as it stands, on the headline workload: quantize A (full size, NumPy,
     one core), quantize W (full size, one core) and the float64 GEMM on a row sample
     (BLAS threads), each timed once.  value = the oracle's step rate (quantize A + the
-    GEMM extrapolated from the sample to all M rows), in the metric's TFLOP/s."""
+    GEMM extrapolated from the sample to all M rows), in the metric's TFLOP/s.  With the
+    GPU's output rows given, the similarity report of those rows against the oracle's
+    (cosine, MAE, MSE / RMSE, max |diff|, L2, relative L2, PSNR) is added."""
     import oracle
+    from oracle import metrics
+    gemm_rows = gemm_rows or CPU_GEMM_ROWS
     M, K = a_bits.shape
     N = w_bits.shape[0]
     model, blas, threads, affinity = host_info()
@@ -271,7 +338,7 @@ def cpu_baseline(a_bits, w_bits, name, scheme, gemm_rows=512):
     rows = min(gemm_rows, M)
     a_rows = dict(aq, codes=aq["codes"][:rows], scales=aq["scales"][:rows], rows=rows)
     t0 = time.perf_counter()
-    oracle.gemm_ref(a_rows, wq)
+    c64 = oracle.gemm_ref(a_rows, wq)
     t_g = time.perf_counter() - t0
     t_g_full = t_g * M / rows
     flops = 2.0 * M * N * K
@@ -282,7 +349,12 @@ def cpu_baseline(a_bits, w_bits, name, scheme, gemm_rows=512):
                       f"extrapolated to all rows; value = 2MNK / (quantize A + GEMM)",
             "quantize_a_s": round(t_qa, 3), "quantize_w_s": round(t_qw, 3), "gemm_sample_s": round(t_g, 3),
             "gemm_full_s_est": round(t_g_full, 2), "host_cpu": model, "blas": blas, "blas_threads": threads,
-            "affinity_cpus": affinity}
+            "affinity_cpus": affinity,
+            **({"similarity_gpu_vs_oracle": {
+                "rows": rows, **{k: float(f"{v:.6g}") for k, v in metrics.similarity(
+                    oracle.bf16_to_f32(c_rows[:rows]).astype(np.float64), c64).items()},
+                "meets_starting_thresholds": bool(metrics.meets_starting_thresholds(metrics.similarity(
+                    oracle.bf16_to_f32(c_rows[:rows]).astype(np.float64), c64)))}} if c_rows is not None else {})}
 
 
 def measured_traffic(profile: str):
@@ -308,8 +380,9 @@ def summary_of(line):
                   "quant_a_hbm_frac_median": line["quant_a"]["hbm_frac_median"],
                   "quant_w_hbm_frac_median": line["quant_w"]["hbm_frac_median"]})
     else:
-        s.update({"gemm_hbm_frac_median": line["gemm"]["hbm_frac_median"],
-                  "gemm_bf16_mfma_frac": line["gemm"]["mfma_frac_bf16"]})
+        s.update({"gemm_hbm_frac_median": line["gemm"]["hbm_frac_median"]})
+        if line["gemm"].get("mfma_frac_bf16") is not None:
+            s["gemm_bf16_mfma_frac"] = line["gemm"]["mfma_frac_bf16"]
     return s
 
 
@@ -327,15 +400,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    runs = [r for r in RUNS if args.only is None or args.only in (r[0], f"{r[0]}:{r[1]}")]
+    every = RUNS[:-1] + (EXTRA if args.all else ()) + RUNS[-1:]
+    runs = [r for r in every if args.only is None or args.only in (r[0], f"{r[0]}:{r[1]}")]
     if not runs:
         print(f"unknown workload {args.only!r}", file=sys.stderr)
         sys.exit(2)
     summary, head, keep = {}, None, {}
     for name, scheme in runs:
-        if name == "w4a16_dit":
-            for line in run_w4a16(torch, pql, args.steps, args.warmup):
-                summary[f"w4a16_dit M={line['M']}"] = summary_of(line)
+        if name in ("w4a16_dit", "fp8_decode"):
+            lines = (run_w4a16 if name == "w4a16_dit" else run_decode)(torch, pql, args.steps, args.warmup)
+            for line in lines:
+                summary[f"{name} {line['scheme']} M={line['M']}"] = summary_of(line)
                 print(json.dumps(line), flush=True)
                 head = line
             continue
@@ -384,7 +459,7 @@ def main():
                               "p90_us": g["p90_us"], "algorithmic_flops": flops}
     result["workloads"] = summary
     if not args.no_cpu and keep:
-        result["cpu_baseline"] = cpu_baseline(keep["a_bits"], keep["w_bits"], name, scheme)
+        result["cpu_baseline"] = cpu_baseline(keep["a_bits"], keep["w_bits"], name, scheme, keep.get("c_rows"))
     print(json.dumps(result), flush=True)
 
 

@@ -152,7 +152,7 @@ int pql_version(void);
 const char* pql_last_error(void);
 
 /* Byte sizes of the codes, scales and zero-point buffers of a quantized
- * [rows, cols] tensor in the canonical layout (zeros_bytes is 0 except for
+ * [rows, cols] tensor in the packed layout (zeros_bytes is 0 except for
  * W4A16).  Size outputs are host pointers; any may be NULL.
  * Errors: INVALID_ARGUMENT for negative sizes or cols / rows that the scheme
  * cannot block (cols % 32 for FP8 tensor/row, INT8_ROW and MX, cols % 128 for
@@ -197,7 +197,7 @@ pql_status pql_workspace_size(int op, int scheme, int role, int64_t M, int64_t N
                               int64_t K, size_t* bytes);
 
 /* Quantize a bf16 tensor x[rows, cols] (row stride ldx elements) into the
- * canonical layout.  Activation role: rows = M; weight role: rows = N.
+ * packed layout.  Activation role: rows = M; weight role: rows = N.
  * `zeros` is written for W4A16 only (may be NULL otherwise).  The scales are
  * dynamic (computed from x).  FP8_TENSOR needs `workspace` of at least
  * pql_workspace_size(PQL_OP_QUANTIZE, ...) bytes; other schemes ignore it.
@@ -207,7 +207,7 @@ pql_status pql_quantize(int scheme, int role, const void* x, int64_t rows, int64
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* y[rows, cols] (bf16, row stride ldy) = bf16_RNE(fp32(decode(code) * scale))
- * (W4A16: bf16_RNE((q - z) * s)).  Inputs in the canonical layout. */
+ * (W4A16: bf16_RNE((q - z) * s)).  Inputs in the packed layout. */
 pql_status pql_dequantize(int scheme, int role, const void* codes, const void* scales,
                           const void* zeros, int64_t rows, int64_t cols, void* y,
                           int64_t ldy, void* stream);
@@ -215,7 +215,7 @@ pql_status pql_dequantize(int scheme, int role, const void* codes, const void* s
 /* C[M, N] (bf16, row stride ldc) = A_hat * W_hat^T on already-quantized
  * operands, fp32 accumulation, bf16 round-to-nearest-even output.
  *   FP8 / MX schemes: a = activation codes [M, K], a_scales its scales
- *   (canonical activation layout); w_codes / w_scales the weight's.
+ *   (packed activation layout); w_codes / w_scales the weight's.
  *   W4A16: a = bf16 activation [M, K] (contiguous), a_scales unused (NULL),
  *   w_zeros required.
  * K must be a multiple of 128; M, N >= 1 may be ragged (tails are masked);
@@ -245,7 +245,7 @@ pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t 
  * scale is supplied instead of computed from x ("[vLLM] Other quantization:
  * FP8, ModelOpt, INC, TorchAO, Quark", section "FP8": the static tensor-wise
  * and static 128-block symmetric scheme keys).  `scales` (device, read only)
- * is in the scheme's canonical scale layout for `role` (f32 [1]; f32
+ * is in the scheme's scale layout for `role` (f32 [1]; f32
  * [rows, cols/128] for activations, f32 [rows/128, cols/128] for weights) and
  * must hold finite positive values (not checked on the device: a zero, NaN or
  * infinite scale gives meaningless codes).  codes = e4m3fn(fp32(x / s)),

@@ -528,8 +528,8 @@ pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64
   pql_status st = check_qlinear(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha, bias,
                                 c, ldc);
   if (st != PQL_OK || M == 0) return st == PQL_OK ? ok() : st;
-  if (!is_w4a16(scheme)) {
-    const size_t need = qlinear_ws_bytes(scheme, M, K);
+  const size_t need = is_w4a16(scheme) ? 0 : qlinear_ws_bytes(scheme, M, K);
+  if (need) {   // W4A16 and the fused few-token kernel need none (the pointer may then be NULL)
     if (!workspace || workspace_bytes < need)
       return fail(PQL_ERR_WORKSPACE, "qlinear needs a %zu-byte workspace (got %zu)", need,
                   workspace ? workspace_bytes : (size_t)0);

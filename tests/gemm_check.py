@@ -6,7 +6,7 @@ Two kinds of check, both on every output element that a test compares:
 * ``check_gemm``: random operands.  Besides the relative Frobenius gate of
   1e-2, every element must satisfy
 
-      |C_gpu - C64| <= 2^-8 |C64| + 2 K 2^-24 T (+ the W4A16 terms below),
+      |C_gpu - C64| <= 2^-8 |C64| + 8 K 2^-24 T (+ the W4A16 terms below),
 
   with C64 the oracle's exact float64 product and T = sum_k |a_hat_k w_hat_k|
   (``oracle.gemm_abs_ref``).  2^-8 |C64| covers the final rounding to bf16

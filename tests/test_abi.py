@@ -184,6 +184,10 @@ def test_qlinear_validation():
     assert q(ws=None, wsb=0) == pql.PQL_ERR_WORKSPACE
     assert q(lda=250) == pql.PQL_ERR_INVALID_ARGUMENT
     assert q(K=96, lda=96) == pql.PQL_ERR_INVALID_ARGUMENT
+    # 1-16 tokens under FP8 / int8 run the fused kernel: no workspace, so a NULL one passes the checks
+    for scheme in ("fp8_tensor", "fp8_row", "fp8_block128", "int8_row"):
+        assert q(scheme=S[scheme], ws=None, wsb=0) != pql.PQL_ERR_WORKSPACE
+    assert q(scheme=S["fp8_row"], M=17, ws=None, wsb=0) == pql.PQL_ERR_WORKSPACE
 
 
 def test_dequantize_validation():
