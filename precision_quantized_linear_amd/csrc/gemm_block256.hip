@@ -132,12 +132,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_block256(GemmArgs g) {
     const int rg = here ? lr : 0;
     const TileRsrc tr = here ? cur : nxt;   // by value: a select of the (scalar) fields
     uint8_t* const base = smem + slot * kRegion;
+    // the scales first: the activation scales are a gather (one cache line per row), and
+    // issued ahead of the code lines they no longer finish last
+    if (wave < 4) lds_load4_so(tr.sa, sa_lds + slot * kSaBytes + wave * 256, voff_sa, rg * 4);
+    lds_load4_so(tr.sw, sw_lds + (slot * kWaves + wave) * kSwBytes, 0, rg * 4);
 #pragma unroll
     for (int p = 0; p < 4; ++p) lds_load16_so(tr.a, base + (wave * 32 + 8 * p) * kRow, voff[p], rg * kRow);
 #pragma unroll
     for (int p = 0; p < 4; ++p) lds_load16_so(tr.w, base + kOp + (wave * 32 + 8 * p) * kRow, voff[p], rg * kRow);
-    if (wave < 4) lds_load4_so(tr.sa, sa_lds + slot * kSaBytes + wave * 256, voff_sa, rg * 4);
-    lds_load4_so(tr.sw, sw_lds + (slot * kWaves + wave) * kSwBytes, 0, rg * 4);
   };
 
   // ---- fragments: 32x32x64 operands, lane row l % 32; slice h (bytes 64 h ..

@@ -265,10 +265,10 @@ def test_qlinear_equals_quantize_then_qgemm(scheme):
 
 
 @pytest.mark.parametrize("M,N,K", [(4300, 4224, 384), (4096, 4096, 1024)])
-def test_block128_qlinear_group_major_scales(M, N, K):
-    """qlinear's own block-128 quantize writes its scales group-major for the 256 x 256
-    kernel; the result equals quantize (canonical scales) + qgemm bit for bit, with and
-    without the alpha / bias epilogue."""
+def test_block128_qlinear_equals_quantize_then_qgemm(M, N, K):
+    """qlinear on shapes that run the 256 x 256 kernel (its own quantize into the
+    workspace, then the GEMM) equals quantize + qgemm bit for bit, with and without the
+    alpha / bias epilogue."""
     assert pql.kernel_name("qgemm", "fp8_block128", "activation", M, N, K) == "k_gemm_block256"
     a = up(wl.small_case(31, M, K))
     wq = pql.quantize(up(wl.small_case(32, N, K, 0.02)), "fp8_block128", "weight")
