@@ -25,7 +25,9 @@
  *     nothing is enqueued and pql_last_error() describes the problem.
  *   - Element sizes: bf16 = 2 bytes, fp32 = 4 bytes.  Leading dimensions
  *     (ldx, ldy, lda, ldc) are in elements.  Device pointers must be 16-byte
- *     aligned and leading dimensions multiples of 8 elements.
+ *     aligned and leading dimensions multiples of 8 elements (ldc: any value
+ *     >= N).  The span a leading dimension addresses, (rows - 1) * ld + cols,
+ *     must stay within 2^40 elements (INVALID_ARGUMENT otherwise).
  *
  * Packed layouts: what every call below except pql_repack produces and
  * consumes, laid out for the GEMM kernels (per scheme; rows = M for

@@ -60,6 +60,20 @@ bool has_epilogue(int s) { return s == PQL_FP8_TENSOR || s == PQL_FP8_ROW || s =
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// A leading dimension: at least `cols`, a multiple of 8 where asked, and the addressed
+// span (rows - 1) * ld + cols at most 2^40 elements, so that every in-kernel offset
+// (row * ld in 64-bit arithmetic) stays in range.
+constexpr int64_t kMaxSpan = int64_t(1) << 40;
+pql_status check_ld(const char* name, int64_t ld, int64_t rows, int64_t cols, bool mult8) {
+  if (ld < cols || (mult8 && ld % 8))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "%s must be >= %lld%s (got %lld)", name, (long long)cols,
+                mult8 ? " and a multiple of 8" : "", (long long)ld);
+  if (rows > 1 && ld > (kMaxSpan - cols) / (rows - 1))
+    return fail(PQL_ERR_INVALID_ARGUMENT, "%s = %lld spans more than 2^40 elements over %lld rows", name,
+                (long long)ld, (long long)rows);
+  return PQL_OK;
+}
+
 int64_t k_granule(int scheme) {
   return scheme == PQL_MXFP4_DUAL ? 512 : (scheme == PQL_FP8_BLOCK128 || is_w4a16(scheme)) ? 128 : 32;
 }
@@ -305,8 +319,7 @@ pql_status pql_quantize(int scheme, int role, const void* x, int64_t rows, int64
   pql_status st = check_scheme_role(scheme, role);
   if (st != PQL_OK) return st;
   if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
-  if (ldx < cols || ldx % 8) return fail(PQL_ERR_INVALID_ARGUMENT, "ldx must be >= cols and a multiple of 8 (got %lld)",
-                                         (long long)ldx);
+  if ((st = check_ld("ldx", ldx, rows, cols, true)) != PQL_OK) return st;
   if (rows == 0) return ok();
   if (!x || !codes || !scales) return fail(PQL_ERR_INVALID_ARGUMENT, "x, codes and scales must be non-NULL");
   if (is_w4a16(scheme) && !zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for W4A16");
@@ -329,8 +342,7 @@ pql_status pql_dequantize(int scheme, int role, const void* codes, const void* s
   pql_status st = check_scheme_role(scheme, role);
   if (st != PQL_OK) return st;
   if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
-  if (ldy < cols || ldy % 8) return fail(PQL_ERR_INVALID_ARGUMENT, "ldy must be >= cols and a multiple of 8 (got %lld)",
-                                         (long long)ldy);
+  if ((st = check_ld("ldy", ldy, rows, cols, true)) != PQL_OK) return st;
   if (rows == 0) return ok();
   if (!codes || !scales || !y) return fail(PQL_ERR_INVALID_ARGUMENT, "codes, scales and y must be non-NULL");
   if (is_w4a16(scheme) && !zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "zeros must be non-NULL for W4A16");
@@ -382,8 +394,7 @@ pql_status pql_quantize_static(int scheme, int role, const void* x, int64_t rows
     return fail(PQL_ERR_UNSUPPORTED, "static scales are defined for FP8_TENSOR and FP8_BLOCK128 only (got %s)",
                 scheme_name(scheme));
   if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
-  if (ldx < cols || ldx % 8) return fail(PQL_ERR_INVALID_ARGUMENT, "ldx must be >= cols and a multiple of 8 (got %lld)",
-                                         (long long)ldx);
+  if ((st = check_ld("ldx", ldx, rows, cols, true)) != PQL_OK) return st;
   if (rows == 0) return ok();
   if (!x || !codes || !scales) return fail(PQL_ERR_INVALID_ARGUMENT, "x, scales and codes must be non-NULL");
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
@@ -403,7 +414,7 @@ pql_status pql_qgemm_ex(int scheme, const void* a, const void* a_scales, const v
   pql_status st = check_gemm_shape(scheme, M, N, K);
   if (st != PQL_OK) return st;
   if ((st = check_epilogue(scheme, N, alpha, bias)) != PQL_OK) return st;
-  if (ldc < N) return fail(PQL_ERR_INVALID_ARGUMENT, "ldc must be >= N (got %lld)", (long long)ldc);
+  if ((st = check_ld("ldc", ldc, M, N, false)) != PQL_OK) return st;
   if (M == 0) return ok();
   if (!a || !w_codes || !w_scales || !c) return fail(PQL_ERR_INVALID_ARGUMENT, "a, w_codes, w_scales and c must be non-NULL");
   if (!is_w4a16(scheme) && !a_scales) return fail(PQL_ERR_INVALID_ARGUMENT, "a_scales must be non-NULL");
@@ -437,9 +448,9 @@ pql_status check_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_
   if (a_static_scales && scheme != PQL_FP8_TENSOR && scheme != PQL_FP8_BLOCK128)
     return fail(PQL_ERR_UNSUPPORTED, "static activation scales are defined for FP8_TENSOR and FP8_BLOCK128 only (got %s)",
                 scheme_name(scheme));
-  if (ldc < N) return fail(PQL_ERR_INVALID_ARGUMENT, "ldc must be >= N (got %lld)", (long long)ldc);
-  if (is_w4a16(scheme) ? lda != K : (lda < K || lda % 8))
-    return fail(PQL_ERR_INVALID_ARGUMENT, is_w4a16(scheme) ? "W4A16 needs lda == K" : "lda must be >= K and a multiple of 8");
+  if ((st = check_ld("ldc", ldc, M, N, false)) != PQL_OK) return st;
+  if (is_w4a16(scheme) && lda != K) return fail(PQL_ERR_INVALID_ARGUMENT, "W4A16 needs lda == K");
+  if ((st = check_ld("lda", lda, M, K, true)) != PQL_OK) return st;
   if (M == 0) return ok();
   if (!a || !w_codes || !w_scales || !c) return fail(PQL_ERR_INVALID_ARGUMENT, "a, w_codes, w_scales and c must be non-NULL");
   if (is_w4a16(scheme) && !w_zeros) return fail(PQL_ERR_INVALID_ARGUMENT, "w_zeros must be non-NULL for W4A16");

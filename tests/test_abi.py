@@ -151,6 +151,8 @@ def test_quantize_validation():
     assert _quantize(scheme=S["fp8_tensor"], ws=_p(16384), wsb=64) == pql.PQL_ERR_WORKSPACE
     assert _quantize(scheme=9) == pql.PQL_ERR_UNSUPPORTED
     assert _quantize(rows=0) == pql.PQL_OK                                 # empty: no-op
+    assert _quantize(ldx=(1 << 63) - 8) == pql.PQL_ERR_INVALID_ARGUMENT    # row offsets would overflow
+    assert _quantize(rows=1 << 20, ldx=1 << 21) == pql.PQL_ERR_INVALID_ARGUMENT   # span over 2^40 elements
     assert "ldx" in _last_error_after(lambda: _quantize(ldx=120))
 
 
@@ -174,6 +176,7 @@ def test_qgemm_validation():
     assert g(scheme=S["w4a16_asym"], wz=_p(4100)) == pql.PQL_ERR_INVALID_ARGUMENT   # misaligned zero-points
     assert g(M=1 << 30, N=1 << 30, ldc=1 << 30) == pql.PQL_ERR_INVALID_ARGUMENT      # 2^48 output tiles
     assert g(M=0) == pql.PQL_OK
+    assert g(ldc=(1 << 63) - 1) == pql.PQL_ERR_INVALID_ARGUMENT               # row offsets would overflow
 
 
 def test_qlinear_validation():
