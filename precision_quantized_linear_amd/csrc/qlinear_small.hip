@@ -24,8 +24,9 @@
 // the 16 K-elements 16 g .. + 15 of a 128-element chunk in bytes 0-15 and
 // 64 + 16 g .. + 15 in bytes 16-31, for the activation and the weight alike
 // (so each K-element meets its partner whatever order the sums run in); lane l
-// then holds C[4 g + r][l % 16], r = 0..3.  The 4 waves take the K-chunks
-// round-robin and add their sums in LDS at the end.
+// then holds C[4 g + r][l % 16], r = 0..3.  The 8 waves take the K-chunks
+// round-robin, each with the loads of three chunks in flight before it uses
+// any, and add their sums in LDS at the end.
 #include <algorithm>
 
 #include "gemm_common.hpp"
@@ -37,7 +38,8 @@ namespace pql {
 
 namespace {
 
-constexpr int kWaves = 4, kThreads = 64 * kWaves;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kBatch = 3;   // K-chunks whose loads a wave has in flight at once
 constexpr int kCols = 32;   // output columns per workgroup (two blocks of 16)
 
 typedef float v4f_t __attribute__((ext_vector_type(4)));
@@ -103,10 +105,14 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_small(const uint16_t* __re
       }
       __syncthreads();
       if (t < 16) {
-        float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+        float amax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, red[w][t]);
         if constexpr (T::kTensor) {   // one scale: the max over every row
           amax = 0.0f;
-          for (int m = 0; m < M; ++m) amax = fmaxf(amax, fmaxf(fmaxf(red[0][m], red[1][m]), fmaxf(red[2][m], red[3][m])));
+          for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) amax = fmaxf(amax, red[w][m]);
         }
         s_row[t] = T::kInt8 ? int8_scale(amax) : fp8_scale(amax);
       }
@@ -122,21 +128,9 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_small(const uint16_t* __re
 
   v4f_t acc[2] = {v4f_t{0.f, 0.f, 0.f, 0.f}, v4f_t{0.f, 0.f, 0.f, 0.f}};
   v4i acci[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-  for (int ck = wave; ck < nk; ck += kWaves) {
-    const int64_t k0 = (int64_t)ck * 128;
-    uint4 x[4] = {uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}};
-    if (row_valid) {
-      x[0] = ldg16(arow + k0 + 16 * g);
-      x[1] = ldg16(arow + k0 + 16 * g + 8);
-      x[2] = ldg16(arow + k0 + 64 + 16 * g);
-      x[3] = ldg16(arow + k0 + 64 + 16 * g + 8);
-    }
-    uint4 wv[2][2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      wv[j][0] = ldg16_nt(wrow[j] + k0 + 16 * g);
-      wv[j][1] = ldg16_nt(wrow[j] + k0 + 64 + 16 * g);
-    }
+  // One chunk's work once its operands are in registers: scale (block-128: from the
+  // chunk's own amax), cast to codes, matrix core.
+  auto chunk = [&](int ck, const uint4 (&x)[4], const uint4 (&wv)[2][2]) __attribute__((always_inline)) {
     float s = s_lane;
     if constexpr (T::kBlock) {
       if constexpr (STATIC) {
@@ -182,9 +176,40 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_small(const uint16_t* __re
                                                                     0, 127);
       }
     }
+  };
+
+  // Each wave takes chunks wave, wave + kWaves, ...; it issues the loads of kBatch of them
+  // before using any, so that enough bytes are in flight to stream the weight.  (The
+  // weight rows are read with ordinary loads: each load instruction covers half of 16
+  // rows' 128-byte lines, and the other half, a second instruction's, then hits in L2.)
+  for (int ck0 = wave; ck0 < nk; ck0 += kWaves * kBatch) {
+    uint4 x[kBatch][4], wv[kBatch][2][2];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int ck = ck0 + u * kWaves;
+      const int64_t k0 = (int64_t)ck * 128;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[u][i] = uint4{0, 0, 0, 0};
+      if (ck < nk) {   // wave-uniform
+        if (row_valid) {
+          x[u][0] = ldg16(arow + k0 + 16 * g);
+          x[u][1] = ldg16(arow + k0 + 16 * g + 8);
+          x[u][2] = ldg16(arow + k0 + 64 + 16 * g);
+          x[u][3] = ldg16(arow + k0 + 64 + 16 * g + 8);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          wv[u][j][0] = ldg16(wrow[j] + k0 + 16 * g);
+          wv[u][j][1] = ldg16(wrow[j] + k0 + 64 + 16 * g);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (ck0 + u * kWaves < nk) chunk(ck0 + u * kWaves, x[u], wv[u]);
   }
 
-  // ---- sums of the 4 waves, then the epilogue (the scales of the row / column GEMMs)
+  // ---- sums of the waves, then the epilogue (the scales of the row / column GEMMs)
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -197,11 +222,17 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_small(const uint16_t* __re
     if (m >= M || n >= N) continue;
     float v;
     if constexpr (T::kInt8) {
-      const int si = __float_as_int(part[0][m][col]) + __float_as_int(part[1][m][col]) +
-                     __float_as_int(part[2][m][col]) + __float_as_int(part[3][m][col]);
+      int si = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) si += __float_as_int(part[w][m][col]);
       v = (float)si;
     } else {
-      v = (part[0][m][col] + part[1][m][col]) + (part[2][m][col] + part[3][m][col]);
+      float p2[kWaves / 2];
+#pragma unroll
+      for (int w = 0; w < kWaves / 2; ++w) p2[w] = part[2 * w][m][col] + part[2 * w + 1][m][col];
+      v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves / 2; ++w) v += p2[w];
     }
     float out;
     if constexpr (T::kBlock) {
