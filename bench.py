@@ -67,6 +67,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--all", action="store_true", help="also time int8 W8A8, the alpha / bias epilogue and static "
                                                       "FP8 scales (before the headline)")
+    p.add_argument("--copy-reference", action="store_true",
+                   help="time torch's own bf16 -> fp8 cast at every quantizer size (the same bytes a quantizer "
+                        "moves, without the scale arithmetic) and a cold read of the W4A16 weight, then exit")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a plain 1 GiB device copy (read 1 GiB, write 1 GiB) three times, the "
                         "reference dispatch that scales FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -386,6 +389,47 @@ def summary_of(line):
     return s
 
 
+def copy_reference(torch, steps):
+    """Achievable-bandwidth references on this machine, from torch's own kernels (no libpql):
+    the elementwise bf16 -> fp8 e4m3 cast at each quantizer shape (reads 2 bytes and writes
+    1 byte per element, like a quantizer without its scale arithmetic) and a sum over the
+    W4A16 weight's bytes read once (an amax) and copied.  Inputs rotate over >= 1 GiB of copies."""
+    shapes = [("fp8_row_dit A", 4096, 3072), ("fp8_row_dit W", 12288, 3072), ("fp8_block_dit A", 8192, 5120),
+              ("fp8_block_dit W", 13824, 5120), ("mx_video_dit A", 20280, 5120), ("mx_video_dit W", 5120, 5120)]
+    for name, rows, cols in shapes:
+        x0 = torch.randn(rows, cols, device="cuda").to(torch.bfloat16)
+        xs = [x0] + [x0.clone() for _ in range(copies_for(x0.numel() * 2) - 1)]
+        y = torch.empty(rows, cols, device="cuda", dtype=torch.float8_e4m3fn)
+
+        def step(i, ev):
+            f = lambda: y.copy_(xs[i % len(xs)])
+            ev(f) if ev else f()
+        _, ev = timed(torch, step, steps, 5)
+        st = stats_us(ev.ms())
+        byts = 3 * rows * cols
+        print(json.dumps({"kind": "copy_reference", "what": f"torch bf16->fp8 cast, {name} ({rows}x{cols})",
+                          "bytes": byts, **{k: round(v, 2) for k, v in st.items()},
+                          "tbs_median": round(byts / (st["median_us"] * 1e-6) / 1e12, 2)}), flush=True)
+        del xs, x0, y
+    nbytes = 12288 * 3072 // 2 + 12288 * 24 * 3            # int4 codes, bf16 scales, u8 zero-points
+    w0 = torch.randn(nbytes // 4, device="cuda")
+    ws = [w0] + [w0.clone() for _ in range(copies_for(nbytes) - 1)]
+    cp = torch.empty_like(w0)
+    out = torch.empty((), device="cuda")
+    for what, fn, byts in (("torch amax over the W4A16 weight's bytes as fp32 (one cold read)",
+                            lambda i: torch.amax(ws[i % len(ws)], dim=0, out=out), nbytes),
+                           ("torch copy of the W4A16 weight's bytes (cold read + write)",
+                            lambda i: cp.copy_(ws[i % len(ws)]), 2 * nbytes)):
+        def rstep(i, ev, fn=fn):
+            f = lambda: fn(i)
+            ev(f) if ev else f()
+        _, ev = timed(torch, rstep, steps, 5)
+        st = stats_us(ev.ms())
+        print(json.dumps({"kind": "copy_reference", "what": what, "bytes": byts,
+                          **{k: round(v, 2) for k, v in st.items()},
+                          "tbs_median": round(byts / (st["median_us"] * 1e-6) / 1e12, 2)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -393,6 +437,9 @@ def main():
               f"run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     torch, pql = gpu_setup()
+    if args.copy_reference:
+        copy_reference(torch, args.steps)
+        return
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)
         dst = torch.empty_like(src)
