@@ -63,6 +63,23 @@ def test_noalloc_matches_qlinear_ex_twice(scheme):
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{scheme} call {call} (M={M})"
 
 
+@pytest.mark.parametrize("scheme", ["fp8_row", "fp8_block128", "int8_row", "mxfp8"])
+def test_noalloc_few_tokens_twice(scheme):
+    """1-16 tokens run the fused kernel for the FP8 / int8 schemes (no scratch needed) and
+    the quantize + GEMM pair for MX: both entry points agree on two calls in a row, the
+    second smaller, after a large call has left the static buffer dirty."""
+    N, K = 512, 1024
+    wq = pql.quantize(up(wl.small_case(81, N, K, 0.02)), scheme, "weight")
+    for call, M in enumerate((600, 16, 3)):
+        x = up(wl.small_case(82 + call, M, K))
+        got = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        want = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        assert _noalloc(scheme, x, wq, got) == 0, pql.lib().pql_last_error()
+        assert _ex(scheme, x, wq, want) == 0, pql.lib().pql_last_error()
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{scheme} call {call} (M={M})"
+
+
 def test_noalloc_static_scales_and_binding():
     N, K, M = 256, 512, 300
     wq = pql.quantize(up(wl.small_case(61, N, K, 0.02)), "fp8_block128", "weight")
