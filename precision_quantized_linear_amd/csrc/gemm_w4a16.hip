@@ -22,6 +22,7 @@
 //     tile (bf16, 32 KB) double-buffered in LDS, each thread expanding one W
 //     row-slice of 64 codes (128-byte rows, chunk c at c ^ (row & 7)).
 #include <algorithm>
+#include <atomic>
 
 #include "gemm_common.hpp"
 #include "pql_device.hpp"
@@ -250,58 +251,78 @@ __global__ __launch_bounds__(256) void k_w4a16_small(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------- M <= 16
 // Weight-bandwidth-bound GEMV-like path.  Codes stay integers: each 16-byte
-// chunk (32 codes of one row) is spread into bf16 pairs 128 + q with two
-// bit operations per pair (bf16 represents 128..143 exactly), and the
-// zero-point is removed per group after the matrix core:
+// chunk (32 codes of one row) is spread into bf16 pairs 128 + q with one AND-OR
+// per pair (bf16 represents 128..143 exactly), and the zero-point is removed
+// per group after the matrix core:
 //   sum_k a_k (q_k - z) = sum_k a_k (128 + q_k) - (128 + z) sum_k a_k,
 // with sum_k a_k from a second MFMA against a bf16 ones operand, so the
 // dequantized weight is never rounded.  Each K-group's sums are promoted with
 // the group's scale: acc += s (P - (128 + z) Q).
 //
-// A workgroup owns 16 output columns; its 4 waves split the K-groups.  Lane
+// A workgroup owns 16 NB output columns; its 8 waves split the K-groups.  Lane
 // (n = l % 16, g = l / 16) streams chunk 4 G + g of weight row n for its
-// wave's groups G (the 4 lanes of a row read 64 contiguous bytes per group),
-// all loads of a batch of 8 groups issued before any is used.  Because the
-// nibbles of a code word come out as pairs (k, k + 4), the A operand of a
-// lane holds a[m, k0 + {0, 4, 1, 5, 2, 6, 3, 7}] (one v_perm per pair); the
-// matrix core's sum over K does not care about the order.
-__device__ __forceinline__ uint4 spread_codes(uint32_t w) {
-  // nibble j of w -> bf16 128 + q_j; dword i holds elements (i, i + 4)
-  const uint32_t base = 0x43004300u;
-  return make_uint4(__builtin_amdgcn_ubfe(w, 0, 4) | (__builtin_amdgcn_ubfe(w, 16, 4) << 16) | base,
-                    __builtin_amdgcn_ubfe(w, 4, 4) | (__builtin_amdgcn_ubfe(w, 20, 4) << 16) | base,
-                    __builtin_amdgcn_ubfe(w, 8, 4) | (__builtin_amdgcn_ubfe(w, 24, 4) << 16) | base,
-                    __builtin_amdgcn_ubfe(w, 12, 4) | (__builtin_amdgcn_ubfe(w, 28, 4) << 16) | base);
+// wave's groups G (the 4 lanes of a row read 64 contiguous bytes per group).
+// Because the nibbles of a code word come out as pairs (k, k + 4), the A
+// operand of a lane holds a[m, k0 + {0, 4, 1, 5, 2, 6, 3, 7}] (one v_perm per
+// pair); the matrix core's sum over K does not care about the order.
+//
+// Order of work in a wave: loads of its share of the activation rows, then
+// every code, scale and zero-point load of its first batch of groups; it
+// writes the activation rows to LDS (the compiler's wait for them leaves the
+// younger weight loads in flight, since loads retire in issue order), meets
+// the other waves, then computes each group as soon as that group's loads
+// have landed.  The whole weight is requested at the start, so a wave that
+// waited for all of its loads would leave every group's arithmetic to the end
+// of the stream; this way it runs under the stream.  Every wait here is the
+// compiler's own: the activation rows are staged with ordinary loads and LDS
+// writes, not direct-to-LDS loads, whose completion the compiler cannot see.
+// nibble j of w -> bf16 128 + q_j; dword i holds elements (i, i + 4).  `low`
+// (0x000F000F, in an SGPR) and `base` (0x43004300, bf16 128 in both halves, in
+// a VGPR) come in as opaque registers: with literal constants the compiler
+// emits a separate AND and OR per dword, since a VOP3 instruction such as
+// v_and_or_b32 takes no literal.
+__device__ __forceinline__ uint4 spread_codes(uint32_t w, uint32_t low, uint32_t base) {
+  return make_uint4((w & low) | base, ((w >> 4) & low) | base, ((w >> 8) & low) | base, ((w >> 12) & low) | base);
 }
-// 8 bf16 a0..a7 (pairs per dword) -> pairs (a0, a4), (a1, a5), (a2, a6), (a3, a7).
+// 8 bf16 a0..a7 (pairs per dword) -> pairs (a0, a4), (a1, a5), (a2, a6), (a3, a7):
+// the order of the spread codes.
 __device__ __forceinline__ uint4 pair_k_k4(uint4 a) {
   return make_uint4(__builtin_amdgcn_perm(a.z, a.x, 0x05040100u), __builtin_amdgcn_perm(a.z, a.x, 0x07060302u),
                     __builtin_amdgcn_perm(a.w, a.y, 0x05040100u), __builtin_amdgcn_perm(a.w, a.y, 0x07060302u));
 }
 
-constexpr int kGemvBatch = 4;   // K-groups whose code loads are in flight together, per wave
 constexpr int kGemvWaves = 8;   // waves per workgroup, splitting the K-groups
 constexpr int kGemvStageMax = 128 * 1024;  // LDS bytes for the staged activation rows
-// LDS bytes per staged activation row: K bf16 rounded up to whole 1 KB loads,
-// plus 16 bytes, which spreads the 16 rows of a fragment read over the banks.
-__host__ __device__ constexpr int64_t gemv_a_row_bytes(int64_t K) { return (K * 2 + 1023) / 1024 * 1024 + 16; }
+// LDS bytes per staged activation row: K bf16 plus 16 bytes, which spreads the
+// 16 rows of a fragment read over the banks (K % 128 == 0).
+__host__ __device__ constexpr int64_t gemv_a_row_bytes(int64_t K) { return K * 2 + 16; }
+
 
 // NB column blocks of 16 per workgroup: every A fragment feeds NB weight row
-// blocks.  The activation rows (M <= 16) are staged once per workgroup in LDS
-// (rows padded by 16 bytes, which spreads the 16 rows of a fragment read over
-// the banks); the code loads of the first batch are in flight meanwhile.
-template <int NB>
+// blocks.  With NB = 1 (M <= 4) the activation rows are staged once per
+// workgroup in LDS, every 8 elements already in the order of the spread codes;
+// with NB = 3 (up to 16 rows, 6 KB each at K = 3072) staging every row costs
+// more than each wave loading the fragments of its own groups, which it does
+// beside the codes (from L2: every workgroup reads the same rows).  MFMA rows
+// past M read row M - 1: their sums are never stored.
+// BATCH groups' loads are in flight per wave, every one of them issued
+// unconditionally (past the wave's last group they reload that group, and its
+// arithmetic is skipped), so the compiler's wait for each group counts exactly
+// the younger loads and nothing waits for the whole batch.
+template <int NB, int BATCH>
 __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* __restrict__ a,
                                                                const uint32_t* __restrict__ wq,
                                                                const uint16_t* __restrict__ w_scales,
                                                                const uint8_t* __restrict__ w_zeros, int64_t M,
                                                                int64_t N, int64_t K, uint16_t* __restrict__ c,
                                                                int64_t ldc) {
+  static_assert(BATCH * 3 * NB <= 63, "the loads of one batch must fit the vmcnt counter");
   extern __shared__ __attribute__((aligned(16))) uint8_t gemv_lds[];
   float (*part)[16][16 * NB + 1] = reinterpret_cast<float (*)[16][16 * NB + 1]>(gemv_lds);
   uint8_t* a_lds = gemv_lds + sizeof(float) * kGemvWaves * 16 * (16 * NB + 1);
-  const int64_t a_row_bytes = gemv_a_row_bytes(K);
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int a_row_bytes = (int)gemv_a_row_bytes(K);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // the K-group loop is uniform per wave
   const int n16 = lane & 15, g = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16 * NB;
   const int ng = (int)(K / 128);
@@ -314,75 +335,121 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
     nrow[nb] = std::min<int64_t>(n0 + nb * 16 + n16, N - 1);   // weight row of this lane (clamped)
     wrow[nb] = wq + nrow[nb] * (K / 8);
   }
-  const bool a_valid = n16 < M;
-  const uint8_t* arow = a_lds + n16 * a_row_bytes;             // A row m = l % 16 of the A operand
-  const v8bf ones = as_v8bf(make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  constexpr bool kDirectA = NB > 1;
+  const int am = std::min<int>(n16, (int)M - 1);                  // A row of this lane
+  const uint8_t* arow = a_lds + am * a_row_bytes + g * 64;       // staged
+  const uint16_t* agl = a + (int64_t)am * K + 32 * g;            // direct
+  // Constants made opaque by empty asm statements (the moves that set them
+  // are the compiler's own): the bf16 ones stay in registers instead of being
+  // rebuilt before every use, and the spread's operands stay registers.
+  uint32_t one2 = 0x3f803f80u, low = 0x000F000Fu, base = 0x43004300u;
+  asm volatile("" : "+v"(one2));
+  asm volatile("" : "+s"(low));
+  asm volatile("" : "+v"(base));
+  const v8bf ones = as_v8bf(make_uint4(one2, one2, one2, one2));
 
+  // Activation chunks (16 bytes) of this thread: the first kEarly rounds are
+  // loaded before the weight loads; rows beyond those (long K) are staged
+  // after them.
+  constexpr int kEarly = 4;   // covers M x K = 4 x 4096
+  const int cpr = (int)(K / 8);   // 16-byte chunks per row
+  const int chunks = (int)M * cpr;
+  auto a_chunk = [&](int idx) __attribute__((always_inline)) {
+    const int m = idx / cpr, j = idx - m * cpr;
+    return ldg16(a + (int64_t)m * K + 8 * j);
+  };
+  auto a_store = [&](int idx, uint4 v) __attribute__((always_inline)) {
+    const int m = idx / cpr, j = idx - m * cpr;
+    *reinterpret_cast<uint4*>(a_lds + m * a_row_bytes + 16 * j) = pair_k_k4(v);
+  };
+  uint4 achunk[kEarly];
+  if constexpr (!kDirectA) {
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i) {
+      const int idx = t + i * 64 * kGemvWaves;
+      if (idx < chunks) achunk[i] = a_chunk(idx);
+    }
+  }
   // Codes, scales and zero-points of a batch of groups; the scale and zero
   // bytes stay raw until used, so that no load waits for another.
-  uint4 code[kGemvBatch][NB];
-  uint32_t sraw[kGemvBatch][NB], zraw[kGemvBatch][NB];
+  uint4 code[BATCH][NB];
+  uint4 afr[kDirectA ? BATCH : 1][4];   // direct A fragments, raw order
+  uint32_t sraw[BATCH][NB], zraw[BATCH][NB];
+  const int glast = std::max(gend - 1, 0);   // a valid group, also for a wave with none
   auto fetch = [&](int b0) {
 #pragma unroll
-    for (int u = 0; u < kGemvBatch; ++u) {
-      const int G = b0 + u;
-      if (G < gend) {
+    for (int u = 0; u < BATCH; ++u) {
+      const int G = std::min(b0 + u, glast);
+      if constexpr (kDirectA) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          code[u][nb] = ldg16_nt(wrow[nb] + (int64_t)G * 16 + g * 4);
-          const int64_t gi = (int64_t)G * N + nrow[nb];   // group-major
-          sraw[u][nb] = w_scales[gi];
-          zraw[u][nb] = w_zeros[gi];
-        }
+        for (int d = 0; d < 4; ++d) afr[u][d] = ldg16(agl + (int64_t)G * 128 + 8 * d);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        code[u][nb] = ldg16(wrow[nb] + (int64_t)G * 16 + g * 4);
+        const int64_t gi = (int64_t)G * N + nrow[nb];   // group-major
+        sraw[u][nb] = w_scales[gi];
+        zraw[u][nb] = w_zeros[gi];
       }
     }
   };
-  fetch(gbeg);
-  // Stage A (M rows of K bf16) with direct-to-LDS loads of 1 KB (64 lanes x 16
-  // bytes of one row); a row's slot is rounded up to whole loads, so the last
-  // load of a row stays inside it.  Then one wait covers these and the batch.
-  {
-    const int per_row = (int)((K * 2 + 1023) / 1024);
-    const v4i a_rsrc = gemm::make_rsrc(a, (int)(M * K * 2));
-    for (int idx = wave; idx < M * per_row; idx += kGemvWaves) {
-      const int m = idx / per_row, j = idx - m * per_row;
-      gemm::lds_load16(a_rsrc, a_lds + m * a_row_bytes + j * 1024, (int)(m * K * 2) + j * 1024 + lane * 16);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-  }
-  __syncthreads();
-
   v4f acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int b0 = gbeg; b0 < gend; b0 += kGemvBatch) {
-    if (b0 != gbeg) fetch(b0);
+  auto compute = [&](int b0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kGemvBatch; ++u) {
-      const int G = b0 + u;
-      if (G >= gend) break;
-      v4f P[NB], Q = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) P[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < BATCH; ++u) {
+      // A slot past the wave's last group (its loads repeat that group) adds
+      // its finite sums times a zero scale.  No branch: a conditional group
+      // would let the compiler sink that group's loads into it, behind the
+      // previous group's arithmetic.
+      const int G = std::min(b0 + u, glast);
+      const bool live = b0 + u < gend;
+      // one group's spread codes at a time: computed ahead, every group's would be live together
+      __builtin_amdgcn_sched_barrier(0);
+      v4f P[NB], Q;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        uint4 av = make_uint4(0, 0, 0, 0);
-        if (a_valid) av = *reinterpret_cast<const uint4*>(arow + (int64_t)G * 256 + g * 64 + d * 16);
-        const v8bf af = as_v8bf(pair_k_k4(av));
-        Q = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, Q, 0, 0, 0);
+        const v8bf af = as_v8bf(kDirectA ? pair_k_k4(afr[kDirectA ? u : 0][d])
+                                         : *reinterpret_cast<const uint4*>(arow + G * 256 + d * 16));
+        Q = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones, d ? Q : v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           const uint32_t cw = d == 0 ? code[u][nb].x : d == 1 ? code[u][nb].y : d == 2 ? code[u][nb].z : code[u][nb].w;
-          P[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_v8bf(spread_codes(cw)), P[nb], 0, 0, 0);
+          P[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, as_v8bf(spread_codes(cw, low, base)),
+                                                          d ? P[nb] : v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
       }
       // lane (n = l % 16, g) holds rows m = 4 g + r of column n
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) {
+        const float s = live ? __uint_as_float(sraw[u][nb] << 16) : 0.f;
+        const float zq = -(128.0f + (float)zraw[u][nb]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[nb][r] = __builtin_fmaf(__uint_as_float(sraw[u][nb] << 16),
-                                      __builtin_fmaf(-(128.0f + (float)zraw[u][nb]), Q[r], P[nb][r]), acc[nb][r]);
+        for (int r = 0; r < 4; ++r) acc[nb][r] = __builtin_fmaf(s, __builtin_fmaf(zq, Q[r], P[nb][r]), acc[nb][r]);
+      }
+    }
+  };
+  if constexpr (kDirectA) {
+    for (int b0 = gbeg; b0 < gend; b0 += BATCH) {
+      fetch(b0);
+      compute(b0);
+    }
+  } else {
+    // The first batch's loads go out before the staging waits for the
+    // activation loads; the barrier is reached by every wave, also one with
+    // no groups.
+    fetch(gbeg);
+#pragma unroll
+    for (int i = 0; i < kEarly; ++i) {
+      const int idx = t + i * 64 * kGemvWaves;
+      if (idx < chunks) a_store(idx, achunk[i]);
+    }
+    for (int idx = t + kEarly * 64 * kGemvWaves; idx < chunks; idx += 64 * kGemvWaves) a_store(idx, a_chunk(idx));
+    __syncthreads();
+    for (int b0 = gbeg; b0 < gend; b0 += BATCH) {
+      if (b0 != gbeg) fetch(b0);
+      compute(b0);
     }
   }
 #pragma unroll
@@ -403,28 +470,42 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
 }
 
 template <int NB>
-size_t gemv_lds_bytes(int64_t M, int64_t K) {
-  return sizeof(float) * kGemvWaves * 16 * (16 * NB + 1) + (size_t)M * (size_t)gemv_a_row_bytes(K);
+size_t gemv_lds_bytes(int64_t M, int64_t K) {   // the partial sums, then (NB = 1) the staged rows
+  return sizeof(float) * kGemvWaves * 16 * (16 * NB + 1) + (NB == 1 ? (size_t)M * (size_t)gemv_a_row_bytes(K) : 0);
 }
 
-template <int NB>
-hipError_t launch_gemv(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales, const uint8_t* w_zeros,
-                       int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc, hipStream_t st) {
+template <int NB, int BATCH>
+hipError_t launch_gemv_batch(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales, const uint8_t* w_zeros,
+                             int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc, hipStream_t st) {
   const size_t lds = gemv_lds_bytes<NB>(M, K);
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  static bool configured[64] = {};
-  if (dev < 64 && !configured[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_w4a16_gemv<NB>),
+  static std::atomic<bool> configured[64] = {};
+  if (dev < 64 && !configured[dev].load()) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_w4a16_gemv<NB, BATCH>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)(gemv_lds_bytes<NB>(0, 0) + kGemvStageMax));
     if (e != hipSuccess) return e;
-    configured[dev] = true;
+    configured[dev].store(true);
   }
-  hipLaunchKernelGGL(k_w4a16_gemv<NB>, dim3((unsigned)((N + 16 * NB - 1) / (16 * NB))), dim3(64 * kGemvWaves), lds, st,
-                     a, wq, w_scales, w_zeros, M, N, K, c, ldc);
+  hipLaunchKernelGGL((k_w4a16_gemv<NB, BATCH>), dim3((unsigned)((N + 16 * NB - 1) / (16 * NB))), dim3(64 * kGemvWaves),
+                     lds, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
   return hipGetLastError();
+}
+
+// The batch is the number of groups each wave owns (K / 128 split over the
+// waves), up to 4; longer K loops over batches of 4.
+template <int NB>
+hipError_t launch_gemv(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales, const uint8_t* w_zeros,
+                       int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc, hipStream_t st) {
+  const int64_t per = (K / 128 + kGemvWaves - 1) / kGemvWaves;
+  switch (per <= 1 ? 1 : per >= 4 ? 4 : (int)per) {
+    case 1: return launch_gemv_batch<NB, 1>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
+    case 2: return launch_gemv_batch<NB, 2>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
+    case 3: return launch_gemv_batch<NB, 3>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
+    default: return launch_gemv_batch<NB, 4>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
+  }
 }
 
 }  // namespace
@@ -450,12 +531,12 @@ hipError_t launch_gemm_w4a16(const uint16_t* a, const uint32_t* wq, const uint16
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  static bool configured[64] = {};
-  if (dev < 64 && !configured[dev]) {
+  static std::atomic<bool> configured[64] = {};
+  if (dev < 64 && !configured[dev].load()) {
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_w4a16_tile),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    configured[dev] = true;
+    configured[dev].store(true);
   }
   hipLaunchKernelGGL(k_w4a16_tile, dim3(tiles), dim3(256), lds, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
   return hipGetLastError();
