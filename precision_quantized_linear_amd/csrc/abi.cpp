@@ -653,13 +653,15 @@ const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, 
         default: return scheme == PQL_W4A16_SYM ? "k_int4<sym>" : "k_int4<asym>";
       }
     case PQL_OP_DEQUANTIZE: return "k_dequant";
-    case PQL_OP_QLINEAR:
+    case PQL_OP_QLINEAR: {
+      const bool few = pql::qlinear_few_applies(M, K);
       switch (small_kind(scheme, M, K)) {
-        case pql::SMALL_TENSOR: return "k_qlinear_small<fp8_tensor>";
-        case pql::SMALL_ROW: return "k_qlinear_small<fp8_row>";
-        case pql::SMALL_INT8: return "k_qlinear_small<int8_row>";
-        case pql::SMALL_BLOCK: return "k_qlinear_small<fp8_block128>";
+        case pql::SMALL_TENSOR: return few ? "k_qlinear_few<fp8_tensor>" : "k_qlinear_small<fp8_tensor>";
+        case pql::SMALL_ROW: return few ? "k_qlinear_few<fp8_row>" : "k_qlinear_small<fp8_row>";
+        case pql::SMALL_INT8: return few ? "k_qlinear_few<int8_row>" : "k_qlinear_small<int8_row>";
+        case pql::SMALL_BLOCK: return few ? "k_qlinear_few<fp8_block128>" : "k_qlinear_small<fp8_block128>";
       }
+    }
       [[fallthrough]];
     case PQL_OP_QGEMM:
       if (is_w4a16(scheme)) return pql::gemm_w4a16_kernel_name(M, N, K);

@@ -113,6 +113,11 @@ struct SmallArgs {
   int64_t ldc;
 };
 inline bool qlinear_small_applies(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K % 128 == 0; }
+// The 1-4 token variant stages the quantized activation in LDS: 2 chunks of 8 elements per
+// thread of one row (K <= 8192) or 3 per thread of 4 rows (K <= 3072).
+inline bool qlinear_few_applies(int64_t M, int64_t K) {
+  return qlinear_small_applies(M, K) && (M == 1 ? K <= 8192 : M <= 4 && K <= 3072);
+}
 hipError_t launch_qlinear_small(int kind, const SmallArgs& s, hipStream_t st);
 
 // W4A16: C = A (bf16) * dequant(Wq)^T

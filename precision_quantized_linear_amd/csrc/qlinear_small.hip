@@ -27,6 +27,13 @@
 // then holds C[4 g + r][l % 16], r = 0..3.  The 8 waves take the K-chunks
 // round-robin, each with the loads of three chunks in flight before it uses
 // any, and add their sums in LDS at the end.
+//
+// Two kernels share this.  k_qlinear_small (up to 16 tokens) quantizes in its
+// main loop: each lane casts its own row's 32 elements of every chunk.
+// k_qlinear_few (1 to 4 tokens, the decode case) quantizes the activation
+// once per workgroup into LDS codes, while its first batch of weight loads is
+// already in flight, and its main loop then holds only weight registers: at
+// one token the per-lane cast of k_qlinear_small repeats one row 16 times.
 #include <algorithm>
 
 #include "gemm_common.hpp"
@@ -246,8 +253,275 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_small(const uint16_t* __re
   }
 }
 
+
+// ---------------------------------------------------------------- 1-4 tokens
+// R rows of the activation are staged (R = 1, or 4 for M = 2..4; rows past M
+// repeat row M - 1, and their outputs are never stored).  Thread t owns the
+// 16-byte activation chunks t + 512 i (i < kPer) of the R x K / 8 chunks.
+// Work order:
+//   1. the thread's activation loads, then the wave's first batch of weight
+//      loads (and block-128 weight scales): loads retire in issue order, so the
+//      activation is waited for while the weight loads stay in flight;
+//   2. the activation scales: per row (or tensor) the max of |x| over the
+//      workgroup (one barrier), or per 1 x 128 group the max over the 16
+//      lanes that hold the group's chunks (no barrier);
+//   3. the cast into LDS codes (K bytes per row plus 16 of padding) and a
+//      barrier;
+//   4. the main loop: each chunk's A codes come from LDS, its weight bytes
+//      from the batch, computed as soon as the chunk's loads have landed; a
+//      slot past the last chunk repeats the batch's first and adds zero.
+template <int R>
+struct Few {
+  static constexpr int kPer = R == 1 ? 2 : 3;   // activation chunks per thread
+};
+
+template <int KIND, bool STATIC, bool EPI, int R>
+__global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __restrict__ a, int64_t M, int64_t K,
+                                                        int64_t lda, const float* __restrict__ a_static,
+                                                        const uint8_t* __restrict__ w,
+                                                        const float* __restrict__ w_scales, int64_t N, float alpha,
+                                                        const uint16_t* __restrict__ bias, uint16_t* __restrict__ c,
+                                                        int64_t ldc) {
+  using T = SmallKind<KIND>;
+  constexpr int kPer = Few<R>::kPer;
+  extern __shared__ __attribute__((aligned(16))) uint8_t few_lds[];
+  const int nk = (int)(K / 128);
+  float (*part)[16][kCols + 1] = reinterpret_cast<float (*)[16][kCols + 1]>(few_lds);
+  float (*red)[4] = reinterpret_cast<float (*)[4]>(few_lds + sizeof(float) * kWaves * 16 * (kCols + 1));
+  float* s_row = &red[kWaves][0];                            // [4]
+  float* sa = s_row + 4;                                     // block-128: [nk][4]
+  uint8_t* codes = reinterpret_cast<uint8_t*>(sa + (T::kBlock ? 4 * nk : 0));   // [R][K + 16]
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * kCols;
+  const int cpr = (int)(K / 8);   // 16-byte activation chunks per row
+  const int ldq = (int)K + 16;    // LDS bytes per row of codes
+  const int mlast = (int)M - 1;
+
+  // ---- 1. activation loads (past the R x cpr chunks: the last one again), then the weight batch
+  uint4 av[kPer];
+  int arow[kPer], acol[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = std::min(t + kThreads * i, R * cpr - 1);
+    arow[i] = R == 1 ? 0 : idx / cpr;
+    acol[i] = idx - arow[i] * cpr;
+    av[i] = ldg16(a + (int64_t)std::min(arow[i], mlast) * lda + 8 * acol[i]);
+  }
+  const uint8_t* wrow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wrow[j] = w + std::min<int64_t>(n0 + 16 * j + r16, N - 1) * K;
+  const int64_t nblk = n0 / 128;   // block-128: the 32 columns lie in one weight block (N % 128 == 0)
+  uint4 wv[kBatch][2][2];
+  float wsc[kBatch];
+  auto fetch = [&](int ck0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int ck = ck0 + u * kWaves < nk ? ck0 + u * kWaves : ck0;   // wave-uniform
+      const int64_t k0 = (int64_t)ck * 128;
+      if constexpr (T::kBlock) wsc[u] = w_scales[nblk * nk + ck];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        wv[u][j][0] = ldg16(wrow[j] + k0 + 16 * g);
+        wv[u][j][1] = ldg16(wrow[j] + k0 + 64 + 16 * g);
+      }
+    }
+  };
+  fetch(std::min(wave, nk - 1));   // a wave with no chunk (nk < 8) loads chunk nk - 1 and never uses it
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- 2. activation scales, one per chunk of this thread
+  float sc[kPer];
+  if constexpr (T::kBlock) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int grp = acol[i] >> 4;   // the group's 16 chunks are 16 consecutive lanes
+      if constexpr (STATIC) {
+        sc[i] = a_static[(int64_t)std::min(arow[i], mlast) * nk + grp];
+      } else {
+        float m = chunk_absmax(av[i]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        sc[i] = fp8_scale(m);
+      }
+      if ((lane & 15) == 0 && t + kThreads * i < R * cpr) sa[grp * 4 + arow[i]] = sc[i];
+    }
+  } else if constexpr (STATIC) {   // per tensor, supplied
+    const float s0 = a_static[0];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) sc[i] = s0;
+    if (t < 4) s_row[t] = s0;
+  } else {   // per row (FP8, int8) or per tensor: maxima over the workgroup
+    float pm[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) pm[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const float m = chunk_absmax(av[i]);   // a repeated chunk repeats a maximum
+#pragma unroll
+      for (int r = 0; r < R; ++r) pm[r] = arow[i] == r ? fmaxf(pm[r], m) : pm[r];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_max(pm[r]);
+      if (lane == 0) red[wave][r] = v;
+    }
+    __syncthreads();
+    float s_of[R];
+    float tmax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float amax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) amax = fmaxf(amax, red[q][r]);
+      s_of[r] = amax;
+      tmax = fmaxf(tmax, amax);   // rows past M repeat row M - 1: the tensor max is over all R
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      s_of[r] = T::kTensor ? fp8_scale(tmax) : T::kInt8 ? int8_scale(s_of[r]) : fp8_scale(s_of[r]);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      float v = s_of[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) v = arow[i] == r ? s_of[r] : v;
+      sc[i] = v;
+    }
+    if (t < R) {
+      float v = s_of[0];
+#pragma unroll
+      for (int r = 1; r < R; ++r) v = t == r ? s_of[r] : v;
+      s_row[t] = v;
+    }
+  }
+
+  // ---- 3. the cast into LDS codes
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (t + kThreads * i < R * cpr) {
+      const float s = sc[i];
+      const bool fast = s >= kSmallestFastScale;
+      const float rcp = fast ? __fdiv_rn(1.0f, s) : 0.0f;
+      uint2 q;
+      if constexpr (T::kInt8) q = fast ? int8_chunk<true>(av[i], s, rcp) : int8_chunk<false>(av[i], s, rcp);
+      else if constexpr (STATIC) q = fast ? fp8_chunk_sat<true>(av[i], s, rcp) : fp8_chunk_sat<false>(av[i], s, rcp);
+      else q = fast ? fp8_chunk<true>(av[i], s, rcp) : fp8_chunk<false>(av[i], s, rcp);
+      *reinterpret_cast<uint2*>(codes + arow[i] * ldq + 8 * acol[i]) = q;
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. the main loop
+  const uint8_t* qrow = codes + std::min(r16, mlast) * ldq + 16 * g;   // the lane's row, as a GEMM operand
+  v4f_t acc[2] = {v4f_t{0.f, 0.f, 0.f, 0.f}, v4f_t{0.f, 0.f, 0.f, 0.f}};
+  v4i acci[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+  auto chunk = [&](int ck, bool live, const uint4 (&wvc)[2][2], float wscale) __attribute__((always_inline)) {
+    uint4 q0 = gemm::lds16(qrow + ck * 128), q1 = gemm::lds16(qrow + ck * 128 + 64);
+    if constexpr (T::kInt8) {
+      if (!live) q0 = q1 = uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        acci[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, q0), __builtin_bit_cast(v4i, wvc[j][0]),
+                                                        acci[j], 0, 0, 0);
+        acci[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, q1), __builtin_bit_cast(v4i, wvc[j][1]),
+                                                        acci[j], 0, 0, 0);
+      }
+    } else if constexpr (T::kBlock) {
+      // the chunk's partial sums, promoted with s_a[m, ck] s_w[block, ck]; the lane's outputs
+      // are rows 4 g + r (past M: row M - 1)
+      float sr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sr[r] = sa[ck * 4 + std::min(4 * g + r, mlast)];
+      const float sw = live ? wscale : 0.0f;
+      const v8i qa = gemm::cat(q0, q1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const v4f_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, gemm::cat(wvc[j][0], wvc[j][1]),
+                                                                        v4f_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(P[r], sr[r] * sw, acc[j][r]);
+      }
+    } else {
+      if (!live) q0 = q1 = uint4{0u, 0u, 0u, 0u};
+      const v8i qa = gemm::cat(q0, q1);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, gemm::cat(wvc[j][0], wvc[j][1]), acc[j], 0, 0, 0,
+                                                                  127, 0, 127);
+    }
+  };
+  for (int ck0 = wave; ck0 < nk; ck0 += kWaves * kBatch) {
+    if (ck0 != wave) {
+      fetch(ck0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool live = ck0 + u * kWaves < nk;
+      chunk(live ? ck0 + u * kWaves : ck0, live, wv[u], wsc[u]);
+    }
+  }
+
+  // ---- sums of the waves, then the epilogue (the scales of the row / column GEMMs)
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      part[wave][4 * g + r][16 * j + r16] = T::kInt8 ? __int_as_float(acci[j][r]) : acc[j][r];
+  __syncthreads();
+  for (int e = t; e < 16 * kCols; e += kThreads) {
+    const int m = e / kCols, col = e - m * kCols;
+    const int64_t n = n0 + col;
+    if (m >= M || n >= N) continue;
+    float v;
+    if constexpr (T::kInt8) {
+      int si = 0;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) si += __float_as_int(part[q][m][col]);
+      v = (float)si;
+    } else {
+      float p2[kWaves / 2];
+#pragma unroll
+      for (int q = 0; q < kWaves / 2; ++q) p2[q] = part[2 * q][m][col] + part[2 * q + 1][m][col];
+      v = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kWaves / 2; ++q) v += p2[q];
+    }
+    float out;
+    if constexpr (T::kBlock) {
+      out = EPI ? __builtin_fmaf(v, alpha, bias ? __uint_as_float((uint32_t)bias[n] << 16) : 0.0f) : v;
+    } else {
+      const float rs = alpha * s_row[m];
+      const float cs = T::kTensor ? w_scales[0] : w_scales[n];
+      out = EPI ? __builtin_fmaf(v * rs, cs, bias ? __uint_as_float((uint32_t)bias[n] << 16) : 0.0f) : v * rs * cs;
+    }
+    c[(int64_t)m * ldc + n] = (uint16_t)(gemm::pack_bf16x2(out, 0.0f) & 0xFFFFu);
+  }
+}
+
+size_t few_lds_bytes(int R, bool block, int64_t K) {
+  return sizeof(float) * (kWaves * 16 * (kCols + 1) + kWaves * 4 + 4 + (block ? 4 * (K / 128) : 0)) +
+         (size_t)R * (size_t)(K + 16);
+}
+
+template <int KIND, bool STATIC, int R>
+hipError_t launch_few(const SmallArgs& s, hipStream_t st) {
+  const dim3 grid((unsigned)((s.N + kCols - 1) / kCols)), block(kThreads);
+  const size_t lds = few_lds_bytes(R, KIND == SMALL_BLOCK, s.K);
+  if (s.alpha != 1.0f || s.bias)
+    hipLaunchKernelGGL((k_qlinear_few<KIND, STATIC, true, R>), grid, block, lds, st, s.a, s.M, s.K, s.lda, s.a_static,
+                       s.w, s.w_scales, s.N, s.alpha, s.bias, s.c, s.ldc);
+  else
+    hipLaunchKernelGGL((k_qlinear_few<KIND, STATIC, false, R>), grid, block, lds, st, s.a, s.M, s.K, s.lda, s.a_static,
+                       s.w, s.w_scales, s.N, s.alpha, s.bias, s.c, s.ldc);
+  return hipGetLastError();
+}
+
 template <int KIND, bool STATIC>
 hipError_t launch_kind(const SmallArgs& s, hipStream_t st) {
+  if (qlinear_few_applies(s.M, s.K))
+    return s.M == 1 ? launch_few<KIND, STATIC, 1>(s, st) : launch_few<KIND, STATIC, 4>(s, st);
   const dim3 grid((unsigned)((s.N + kCols - 1) / kCols)), block(kThreads);
   if (s.alpha != 1.0f || s.bias)
     hipLaunchKernelGGL((k_qlinear_small<KIND, STATIC, true>), grid, block, 0, st, s.a, s.M, s.K, s.lda, s.a_static,

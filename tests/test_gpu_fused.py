@@ -29,6 +29,13 @@ DEV = "cuda"
 FUSED = ("fp8_tensor", "fp8_row", "int8_row", "fp8_block128")
 
 
+def fused_kernel(scheme, M, K):
+    """The fused kernel qlinear runs: the 1-4 token variant stages the quantized activation in LDS
+    (one row up to K = 8192, four rows up to K = 3072)."""
+    few = (M == 1 and K <= 8192) or (2 <= M <= 4 and K <= 3072)
+    return f"k_qlinear_{'few' if few else 'small'}<{scheme}>"
+
+
 def _weight(scheme, N, K, seed):
     w = wl.pow2_blocks(wl.small_case(seed, N, K, 0.02), seed, 128 if scheme == "fp8_block128" else 1, 128)
     wq = oracle.quantize(w, scheme, "weight")
@@ -39,7 +46,7 @@ def _weight(scheme, N, K, seed):
 @pytest.mark.parametrize("M", [1, 2, 5, 16])
 def test_fused_exact(scheme, M):
     N, K = (512 if scheme == "fp8_block128" else 520), 512
-    assert pql.kernel_name("qlinear", scheme, "activation", M, N, K) == f"k_qlinear_small<{scheme}>"
+    assert pql.kernel_name("qlinear", scheme, "activation", M, N, K) == fused_kernel(scheme, M, K)
     a_bits = fused_exact_activation(scheme, M, K, 10 + M)
     wq = exact_operand(scheme, "weight", N, K, 20 + M)
     aq = oracle.quantize(a_bits, scheme, "activation")
@@ -112,7 +119,7 @@ def test_fused_full_size_weights(name, scheme, M):
     w_bits = wl.weight(w_)
     wq_t = pql.quantize(up(w_bits), scheme, "weight")
     y = pql.qlinear(up(a_bits), wq_t)
-    assert pql.kernel_name("qlinear", scheme, "activation", M, w_.N, w_.K) == f"k_qlinear_small<{scheme}>"
+    assert pql.kernel_name("qlinear", scheme, "activation", M, w_.N, w_.K) == fused_kernel(scheme, M, w_.K)
     rw = tile_sample(w_.N, 5, tile=128, per_tile=1)
     wq_np = pql.to_numpy(wq_t)
     w_rows = dict(wq_np, codes=wq_np["codes"][rw], rows=len(rw))
