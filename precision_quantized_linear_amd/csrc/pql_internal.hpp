@@ -113,10 +113,10 @@ struct SmallArgs {
   int64_t ldc;
 };
 inline bool qlinear_small_applies(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K % 128 == 0; }
-// The 1-4 token variant stages the quantized activation in LDS: 2 chunks of 8 elements per
-// thread of one row (K <= 8192) or 3 per thread of 4 rows (K <= 3072).
+// The staged-activation variant: each thread quantizes one 8-element column-chunk of every
+// staged row (two for a single row), so K <= 4096 (8192 for one token).
 inline bool qlinear_few_applies(int64_t M, int64_t K) {
-  return qlinear_small_applies(M, K) && (M == 1 ? K <= 8192 : M <= 4 && K <= 3072);
+  return qlinear_small_applies(M, K) && K <= (M == 1 ? 8192 : 4096);
 }
 hipError_t launch_qlinear_small(int kind, const SmallArgs& s, hipStream_t st);
 

@@ -28,13 +28,13 @@
 // round-robin, each with the loads of three chunks in flight before it uses
 // any, and add their sums in LDS at the end.
 //
-// Two kernels share this.  k_qlinear_small (up to 16 tokens) quantizes in its
-// main loop: each lane casts its own row's 32 elements of every chunk.
-// k_qlinear_few (1 to 4 tokens, the decode case) quantizes the activation
-// once per workgroup into LDS codes, while its first batch of weight loads is
-// already in flight, and its main loop then holds only weight registers: at
-// one token the per-lane cast of k_qlinear_small repeats one row 16 times.
+// Two kernels share this.  k_qlinear_few (K up to 4096, 8192 for one token)
+// quantizes the activation once per workgroup into LDS codes, while its first
+// batch of weight loads is already in flight, and its main loop then holds
+// only weight registers.  k_qlinear_small (longer K) quantizes in its main
+// loop: each lane casts its own row's 32 elements of every chunk.
 #include <algorithm>
+#include <atomic>
 
 #include "gemm_common.hpp"
 #include "pql_device.hpp"
@@ -48,6 +48,7 @@ namespace {
 constexpr int kWaves = 8, kThreads = 64 * kWaves;
 constexpr int kBatch = 3;   // K-chunks whose loads a wave has in flight at once
 constexpr int kCols = 32;   // output columns per workgroup (two blocks of 16)
+constexpr int64_t kFewMaxK = 8192;   // the longest K of the staged-activation kernel
 
 typedef float v4f_t __attribute__((ext_vector_type(4)));
 
@@ -254,28 +255,29 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_small(const uint16_t* __re
 }
 
 
-// ---------------------------------------------------------------- 1-4 tokens
-// R rows of the activation are staged (R = 1, or 4 for M = 2..4; rows past M
-// repeat row M - 1, and their outputs are never stored).  Thread t owns the
-// 16-byte activation chunks t + 512 i (i < kPer) of the R x K / 8 chunks.
+// ---------------------------------------------------------------- staged activation
+// R rows of the activation are staged (R = 1, 4 or 16, the smallest that
+// covers M; rows past M repeat row M - 1, and their outputs are never
+// stored).  Thread t owns the 16-byte activation column-chunk j = t (+ 512 for
+// R = 1 and K > 4096) of every staged row, so a row is a compile-time index.
 // Work order:
 //   1. the thread's activation loads, then the wave's first batch of weight
 //      loads (and block-128 weight scales): loads retire in issue order, so the
 //      activation is waited for while the weight loads stay in flight;
 //   2. the activation scales: per row (or tensor) the max of |x| over the
 //      workgroup (one barrier), or per 1 x 128 group the max over the 16
-//      lanes that hold the group's chunks (no barrier);
+//      lanes that hold the group's chunks (no barrier).  With 16 rows and a
+//      per-row or per-tensor scale the thread's 16 chunks are loaded twice:
+//      once, before any weight load, for the maxima, and again beside the
+//      weight batch for the cast, so that the chunks and the batch are not
+//      held through the barrier together (the registers would cost the second
+//      workgroup per CU);
 //   3. the cast into LDS codes (K bytes per row plus 16 of padding) and a
 //      barrier;
 //   4. the main loop: each chunk's A codes come from LDS, its weight bytes
 //      from the batch, computed as soon as the chunk's loads have landed; a
 //      slot past the last chunk repeats the batch's first and adds zero.
-template <int R>
-struct Few {
-  static constexpr int kPer = R == 1 ? 2 : 3;   // activation chunks per thread
-};
-
-template <int KIND, bool STATIC, bool EPI, int R>
+template <int KIND, bool STATIC, bool EPI, int R, int J>   // J: column-chunks per thread (K <= 4096 J)
 __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __restrict__ a, int64_t M, int64_t K,
                                                         int64_t lda, const float* __restrict__ a_static,
                                                         const uint8_t* __restrict__ w,
@@ -283,14 +285,16 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
                                                         const uint16_t* __restrict__ bias, uint16_t* __restrict__ c,
                                                         int64_t ldc) {
   using T = SmallKind<KIND>;
-  constexpr int kPer = Few<R>::kPer;
+  constexpr int kJ = J;
+  constexpr bool kTwoPass = R == 16 && !T::kBlock && !STATIC;
   extern __shared__ __attribute__((aligned(16))) uint8_t few_lds[];
   const int nk = (int)(K / 128);
   float (*part)[16][kCols + 1] = reinterpret_cast<float (*)[16][kCols + 1]>(few_lds);
-  float (*red)[4] = reinterpret_cast<float (*)[4]>(few_lds + sizeof(float) * kWaves * 16 * (kCols + 1));
-  float* s_row = &red[kWaves][0];                            // [4]
-  float* sa = s_row + 4;                                     // block-128: [nk][4]
-  uint8_t* codes = reinterpret_cast<uint8_t*>(sa + (T::kBlock ? 4 * nk : 0));   // [R][K + 16]
+  float (*red)[R] = reinterpret_cast<float (*)[R]>(few_lds + sizeof(float) * kWaves * 16 * (kCols + 1));
+  float* s_row = &red[kWaves][0];                            // [R]
+  float* sa = s_row + R;                                     // block-128: [nk][R]
+  // [R][K + 16], 16-byte aligned for the 16-byte fragment reads
+  uint8_t* codes = few_lds + ((reinterpret_cast<uint8_t*>(sa + (T::kBlock ? R * nk : 0)) - few_lds + 15) & ~15);
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -299,25 +303,30 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
   const int ldq = (int)K + 16;    // LDS bytes per row of codes
   const int mlast = (int)M - 1;
 
-  // ---- 1. activation loads (past the R x cpr chunks: the last one again), then the weight batch
-  uint4 av[kPer];
-  int arow[kPer], acol[kPer];
+  // ---- 1. activation loads (a column past the row repeats the last), then the weight batch
+  uint4 av[kJ][R];
+  float ast[T::kBlock && STATIC ? kJ : 1][R];   // static block-128: the supplied scale of each chunk
+  auto load_act = [&](const uint16_t* ap) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int idx = std::min(t + kThreads * i, R * cpr - 1);
-    arow[i] = R == 1 ? 0 : idx / cpr;
-    acol[i] = idx - arow[i] * cpr;
-    av[i] = ldg16(a + (int64_t)std::min(arow[i], mlast) * lda + 8 * acol[i]);
-  }
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int j = std::min(t + kThreads * jj, cpr - 1);
+#pragma unroll
+      for (int m = 0; m < R; ++m) {
+        av[jj][m] = ldg16(ap + (int64_t)std::min(m, mlast) * lda + 8 * j);
+        if constexpr (T::kBlock && STATIC) ast[jj][m] = a_static[(int64_t)std::min(m, mlast) * nk + (j >> 4)];
+      }
+    }
+  };
   const uint8_t* wrow[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) wrow[j] = w + std::min<int64_t>(n0 + 16 * j + r16, N - 1) * K;
   const int64_t nblk = n0 / 128;   // block-128: the 32 columns lie in one weight block (N % 128 == 0)
   uint4 wv[kBatch][2][2];
   float wsc[kBatch];
-  auto fetch = [&](int ck0) __attribute__((always_inline)) {
+  // slots u0 .. u1 - 1 of the batch starting at chunk ck0
+  auto fetch = [&](int ck0, int u0 = 0, int u1 = kBatch) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
+    for (int u = u0; u < u1; ++u) {
       const int ck = ck0 + u * kWaves < nk ? ck0 + u * kWaves : ck0;   // wave-uniform
       const int64_t k0 = (int64_t)ck * 128;
       if constexpr (T::kBlock) wsc[u] = w_scales[nblk * nk + ck];
@@ -328,88 +337,110 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
       }
     }
   };
-  fetch(std::min(wave, nk - 1));   // a wave with no chunk (nk < 8) loads chunk nk - 1 and never uses it
-  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- 2. activation scales, one per chunk of this thread
-  float sc[kPer];
-  if constexpr (T::kBlock) {
+  // the scale of staged row m (per tensor: row 0 holds the tensor's max) from the maxima
+  auto row_scale = [&](int m) __attribute__((always_inline)) {
+    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int grp = acol[i] >> 4;   // the group's 16 chunks are 16 consecutive lanes
-      if constexpr (STATIC) {
-        sc[i] = a_static[(int64_t)std::min(arow[i], mlast) * nk + grp];
-      } else {
-        float m = chunk_absmax(av[i]);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-        sc[i] = fp8_scale(m);
-      }
-      if ((lane & 15) == 0 && t + kThreads * i < R * cpr) sa[grp * 4 + arow[i]] = sc[i];
-    }
-  } else if constexpr (STATIC) {   // per tensor, supplied
-    const float s0 = a_static[0];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) sc[i] = s0;
-    if (t < 4) s_row[t] = s0;
-  } else {   // per row (FP8, int8) or per tensor: maxima over the workgroup
+    for (int q = 0; q < kWaves; ++q) amax = fmaxf(amax, red[q][m]);
+    return T::kInt8 ? int8_scale(amax) : fp8_scale(amax);
+  };
+  // ---- 2. per-row / per-tensor maxima (dynamic, not block-128): thread m < R turns row m's
+  // maximum (per tensor: the tensor's) into its scale in s_row; two barriers
+  auto row_maxima = [&]() __attribute__((always_inline)) {
     float pm[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) pm[r] = 0.0f;
+    for (int m = 0; m < R; ++m) pm[m] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const float m = chunk_absmax(av[i]);   // a repeated chunk repeats a maximum
+    for (int jj = 0; jj < kJ; ++jj)
 #pragma unroll
-      for (int r = 0; r < R; ++r) pm[r] = arow[i] == r ? fmaxf(pm[r], m) : pm[r];
-    }
+      for (int m = 0; m < R; ++m) pm[m] = fmaxf(pm[m], chunk_absmax(av[jj][m]));   // a repeat repeats a maximum
+    if constexpr (T::kTensor) {   // rows past M repeat row M - 1: the max over all R rows is the tensor's
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = wave_max(pm[r]);
-      if (lane == 0) red[wave][r] = v;
+      for (int m = 1; m < R; ++m) pm[0] = fmaxf(pm[0], pm[m]);
+      const float v = wave_max(pm[0]);
+      if (lane == 0) red[wave][0] = v;
+    } else {
+#pragma unroll
+      for (int m = 0; m < R; ++m) {
+        const float v = wave_max(pm[m]);
+        if (lane == 0) red[wave][m] = v;
+      }
     }
     __syncthreads();
-    float s_of[R];
-    float tmax = 0.0f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float amax = 0.0f;
-#pragma unroll
-      for (int q = 0; q < kWaves; ++q) amax = fmaxf(amax, red[q][r]);
-      s_of[r] = amax;
-      tmax = fmaxf(tmax, amax);   // rows past M repeat row M - 1: the tensor max is over all R
+    if constexpr (R == 16) {   // one thread per row: 16 scales in every thread would cost registers
+      if (t < R) s_row[t] = row_scale(T::kTensor ? 0 : t);   // rows past M: row M - 1's scale
+      __syncthreads();
     }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      s_of[r] = T::kTensor ? fp8_scale(tmax) : T::kInt8 ? int8_scale(s_of[r]) : fp8_scale(s_of[r]);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      float v = s_of[0];
-#pragma unroll
-      for (int r = 1; r < R; ++r) v = arow[i] == r ? s_of[r] : v;
-      sc[i] = v;
-    }
-    if (t < R) {
-      float v = s_of[0];
-#pragma unroll
-      for (int r = 1; r < R; ++r) v = t == r ? s_of[r] : v;
-      s_row[t] = v;
-    }
-  }
+  };
 
-  // ---- 3. the cast into LDS codes
+  // With 16 rows the cast holds two of the batch's three chunks: the 16 activation chunks
+  // beside a whole batch would cost the second workgroup per CU.
+  constexpr int kEarly = R == 16 ? 2 : kBatch;
+  const int ck_first = std::min(wave, nk - 1);   // a wave with no chunk (nk < 8) loads chunk nk - 1, unused
+  load_act(a);
+  if constexpr (kTwoPass) {
+    row_maxima();
+    // the same bytes again: an opaque zero offset makes them loads, where the compiler
+    // would otherwise keep the first pass's registers live through the barrier (an opaque
+    // pointer would lose its address space and turn them into flat loads)
+    int zero = 0;
+    asm volatile("" : "+s"(zero));
+    load_act(a + zero);
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every activation-side load goes out before the weight batch
+  fetch(ck_first, 0, kEarly);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!T::kBlock && !STATIC && !kTwoPass) row_maxima();
+
+  // ---- 3. scales and the cast into LDS codes: every staged row, with no branch on M (a
+  // branch would make the compiler wait for the weight batch too); rows past M repeat row
+  // M - 1 and are never read
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    if (t + kThreads * i < R * cpr) {
-      const float s = sc[i];
-      const bool fast = s >= kSmallestFastScale;
-      const float rcp = fast ? __fdiv_rn(1.0f, s) : 0.0f;
+  for (int m = 0; m < R; ++m) {
+    __builtin_amdgcn_sched_barrier(0);   // one row's scale and cast at a time
+    float s;
+    if constexpr (T::kBlock || !STATIC) s = 0.0f;
+    if constexpr (!T::kBlock) {
+      if constexpr (STATIC) {
+        s = a_static[0];
+        if (t == 0) s_row[m] = s;
+      } else if constexpr (R == 16) {
+        s = s_row[m];
+      } else {
+        s = row_scale(T::kTensor ? 0 : m);
+        if (t == 0) s_row[m] = s;   // rows past M: row M - 1's scale
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj) {
+      const int j = t + kThreads * jj;
+      float sj = s;
+      if constexpr (T::kBlock) {   // the group's 16 chunks are 16 consecutive lanes
+        const int grp = std::min(j, cpr - 1) >> 4;
+        if constexpr (STATIC) {
+          sj = ast[T::kBlock && STATIC ? jj : 0][m];
+        } else {
+          float mx = chunk_absmax(av[jj][m]);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+          sj = fp8_scale(mx);
+        }
+        if ((lane & 15) == 0 && j < cpr) sa[grp * R + m] = sj;
+      }
+      // the cast is unconditional (a column past the row repeats the last one) and only the
+      // store is not: a cast under the branch let the compiler sink the chunk's load into it,
+      // behind the weight loads
+      const bool fast = sj >= kSmallestFastScale;
+      const float rcp = fast ? __fdiv_rn(1.0f, sj) : 0.0f;
       uint2 q;
-      if constexpr (T::kInt8) q = fast ? int8_chunk<true>(av[i], s, rcp) : int8_chunk<false>(av[i], s, rcp);
-      else if constexpr (STATIC) q = fast ? fp8_chunk_sat<true>(av[i], s, rcp) : fp8_chunk_sat<false>(av[i], s, rcp);
-      else q = fast ? fp8_chunk<true>(av[i], s, rcp) : fp8_chunk<false>(av[i], s, rcp);
-      *reinterpret_cast<uint2*>(codes + arow[i] * ldq + 8 * acol[i]) = q;
+      if constexpr (T::kInt8) q = fast ? int8_chunk<true>(av[jj][m], sj, rcp) : int8_chunk<false>(av[jj][m], sj, rcp);
+      else if constexpr (STATIC) q = fast ? fp8_chunk_sat<true>(av[jj][m], sj, rcp) : fp8_chunk_sat<false>(av[jj][m], sj, rcp);
+      else q = fast ? fp8_chunk<true>(av[jj][m], sj, rcp) : fp8_chunk<false>(av[jj][m], sj, rcp);
+      if (j < cpr) *reinterpret_cast<uint2*>(codes + m * ldq + 8 * j) = q;
     }
   }
+  if constexpr (kEarly < kBatch) fetch(ck_first, kEarly, kBatch);
   __syncthreads();
 
   // ---- 4. the main loop
@@ -432,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
       // are rows 4 g + r (past M: row M - 1)
       float sr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sr[r] = sa[ck * 4 + std::min(4 * g + r, mlast)];
+      for (int r = 0; r < 4; ++r) sr[r] = sa[ck * R + std::min(4 * g + r, mlast)];
       const float sw = live ? wscale : 0.0f;
       const v8i qa = gemm::cat(q0, q1);
 #pragma unroll
@@ -501,27 +532,44 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
 }
 
 size_t few_lds_bytes(int R, bool block, int64_t K) {
-  return sizeof(float) * (kWaves * 16 * (kCols + 1) + kWaves * 4 + 4 + (block ? 4 * (K / 128) : 0)) +
-         (size_t)R * (size_t)(K + 16);
+  const size_t head = sizeof(float) * (kWaves * 16 * (kCols + 1) + (kWaves + 1) * R + (block ? R * (K / 128) : 0));
+  return (head + 15) / 16 * 16 + (size_t)R * (size_t)(K + 16);
 }
 
-template <int KIND, bool STATIC, int R>
-hipError_t launch_few(const SmallArgs& s, hipStream_t st) {
-  const dim3 grid((unsigned)((s.N + kCols - 1) / kCols)), block(kThreads);
+template <int KIND, bool STATIC, bool EPI, int R, int J>
+hipError_t launch_few_epi(const SmallArgs& s, hipStream_t st) {
   const size_t lds = few_lds_bytes(R, KIND == SMALL_BLOCK, s.K);
-  if (s.alpha != 1.0f || s.bias)
-    hipLaunchKernelGGL((k_qlinear_few<KIND, STATIC, true, R>), grid, block, lds, st, s.a, s.M, s.K, s.lda, s.a_static,
-                       s.w, s.w_scales, s.N, s.alpha, s.bias, s.c, s.ldc);
-  else
-    hipLaunchKernelGGL((k_qlinear_few<KIND, STATIC, false, R>), grid, block, lds, st, s.a, s.M, s.K, s.lda, s.a_static,
-                       s.w, s.w_scales, s.N, s.alpha, s.bias, s.c, s.ldc);
+  if (lds > 64 * 1024) {   // above the default dynamic-LDS limit: raise it once per device
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    static std::atomic<bool> configured[64] = {};
+    if (dev >= 64) return hipErrorInvalidDevice;
+    if (!configured[dev].load()) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qlinear_few<KIND, STATIC, EPI, R, J>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)few_lds_bytes(R, true, kFewMaxK));
+      if (e != hipSuccess) return e;
+      configured[dev].store(true);
+    }
+  }
+  hipLaunchKernelGGL((k_qlinear_few<KIND, STATIC, EPI, R, J>), dim3((unsigned)((s.N + kCols - 1) / kCols)),
+                     dim3(kThreads), lds, st, s.a, s.M, s.K, s.lda, s.a_static, s.w, s.w_scales, s.N, s.alpha, s.bias,
+                     s.c, s.ldc);
   return hipGetLastError();
+}
+
+template <int KIND, bool STATIC, int R, int J = 1>
+hipError_t launch_few(const SmallArgs& s, hipStream_t st) {
+  return (s.alpha != 1.0f || s.bias) ? launch_few_epi<KIND, STATIC, true, R, J>(s, st)
+                                     : launch_few_epi<KIND, STATIC, false, R, J>(s, st);
 }
 
 template <int KIND, bool STATIC>
 hipError_t launch_kind(const SmallArgs& s, hipStream_t st) {
   if (qlinear_few_applies(s.M, s.K))
-    return s.M == 1 ? launch_few<KIND, STATIC, 1>(s, st) : launch_few<KIND, STATIC, 4>(s, st);
+    return s.M == 1   ? (s.K <= 4096 ? launch_few<KIND, STATIC, 1>(s, st) : launch_few<KIND, STATIC, 1, 2>(s, st))
+           : s.M <= 4 ? launch_few<KIND, STATIC, 4>(s, st)
+                      : launch_few<KIND, STATIC, 16>(s, st);
   const dim3 grid((unsigned)((s.N + kCols - 1) / kCols)), block(kThreads);
   if (s.alpha != 1.0f || s.bias)
     hipLaunchKernelGGL((k_qlinear_small<KIND, STATIC, true>), grid, block, 0, st, s.a, s.M, s.K, s.lda, s.a_static,

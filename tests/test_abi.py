@@ -94,13 +94,14 @@ def test_workspace_sizes():
 
 def test_small_m_qlinear_runs_the_fused_kernel():
     for s in ("fp8_tensor", "fp8_row", "fp8_block128", "int8_row"):
-        for M, family in ((1, "few"), (4, "few"), (5, "small"), (16, "small")):
-            assert pql.kernel_name("qlinear", s, "activation", M, 3072, 3072) == f"k_qlinear_{family}<{s}>"
+        for M in (1, 4, 5, 16):
+            assert pql.kernel_name("qlinear", s, "activation", M, 3072, 3072) == f"k_qlinear_few<{s}>"
             assert not pql.kernel_name("qgemm", s, "activation", M, 3072, 3072).startswith("k_qlinear")
-        # the 1-4 token variant's LDS stage: one row up to K = 8192, four rows up to K = 3072
+        # the staged activation: K <= 4096 (8192 for one token); longer K casts in the main loop
         assert pql.kernel_name("qlinear", s, "activation", 1, 3072, 8192) == f"k_qlinear_few<{s}>"
         assert pql.kernel_name("qlinear", s, "activation", 1, 3072, 8320) == f"k_qlinear_small<{s}>"
-        assert pql.kernel_name("qlinear", s, "activation", 4, 3072, 3200) == f"k_qlinear_small<{s}>"
+        assert pql.kernel_name("qlinear", s, "activation", 16, 3072, 4096) == f"k_qlinear_few<{s}>"
+        assert pql.kernel_name("qlinear", s, "activation", 16, 3072, 4224) == f"k_qlinear_small<{s}>"
         assert not pql.kernel_name("qlinear", s, "activation", 17, 3072, 3072).startswith("k_qlinear")
     for s in ("mxfp8", "mxfp4", "mxfp4_dual", "w4a16_asym"):
         assert not pql.kernel_name("qlinear", s, "activation", 1, 3072, 3072).startswith("k_qlinear")

@@ -30,9 +30,9 @@ FUSED = ("fp8_tensor", "fp8_row", "int8_row", "fp8_block128")
 
 
 def fused_kernel(scheme, M, K):
-    """The fused kernel qlinear runs: the 1-4 token variant stages the quantized activation in LDS
-    (one row up to K = 8192, four rows up to K = 3072)."""
-    few = (M == 1 and K <= 8192) or (2 <= M <= 4 and K <= 3072)
+    """The fused kernel qlinear runs: the staged-activation variant quantizes the activation once per
+    workgroup into LDS (K <= 4096, or 8192 for one token); longer K casts in the main loop."""
+    few = K <= (8192 if M == 1 else 4096)
     return f"k_qlinear_{'few' if few else 'small'}<{scheme}>"
 
 
@@ -55,11 +55,15 @@ def test_fused_exact(scheme, M):
     check_gemm_exact(down_bf16(y), oracle.gemm_ref(aq, wq), f"{scheme} M={M}")
 
 
+# the staged-activation kernel at 1, 4 and 16 staged rows, and (K past its stage) the kernel that casts
+# in its main loop
 @pytest.mark.parametrize("scheme", FUSED)
-@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (3, 300 * 4, 640), (16, 4100, 3072), (9, 384, 1152)])
+@pytest.mark.parametrize("M,N,K", [(1, 256, 128), (3, 300 * 4, 640), (16, 4100, 3072), (9, 384, 1152),
+                                   (1, 256, 6144), (1, 256, 8320), (2, 384, 4224), (16, 256, 4352)])
 def test_fused_matches_oracle(scheme, M, N, K):
     if scheme == "fp8_block128":
         N = -(-N // 128) * 128
+    assert pql.kernel_name("qlinear", scheme, "activation", M, N, K) == fused_kernel(scheme, M, K)
     a_bits = wl.pow2_blocks(wl.small_case(M * 31 + K, M, K), M, 1, 128).copy()
     a_bits[0, :7] = 0x8000                                   # -0 and zeros among the codes
     a_bits[M - 1, K // 2] = wl.f32_to_bf16_bits(np.array([300.0], np.float32))[0]   # an outlier
