@@ -291,7 +291,9 @@ __device__ __forceinline__ uint4 pair_k_k4(uint4 a) {
                     __builtin_amdgcn_perm(a.w, a.y, 0x05040100u), __builtin_amdgcn_perm(a.w, a.y, 0x07060302u));
 }
 
-constexpr int kGemvWaves = 8;   // waves per workgroup, splitting the K-groups
+// Waves per workgroup, splitting the K-groups: 8, or 12 for the 48-column variant, whose
+// 256 workgroups for N = 12288 put one workgroup on each CU.
+__host__ __device__ constexpr int gemv_waves(int NB) { return NB == 1 ? 8 : 12; }
 constexpr int kGemvStageMax = 128 * 1024;  // LDS bytes for the staged activation rows
 // LDS bytes per staged activation row: K bf16 plus 16 bytes, which spreads the
 // 16 rows of a fragment read over the banks (K % 128 == 0).
@@ -310,12 +312,13 @@ __host__ __device__ constexpr int64_t gemv_a_row_bytes(int64_t K) { return K * 2
 // arithmetic is skipped), so the compiler's wait for each group counts exactly
 // the younger loads and nothing waits for the whole batch.
 template <int NB, int BATCH>
-__global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* __restrict__ a,
+__global__ __launch_bounds__(64 * gemv_waves(NB)) void k_w4a16_gemv(const uint16_t* __restrict__ a,
                                                                const uint32_t* __restrict__ wq,
                                                                const uint16_t* __restrict__ w_scales,
                                                                const uint8_t* __restrict__ w_zeros, int64_t M,
                                                                int64_t N, int64_t K, uint16_t* __restrict__ c,
                                                                int64_t ldc) {
+  constexpr int kGemvWaves = gemv_waves(NB);
   static_assert(BATCH * 3 * NB <= 63, "the loads of one batch must fit the vmcnt counter");
   extern __shared__ __attribute__((aligned(16))) uint8_t gemv_lds[];
   float (*part)[16][16 * NB + 1] = reinterpret_cast<float (*)[16][16 * NB + 1]>(gemv_lds);
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void k_w4a16_gemv(const uint16_t* 
 
 template <int NB>
 size_t gemv_lds_bytes(int64_t M, int64_t K) {   // the partial sums, then (NB = 1) the staged rows
-  return sizeof(float) * kGemvWaves * 16 * (16 * NB + 1) + (NB == 1 ? (size_t)M * (size_t)gemv_a_row_bytes(K) : 0);
+  return sizeof(float) * gemv_waves(NB) * 16 * (16 * NB + 1) + (NB == 1 ? (size_t)M * (size_t)gemv_a_row_bytes(K) : 0);
 }
 
 template <int NB, int BATCH>
@@ -482,29 +485,31 @@ hipError_t launch_gemv_batch(const uint16_t* a, const uint32_t* wq, const uint16
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   static std::atomic<bool> configured[64] = {};
-  if (dev < 64 && !configured[dev].load()) {
+  if (NB == 1 && dev < 64 && !configured[dev].load()) {   // only the staged variant passes 64 KB
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_w4a16_gemv<NB, BATCH>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)(gemv_lds_bytes<NB>(0, 0) + kGemvStageMax));
     if (e != hipSuccess) return e;
     configured[dev].store(true);
   }
-  hipLaunchKernelGGL((k_w4a16_gemv<NB, BATCH>), dim3((unsigned)((N + 16 * NB - 1) / (16 * NB))), dim3(64 * kGemvWaves),
+  hipLaunchKernelGGL((k_w4a16_gemv<NB, BATCH>), dim3((unsigned)((N + 16 * NB - 1) / (16 * NB))), dim3(64 * gemv_waves(NB)),
                      lds, st, a, wq, w_scales, w_zeros, M, N, K, c, ldc);
   return hipGetLastError();
 }
 
 // The batch is the number of groups each wave owns (K / 128 split over the
-// waves), up to 4; longer K loops over batches of 4.
+// waves), up to 4 (3 for the 48-column variant, whose 12 waves leave 168
+// registers per lane); longer K loops over batches.
 template <int NB>
 hipError_t launch_gemv(const uint16_t* a, const uint32_t* wq, const uint16_t* w_scales, const uint8_t* w_zeros,
                        int64_t M, int64_t N, int64_t K, uint16_t* c, int64_t ldc, hipStream_t st) {
-  const int64_t per = (K / 128 + kGemvWaves - 1) / kGemvWaves;
-  switch (per <= 1 ? 1 : per >= 4 ? 4 : (int)per) {
+  const int64_t per = (K / 128 + gemv_waves(NB) - 1) / gemv_waves(NB);
+  const int64_t most = NB == 1 ? 4 : 3;
+  switch (per <= 1 ? 1 : per >= most ? (int)most : (int)per) {
     case 1: return launch_gemv_batch<NB, 1>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
     case 2: return launch_gemv_batch<NB, 2>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
     case 3: return launch_gemv_batch<NB, 3>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
-    default: return launch_gemv_batch<NB, 4>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
+    default: return launch_gemv_batch<NB, NB == 1 ? 4 : 3>(a, wq, w_scales, w_zeros, M, N, K, c, ldc, st);
   }
 }
 
