@@ -23,6 +23,13 @@
  *     and the call returns without synchronizing.  Calls are re-entrant.
  *   - Every argument check runs before anything is enqueued; on any error
  *     nothing is enqueued and pql_last_error() describes the problem.
+ *   - Launch log: with the environment variable PQL_LOG set to anything but
+ *     "" or "0" (read once, at the first call), pql_quantize,
+ *     pql_quantize_static, pql_dequantize, pql_qgemm(_ex), pql_qlinear(_ex),
+ *     pql_qlinear_noalloc and pql_repack each write one line to stderr: the
+ *     call, scheme, role and shape, then the kernel enqueued (the name
+ *     pql_kernel_name gives) and the stream, "nothing to do" for an empty
+ *     operand, or "rejected (status S)" with the pql_last_error() text.
  *   - Element sizes: bf16 = 2 bytes, fp32 = 4 bytes.  Leading dimensions
  *     (ldx, ldy, lda, ldc) are in elements.  Device pointers must be 16-byte
  *     aligned and leading dimensions multiples of 8 elements (ldc: any value

@@ -12,6 +12,7 @@
 #include <mutex>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -156,6 +157,33 @@ pql_status check_device() {
 pql_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(PQL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// Launch log: with the environment variable PQL_LOG set (to anything but "" or
+// "0"; read once per process), every call of the entry points that enqueue work
+// writes one line to stderr: the call, scheme, role and shape, the kernel it
+// runs (the name pql_kernel_name reports) and the outcome, with the error
+// message when a check rejected it.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("PQL_LOG");
+    return v != nullptr && *v != '\0' && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void log_call(pql_status st, const char* call, int scheme, int role, int64_t M, int64_t N, int64_t K,
+              const char* kernel, const void* stream) {
+  const char* role_name = role == PQL_ACTIVATION ? " activation" : role == PQL_WEIGHT ? " weight" : "";
+  if (st != PQL_OK)
+    std::fprintf(stderr, "[pql] %s %s%s M=%lld N=%lld K=%lld: rejected (status %d): %s\n", call, scheme_name(scheme),
+                 role_name, (long long)M, (long long)N, (long long)K, (int)st, g_error.c_str());
+  else if (M == 0)
+    std::fprintf(stderr, "[pql] %s %s%s M=0 N=%lld K=%lld: nothing to do\n", call, scheme_name(scheme), role_name,
+                 (long long)N, (long long)K);
+  else
+    std::fprintf(stderr, "[pql] %s %s%s M=%lld N=%lld K=%lld -> %s on stream %p\n", call, scheme_name(scheme),
+                 role_name, (long long)M, (long long)N, (long long)K, kernel, stream);
 }
 
 // Quantize without re-validating (shared by pql_quantize and pql_qlinear).
@@ -314,8 +342,9 @@ pql_status pql_workspace_size(int op, int scheme, int role, int64_t M, int64_t N
   return ok();
 }
 
-pql_status pql_quantize(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx, void* codes,
-                        void* scales, void* zeros, void* workspace, size_t workspace_bytes, void* stream) {
+static pql_status quantize_impl(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                void* codes, void* scales, void* zeros, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   pql_status st = check_scheme_role(scheme, role);
   if (st != PQL_OK) return st;
   if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
@@ -337,8 +366,18 @@ pql_status pql_quantize(int scheme, int role, const void* x, int64_t rows, int64
                   "quantize launch");
 }
 
-pql_status pql_dequantize(int scheme, int role, const void* codes, const void* scales, const void* zeros,
-                          int64_t rows, int64_t cols, void* y, int64_t ldy, void* stream) {
+pql_status pql_quantize(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx, void* codes,
+                        void* scales, void* zeros, void* workspace, size_t workspace_bytes, void* stream) {
+  const pql_status st =
+      quantize_impl(scheme, role, x, rows, cols, ldx, codes, scales, zeros, workspace, workspace_bytes, stream);
+  if (log_enabled())
+    log_call(st, "quantize", scheme, role, rows, 0, cols, pql_kernel_name(PQL_OP_QUANTIZE, scheme, role, rows, 0, cols),
+             stream);
+  return st;
+}
+
+static pql_status dequantize_impl(int scheme, int role, const void* codes, const void* scales, const void* zeros,
+                                  int64_t rows, int64_t cols, void* y, int64_t ldy, void* stream) {
   pql_status st = check_scheme_role(scheme, role);
   if (st != PQL_OK) return st;
   if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
@@ -367,6 +406,13 @@ pql_status pql_dequantize(int scheme, int role, const void* codes, const void* s
                   "dequantize launch");
 }
 
+pql_status pql_dequantize(int scheme, int role, const void* codes, const void* scales, const void* zeros,
+                          int64_t rows, int64_t cols, void* y, int64_t ldy, void* stream) {
+  const pql_status st = dequantize_impl(scheme, role, codes, scales, zeros, rows, cols, y, ldy, stream);
+  if (log_enabled()) log_call(st, "dequantize", scheme, role, rows, 0, cols, "k_dequant", stream);
+  return st;
+}
+
 }  // extern "C"
 
 namespace {
@@ -386,8 +432,8 @@ pql_status check_epilogue(int scheme, int64_t N, float alpha, const void* bias) 
 
 extern "C" {
 
-pql_status pql_quantize_static(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx,
-                               const void* scales, void* codes, void* stream) {
+static pql_status quantize_static_impl(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                       const void* scales, void* codes, void* stream) {
   pql_status st = check_scheme_role(scheme, role);
   if (st != PQL_OK) return st;
   if (scheme != PQL_FP8_TENSOR && scheme != PQL_FP8_BLOCK128)
@@ -407,9 +453,18 @@ pql_status pql_quantize_static(int scheme, int role, const void* x, int64_t rows
                   "static quantize launch");
 }
 
-pql_status pql_qgemm_ex(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
-                        const void* w_zeros, int64_t M, int64_t N, int64_t K, float alpha, const void* bias,
-                        void* c, int64_t ldc, void* stream) {
+pql_status pql_quantize_static(int scheme, int role, const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                               const void* scales, void* codes, void* stream) {
+  const pql_status st = quantize_static_impl(scheme, role, x, rows, cols, ldx, scales, codes, stream);
+  if (log_enabled())
+    log_call(st, "quantize_static", scheme, role, rows, 0, cols,
+             scheme == PQL_FP8_TENSOR ? "k_fp8_static<tensor>" : "k_fp8_static<block128>", stream);
+  return st;
+}
+
+static pql_status qgemm_ex_impl(int scheme, const void* a, const void* a_scales, const void* w_codes,
+                                const void* w_scales, const void* w_zeros, int64_t M, int64_t N, int64_t K,
+                                float alpha, const void* bias, void* c, int64_t ldc, void* stream) {
   if (!valid_scheme(scheme)) return fail(PQL_ERR_UNSUPPORTED, "unknown scheme %d", scheme);
   pql_status st = check_gemm_shape(scheme, M, N, K);
   if (st != PQL_OK) return st;
@@ -426,6 +481,16 @@ pql_status pql_qgemm_ex(int scheme, const void* a, const void* a_scales, const v
   return launched(do_qgemm(scheme, a, a_scales, w_codes, w_scales, w_zeros, M, N, K, alpha, bias, c, ldc,
                            static_cast<hipStream_t>(stream)),
                   "qgemm launch");
+}
+
+pql_status pql_qgemm_ex(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
+                        const void* w_zeros, int64_t M, int64_t N, int64_t K, float alpha, const void* bias,
+                        void* c, int64_t ldc, void* stream) {
+  const pql_status st =
+      qgemm_ex_impl(scheme, a, a_scales, w_codes, w_scales, w_zeros, M, N, K, alpha, bias, c, ldc, stream);
+  if (log_enabled())
+    log_call(st, "qgemm", scheme, -1, M, N, K, pql_kernel_name(PQL_OP_QGEMM, scheme, PQL_ACTIVATION, M, N, K), stream);
+  return st;
 }
 
 pql_status pql_qgemm(int scheme, const void* a, const void* a_scales, const void* w_codes, const void* w_scales,
@@ -532,10 +597,10 @@ pql_status scratch_address(void** out) {
 
 extern "C" {
 
-pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
-                          const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
-                          const void* bias, void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+static pql_status qlinear_ex_impl(int scheme, const void* a, int64_t M, int64_t K, int64_t lda,
+                                  const void* a_static_scales, const void* w_codes, const void* w_scales,
+                                  const void* w_zeros, int64_t N, float alpha, const void* bias, void* c, int64_t ldc,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   pql_status st = check_qlinear(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha, bias,
                                 c, ldc);
   if (st != PQL_OK || M == 0) return st == PQL_OK ? ok() : st;
@@ -551,12 +616,24 @@ pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64
                      workspace, stream);
 }
 
+pql_status pql_qlinear_ex(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* a_static_scales,
+                          const void* w_codes, const void* w_scales, const void* w_zeros, int64_t N, float alpha,
+                          const void* bias, void* c, int64_t ldc, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  const pql_status st = qlinear_ex_impl(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha,
+                                        bias, c, ldc, workspace, workspace_bytes, stream);
+  if (log_enabled())
+    log_call(st, "qlinear", scheme, -1, M, N, K, pql_kernel_name(PQL_OP_QLINEAR, scheme, PQL_ACTIVATION, M, N, K),
+             stream);
+  return st;
+}
+
 size_t pql_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
-pql_status pql_qlinear_noalloc(int scheme, const void* a, int64_t M, int64_t K, int64_t lda,
-                               const void* a_static_scales, const void* w_codes, const void* w_scales,
-                               const void* w_zeros, int64_t N, float alpha, const void* bias, void* c, int64_t ldc,
-                               void* stream) {
+static pql_status qlinear_noalloc_impl(int scheme, const void* a, int64_t M, int64_t K, int64_t lda,
+                                       const void* a_static_scales, const void* w_codes, const void* w_scales,
+                                       const void* w_zeros, int64_t N, float alpha, const void* bias, void* c,
+                                       int64_t ldc, void* stream) {
   pql_status st = check_qlinear(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha, bias,
                                 c, ldc);
   if (st != PQL_OK || M == 0) return st == PQL_OK ? ok() : st;
@@ -569,6 +646,18 @@ pql_status pql_qlinear_noalloc(int scheme, const void* a, int64_t M, int64_t K, 
   if (need && (st = scratch_address(&ws)) != PQL_OK) return st;
   return run_qlinear(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N, alpha, bias, c, ldc, ws,
                      stream);
+}
+
+pql_status pql_qlinear_noalloc(int scheme, const void* a, int64_t M, int64_t K, int64_t lda,
+                               const void* a_static_scales, const void* w_codes, const void* w_scales,
+                               const void* w_zeros, int64_t N, float alpha, const void* bias, void* c, int64_t ldc,
+                               void* stream) {
+  const pql_status st = qlinear_noalloc_impl(scheme, a, M, K, lda, a_static_scales, w_codes, w_scales, w_zeros, N,
+                                             alpha, bias, c, ldc, stream);
+  if (log_enabled())
+    log_call(st, "qlinear_noalloc", scheme, -1, M, N, K,
+             pql_kernel_name(PQL_OP_QLINEAR, scheme, PQL_ACTIVATION, M, N, K), stream);
+  return st;
 }
 
 pql_status pql_qlinear(int scheme, const void* a, int64_t M, int64_t K, int64_t lda, const void* w_codes,
@@ -588,9 +677,9 @@ pql_status pql_layout_sizes(int scheme, int role, int layout, int64_t rows, int6
   return ok();
 }
 
-pql_status pql_repack(int scheme, int role, int from_layout, int to_layout, const void* scales_in,
-                      const void* zeros_in, void* scales_out, void* zeros_out, int64_t rows, int64_t cols,
-                      void* stream) {
+static pql_status repack_impl(int scheme, int role, int from_layout, int to_layout, const void* scales_in,
+                              const void* zeros_in, void* scales_out, void* zeros_out, int64_t rows, int64_t cols,
+                              void* stream) {
   pql_status st = check_scheme_role(scheme, role);
   if (st != PQL_OK) return st;
   if ((st = check_shape(scheme, role, rows, cols)) != PQL_OK) return st;
@@ -635,6 +724,15 @@ pql_status pql_repack(int scheme, int role, int from_layout, int to_layout, cons
   if (e == hipSuccess && zeros_in && zeros_out && zeros_in != zeros_out)
     e = hipMemcpyAsync(zeros_out, zeros_in, sz.zeros, hipMemcpyDeviceToDevice, hs);
   return launched(e, "repack copy");
+}
+
+pql_status pql_repack(int scheme, int role, int from_layout, int to_layout, const void* scales_in,
+                      const void* zeros_in, void* scales_out, void* zeros_out, int64_t rows, int64_t cols,
+                      void* stream) {
+  const pql_status st =
+      repack_impl(scheme, role, from_layout, to_layout, scales_in, zeros_in, scales_out, zeros_out, rows, cols, stream);
+  if (log_enabled()) log_call(st, "repack", scheme, role, rows, 0, cols, "k_repack", stream);
+  return st;
 }
 
 const char* pql_kernel_name(int op, int scheme, int role, int64_t M, int64_t N, int64_t K) {

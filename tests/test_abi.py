@@ -298,3 +298,43 @@ def test_repack_validation():
         == pql.PQL_ERR_INVALID_ARGUMENT
     assert L.pql_repack(S["w4a16_asym"], A, 1, 0, fake, fake, fake, fake, 4, 128, None) == pql.PQL_ERR_UNSUPPORTED
     assert L.pql_repack(S["mxfp8"], W, 0, 1, fake, None, fake + 4096, None, 4, 48, None) == pql.PQL_ERR_INVALID_ARGUMENT
+
+
+def _run_logged(code, env_value):
+    """Run `code` in a fresh interpreter (PQL_LOG is read once per process) and return its stderr."""
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("PQL_LOG", None)
+    if env_value is not None:
+        env["PQL_LOG"] = env_value
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return r.stderr
+
+
+LOG_CODE = """
+import ctypes, precision_quantized_linear_amd as pql
+L = pql.lib()
+c_i64 = ctypes.c_int64
+buf = ctypes.c_void_p(256)
+S = pql.SCHEMES
+# an empty GEMM (enqueues nothing), an unknown scheme, and a bad leading dimension
+assert L.pql_qgemm(S["fp8_row"], buf, buf, buf, buf, None, c_i64(0), c_i64(256), c_i64(512), buf, c_i64(256), None) == 0
+assert L.pql_qgemm(99, buf, buf, buf, buf, None, c_i64(8), c_i64(256), c_i64(512), buf, c_i64(256), None) != 0
+assert L.pql_quantize(S["fp8_block128"], 0, buf, c_i64(4), c_i64(256), c_i64(100), buf, buf, None, None,
+                      ctypes.c_size_t(0), None) != 0
+"""
+
+
+def test_pql_log_lines():
+    """PQL_LOG=1 logs every entry-point call with its shape and outcome; unset, the library prints nothing."""
+    err = _run_logged(LOG_CODE, "1")
+    lines = [l for l in err.splitlines() if l.startswith("[pql] ")]
+    assert len(lines) == 3, err
+    assert lines[0] == "[pql] qgemm FP8_ROW M=0 N=256 K=512: nothing to do"
+    assert lines[1].startswith("[pql] qgemm ") and "rejected (status" in lines[1] and "unknown scheme 99" in lines[1]
+    assert lines[2].startswith("[pql] quantize FP8_BLOCK128 activation M=4 N=0 K=256: rejected (status 1)")
+    assert "ldx" in lines[2]
+    assert "[pql]" not in _run_logged(LOG_CODE, None)
+    assert "[pql]" not in _run_logged(LOG_CODE, "0")
