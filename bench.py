@@ -375,18 +375,19 @@ def cpu_baseline(a_bits, w_bits, name, scheme, c_rows=None, gemm_rows=None):
                     oracle.bf16_to_f32(c_rows[:rows]).astype(np.float64), c64)))}} if c_rows is not None else {})}
 
 
-def measured_traffic(profile: str):
+def measured_traffic(profile: str, key: str = "traffic_bytes_per_launch"):
     """HBM bytes per launch of a kernel from its committed FETCH_SIZE / WRITE_SIZE summary
-    under profiles/, or None when that summary was taken on a different kernel source."""
+    under profiles/ (the line `key: bytes`), or None when that summary was taken on a
+    different kernel source."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     try:
         text = open(os.path.join(root, "profiles", profile)).read().splitlines()
         fields = dict(line.split(": ", 1) for line in text if ": " in line and line.split(": ", 1)[0] in
-                      ("traffic_bytes_per_launch", "kernel_source", "kernel_source_sha256_16"))
+                      (key, "kernel_source", "kernel_source_sha256_16"))
         src = os.path.join(root, fields["kernel_source"])
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        return int(fields["traffic_bytes_per_launch"]) if sha == fields["kernel_source_sha256_16"] else None
+        return int(fields[key]) if sha == fields["kernel_source_sha256_16"] else None
     except (OSError, KeyError, ValueError):
         return None
 
@@ -512,11 +513,15 @@ def main():
                                                                      "hbm_frac_median", "bytes")}
         peak = g["peak_tflops"]
         achieved = flops / (g["mean_us"] * 1e-6) / 1e12
-        prof = {"k_gemm_block256": "k_gemm_block256__fp8_block_dit.md",
-                "k_gemm32_fp8": "k_gemm32_fp8__fp8_row_dit.md"}.get(g["kernel"])
+        prof = {"k_gemm_block256": ("k_gemm_block256__fp8_block_dit.md", "traffic_bytes_per_launch"),
+                "k_gemm32_fp8": ("k_gemm32_fp8__fp8_row_dit.md", "traffic_bytes_per_launch"),
+                "k_gemm32<mxfp4>": ("k_gemm32_mx__mx_video_dit.md", "traffic_bytes_per_launch_mxfp4"),
+                "k_gemm32<mxfp8>": ("k_gemm32_mx__mx_video_dit.md", "traffic_bytes_per_launch_mxfp8"),
+                }.get(g["kernel"]) if (name, scheme) in (("fp8_block_dit", "fp8_block128"), ("fp8_row_dit", "fp8_row"),
+                                                          ("mx_video_dit", "mxfp4"), ("mx_video_dit", "mxfp8")) else None
         result["roofline"] = {"kernel": g["kernel"], "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                               "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                              "traffic": measured_traffic(prof) if prof else None,
+                              "traffic": measured_traffic(*prof) if prof else None,
                               "avg_us": g["mean_us"], "median_us": g["median_us"], "p10_us": g["p10_us"],
                               "p90_us": g["p90_us"], "algorithmic_flops": flops}
     result["workloads"] = summary
