@@ -31,8 +31,11 @@
 // Two kernels share this.  k_qlinear_few (K up to 4096, 8192 for one token)
 // quantizes the activation once per workgroup into LDS codes, while its first
 // batch of weight loads is already in flight, and its main loop then holds
-// only weight registers.  k_qlinear_small (longer K) quantizes in its main
-// loop: each lane casts its own row's 32 elements of every chunk.
+// only weight registers; with more than 4 rows its workgroups own 48 columns
+// instead of 32 (256 workgroups at N = 12288, one per CU), since the cast that
+// every workgroup repeats is then the larger part of its work.
+// k_qlinear_small (longer K) quantizes in its main loop: each lane casts its
+// own row's 32 elements of every chunk.
 #include <algorithm>
 #include <atomic>
 
@@ -277,7 +280,8 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_small(const uint16_t* __re
 //   4. the main loop: each chunk's A codes come from LDS, its weight bytes
 //      from the batch, computed as soon as the chunk's loads have landed; a
 //      slot past the last chunk repeats the batch's first and adds zero.
-template <int KIND, bool STATIC, bool EPI, int R, int J>   // J: column-chunks per thread (K <= 4096 J)
+// J: column-chunks per thread (K <= 4096 J); NB: 16-column blocks per workgroup
+template <int KIND, bool STATIC, bool EPI, int R, int J, int NB>
 __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __restrict__ a, int64_t M, int64_t K,
                                                         int64_t lda, const float* __restrict__ a_static,
                                                         const uint8_t* __restrict__ w,
@@ -286,11 +290,15 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
                                                         int64_t ldc) {
   using T = SmallKind<KIND>;
   constexpr int kJ = J;
-  constexpr bool kTwoPass = R == 16 && !T::kBlock && !STATIC;
+  constexpr int kC = 16 * NB;   // output columns of the workgroup
+  // 16 rows in 32-column workgroups (two per CU): the dynamic row maxima are taken on a first
+  // pass over the activation and the cast reloads it, so that its 16 chunks are not live
+  // across the barrier; one 48-column workgroup per CU keeps them.
+  constexpr bool kTwoPass = R == 16 && NB == 2 && !T::kBlock && !STATIC;
   extern __shared__ __attribute__((aligned(16))) uint8_t few_lds[];
   const int nk = (int)(K / 128);
-  float (*part)[16][kCols + 1] = reinterpret_cast<float (*)[16][kCols + 1]>(few_lds);
-  float (*red)[R] = reinterpret_cast<float (*)[R]>(few_lds + sizeof(float) * kWaves * 16 * (kCols + 1));
+  float (*part)[16][kC + 1] = reinterpret_cast<float (*)[16][kC + 1]>(few_lds);
+  float (*red)[R] = reinterpret_cast<float (*)[R]>(few_lds + sizeof(float) * kWaves * 16 * (kC + 1));
   float* s_row = &red[kWaves][0];                            // [R]
   float* sa = s_row + R;                                     // block-128: [nk][R]
   // [R][K + 16], 16-byte aligned for the 16-byte fragment reads
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * kCols;
+  const int64_t n0 = (int64_t)blockIdx.x * kC;
   const int cpr = (int)(K / 8);   // 16-byte activation chunks per row
   const int ldq = (int)K + 16;    // LDS bytes per row of codes
   const int mlast = (int)M - 1;
@@ -317,21 +325,24 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
       }
     }
   };
-  const uint8_t* wrow[2];
+  const uint8_t* wrow[NB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) wrow[j] = w + std::min<int64_t>(n0 + 16 * j + r16, N - 1) * K;
-  const int64_t nblk = n0 / 128;   // block-128: the 32 columns lie in one weight block (N % 128 == 0)
-  uint4 wv[kBatch][2][2];
-  float wsc[kBatch];
+  for (int j = 0; j < NB; ++j) wrow[j] = w + std::min<int64_t>(n0 + 16 * j + r16, N - 1) * K;
+  // block-128 (N % 128 == 0): the weight block of each 16-column block, clamped inside N
+  int64_t nblk[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) nblk[j] = std::min<int64_t>((n0 + 16 * j) / 128, N / 128 - 1);
+  uint4 wv[kBatch][NB][2];
+  float wsc[kBatch][NB];
   // slots u0 .. u1 - 1 of the batch starting at chunk ck0
   auto fetch = [&](int ck0, int u0 = 0, int u1 = kBatch) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = u0; u < u1; ++u) {
       const int ck = ck0 + u * kWaves < nk ? ck0 + u * kWaves : ck0;   // wave-uniform
       const int64_t k0 = (int64_t)ck * 128;
-      if constexpr (T::kBlock) wsc[u] = w_scales[nblk * nk + ck];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (T::kBlock) wsc[u][j] = w_scales[nblk[j] * nk + ck];
         wv[u][j][0] = ldg16(wrow[j] + k0 + 16 * g);
         wv[u][j][1] = ldg16(wrow[j] + k0 + 64 + 16 * g);
       }
@@ -374,8 +385,9 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
     }
   };
 
-  // With 16 rows the cast holds two of the batch's three chunks: the 16 activation chunks
-  // beside a whole batch would cost the second workgroup per CU.
+  // With 16 rows the cast holds two of the batch's three chunks: with 32 columns the 16
+  // activation chunks beside a whole batch would cost the second workgroup per CU, and with 48
+  // the third chunk's loads, issued before the cast, measured slower for block-128.
   constexpr int kEarly = R == 16 ? 2 : kBatch;
   const int ck_first = std::min(wave, nk - 1);   // a wave with no chunk (nk < 8) loads chunk nk - 1, unused
   load_act(a);
@@ -445,14 +457,19 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
 
   // ---- 4. the main loop
   const uint8_t* qrow = codes + std::min(r16, mlast) * ldq + 16 * g;   // the lane's row, as a GEMM operand
-  v4f_t acc[2] = {v4f_t{0.f, 0.f, 0.f, 0.f}, v4f_t{0.f, 0.f, 0.f, 0.f}};
-  v4i acci[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
-  auto chunk = [&](int ck, bool live, const uint4 (&wvc)[2][2], float wscale) __attribute__((always_inline)) {
+  v4f_t acc[NB];
+  v4i acci[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    acc[j] = v4f_t{0.f, 0.f, 0.f, 0.f};
+    acci[j] = v4i{0, 0, 0, 0};
+  }
+  auto chunk = [&](int ck, bool live, const uint4 (&wvc)[NB][2], const float (&wscale)[NB]) __attribute__((always_inline)) {
     uint4 q0 = gemm::lds16(qrow + ck * 128), q1 = gemm::lds16(qrow + ck * 128 + 64);
     if constexpr (T::kInt8) {
       if (!live) q0 = q1 = uint4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NB; ++j) {
         acci[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, q0), __builtin_bit_cast(v4i, wvc[j][0]),
                                                         acci[j], 0, 0, 0);
         acci[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, q1), __builtin_bit_cast(v4i, wvc[j][1]),
@@ -464,10 +481,10 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
       float sr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sr[r] = sa[ck * R + std::min(4 * g + r, mlast)];
-      const float sw = live ? wscale : 0.0f;
       const v8i qa = gemm::cat(q0, q1);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NB; ++j) {
+        const float sw = live ? wscale[j] : 0.0f;
         const v4f_t P = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, gemm::cat(wvc[j][0], wvc[j][1]),
                                                                         v4f_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
@@ -477,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
       if (!live) q0 = q1 = uint4{0u, 0u, 0u, 0u};
       const v8i qa = gemm::cat(q0, q1);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NB; ++j)
         acc[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, gemm::cat(wvc[j][0], wvc[j][1]), acc[j], 0, 0, 0,
                                                                   127, 0, 127);
     }
@@ -496,13 +513,13 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
 
   // ---- sums of the waves, then the epilogue (the scales of the row / column GEMMs)
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       part[wave][4 * g + r][16 * j + r16] = T::kInt8 ? __int_as_float(acci[j][r]) : acc[j][r];
   __syncthreads();
-  for (int e = t; e < 16 * kCols; e += kThreads) {
-    const int m = e / kCols, col = e - m * kCols;
+  for (int e = t; e < 16 * kC; e += kThreads) {
+    const int m = e / kC, col = e - m * kC;
     const int64_t n = n0 + col;
     if (m >= M || n >= N) continue;
     float v;
@@ -531,14 +548,14 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
   }
 }
 
-size_t few_lds_bytes(int R, bool block, int64_t K) {
-  const size_t head = sizeof(float) * (kWaves * 16 * (kCols + 1) + (kWaves + 1) * R + (block ? R * (K / 128) : 0));
+size_t few_lds_bytes(int R, int NB, bool block, int64_t K) {
+  const size_t head = sizeof(float) * (kWaves * 16 * (16 * NB + 1) + (kWaves + 1) * R + (block ? R * (K / 128) : 0));
   return (head + 15) / 16 * 16 + (size_t)R * (size_t)(K + 16);
 }
 
-template <int KIND, bool STATIC, bool EPI, int R, int J>
+template <int KIND, bool STATIC, bool EPI, int R, int J, int NB>
 hipError_t launch_few_epi(const SmallArgs& s, hipStream_t st) {
-  const size_t lds = few_lds_bytes(R, KIND == SMALL_BLOCK, s.K);
+  const size_t lds = few_lds_bytes(R, NB, KIND == SMALL_BLOCK, s.K);
   if (lds > 64 * 1024) {   // above the default dynamic-LDS limit: raise it once per device
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -546,22 +563,24 @@ hipError_t launch_few_epi(const SmallArgs& s, hipStream_t st) {
     static std::atomic<bool> configured[64] = {};
     if (dev >= 64) return hipErrorInvalidDevice;
     if (!configured[dev].load()) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qlinear_few<KIND, STATIC, EPI, R, J>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)few_lds_bytes(R, true, kFewMaxK));
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_qlinear_few<KIND, STATIC, EPI, R, J, NB>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)few_lds_bytes(R, NB, true, kFewMaxK));
       if (e != hipSuccess) return e;
       configured[dev].store(true);
     }
   }
-  hipLaunchKernelGGL((k_qlinear_few<KIND, STATIC, EPI, R, J>), dim3((unsigned)((s.N + kCols - 1) / kCols)),
+  hipLaunchKernelGGL((k_qlinear_few<KIND, STATIC, EPI, R, J, NB>), dim3((unsigned)((s.N + 16 * NB - 1) / (16 * NB))),
                      dim3(kThreads), lds, st, s.a, s.M, s.K, s.lda, s.a_static, s.w, s.w_scales, s.N, s.alpha, s.bias,
                      s.c, s.ldc);
   return hipGetLastError();
 }
 
-template <int KIND, bool STATIC, int R, int J = 1>
+// 16 staged rows: 48-column workgroups (256 of them at N = 12288, one per CU), since every
+// workgroup repeats the 16-row cast; fewer rows: 32 columns.
+template <int KIND, bool STATIC, int R, int J = 1, int NB = R == 16 ? 3 : 2>
 hipError_t launch_few(const SmallArgs& s, hipStream_t st) {
-  return (s.alpha != 1.0f || s.bias) ? launch_few_epi<KIND, STATIC, true, R, J>(s, st)
-                                     : launch_few_epi<KIND, STATIC, false, R, J>(s, st);
+  return (s.alpha != 1.0f || s.bias) ? launch_few_epi<KIND, STATIC, true, R, J, NB>(s, st)
+                                     : launch_few_epi<KIND, STATIC, false, R, J, NB>(s, st);
 }
 
 template <int KIND, bool STATIC>
