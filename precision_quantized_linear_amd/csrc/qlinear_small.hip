@@ -31,9 +31,10 @@
 // Two kernels share this.  k_qlinear_few (K up to 4096, 8192 for one token)
 // quantizes the activation once per workgroup into LDS codes, while its first
 // batch of weight loads is already in flight, and its main loop then holds
-// only weight registers; with more than 4 rows its workgroups own 48 columns
-// instead of 32 (256 workgroups at N = 12288, one per CU), since the cast that
-// every workgroup repeats is then the larger part of its work.
+// only weight registers; for wide outputs its workgroups own 48 columns
+// instead of 32 (256 workgroups at N = 12288, one per CU, rather than two on
+// half of the CUs), since every workgroup repeats the cast and streams its own
+// weight rows.
 // k_qlinear_small (longer K) quantizes in its main loop: each lane casts its
 // own row's 32 elements of every chunk.
 #include <algorithm>
@@ -291,9 +292,9 @@ __global__ __launch_bounds__(kThreads) void k_qlinear_few(const uint16_t* __rest
   using T = SmallKind<KIND>;
   constexpr int kJ = J;
   constexpr int kC = 16 * NB;   // output columns of the workgroup
-  // 16 rows in 32-column workgroups (two per CU): the dynamic row maxima are taken on a first
-  // pass over the activation and the cast reloads it, so that its 16 chunks are not live
-  // across the barrier; one 48-column workgroup per CU keeps them.
+  // 16 rows in 32-column workgroups (two may share a CU): the dynamic row maxima are taken on
+  // a first pass over the activation and the cast reloads it, so that its 16 chunks are not
+  // live across the barrier; 48-column workgroups, one per CU, keep them.
   constexpr bool kTwoPass = R == 16 && NB == 2 && !T::kBlock && !STATIC;
   extern __shared__ __attribute__((aligned(16))) uint8_t few_lds[];
   const int nk = (int)(K / 128);
@@ -575,12 +576,24 @@ hipError_t launch_few_epi(const SmallArgs& s, hipStream_t st) {
   return hipGetLastError();
 }
 
-// 16 staged rows: 48-column workgroups (256 of them at N = 12288, one per CU), since every
-// workgroup repeats the 16-row cast; fewer rows: 32 columns.
-template <int KIND, bool STATIC, int R, int J = 1, int NB = R == 16 ? 3 : 2>
+// Workgroups of 48 columns instead of 32 when that leaves fewer columns on the busiest of the
+// 256 CUs (N = 12288: 256 workgroups, one per CU, against 384, two on half of the CUs, each
+// repeating the activation cast and streaming its own weight rows); 32 keeps more workgroups
+// for narrower outputs.
+inline bool few_wide(int64_t N) {
+  constexpr int64_t kCUs = 256;
+  const int64_t per_cu32 = ((N + 31) / 32 + kCUs - 1) / kCUs * 32;
+  const int64_t per_cu48 = ((N + 47) / 48 + kCUs - 1) / kCUs * 48;
+  return per_cu48 < per_cu32;
+}
+
+template <int KIND, bool STATIC, int R, int J = 1>
 hipError_t launch_few(const SmallArgs& s, hipStream_t st) {
-  return (s.alpha != 1.0f || s.bias) ? launch_few_epi<KIND, STATIC, true, R, J, NB>(s, st)
-                                     : launch_few_epi<KIND, STATIC, false, R, J, NB>(s, st);
+  const bool epi = s.alpha != 1.0f || s.bias;
+  if (few_wide(s.N))
+    return epi ? launch_few_epi<KIND, STATIC, true, R, J, 3>(s, st)
+               : launch_few_epi<KIND, STATIC, false, R, J, 3>(s, st);
+  return epi ? launch_few_epi<KIND, STATIC, true, R, J, 2>(s, st) : launch_few_epi<KIND, STATIC, false, R, J, 2>(s, st);
 }
 
 template <int KIND, bool STATIC>

@@ -56,10 +56,12 @@ def test_fused_exact(scheme, M):
 
 
 # the staged-activation kernel at 1, 4 and 16 staged rows, and (K past its stage) the kernel that casts
-# in its main loop
+# in its main loop; N >= 8200 or so selects the staged kernel's 48-column workgroups (fewer columns per CU
+# than 32-column ones), here with a ragged last workgroup (8232 = 171 x 48 + 24; block-128: 8320)
 @pytest.mark.parametrize("scheme", FUSED)
 @pytest.mark.parametrize("M,N,K", [(1, 256, 128), (3, 300 * 4, 640), (16, 4100, 3072), (9, 384, 1152),
-                                   (1, 256, 6144), (1, 256, 8320), (2, 384, 4224), (16, 256, 4352)])
+                                   (1, 256, 6144), (1, 256, 8320), (2, 384, 4224), (16, 256, 4352),
+                                   (1, 8232, 640), (3, 8232, 640), (16, 8232, 1152)])
 def test_fused_matches_oracle(scheme, M, N, K):
     if scheme == "fp8_block128":
         N = -(-N // 128) * 128
@@ -73,9 +75,10 @@ def test_fused_matches_oracle(scheme, M, N, K):
 
 
 @pytest.mark.parametrize("scheme", FUSED)
-def test_fused_epilogue_and_strided_output(scheme):
+@pytest.mark.parametrize("N", [512, 8320])   # 32- and 48-column workgroups
+def test_fused_epilogue_and_strided_output(scheme, N):
     from test_gpu_exact import _check_sentinels, _sentinel_buffer
-    M, N, K = 7, 512, 640
+    M, K = 7, 640
     a_bits = wl.small_case(61, M, K)
     wq, wq_t = _weight(scheme, N, K, 62)
     bias = wl.f32_to_bf16_bits(np.random.default_rng(3).normal(0, 0.5, N).astype(np.float32))
@@ -88,9 +91,10 @@ def test_fused_epilogue_and_strided_output(scheme):
 
 @pytest.mark.parametrize("scheme", ["fp8_tensor", "fp8_block128"])
 @pytest.mark.parametrize("tiny", [False, True])
-def test_fused_static_scales(scheme, tiny):
+@pytest.mark.parametrize("N", [384, 8320])   # 32- and 48-column workgroups
+def test_fused_static_scales(scheme, tiny, N):
     """Static activation scales, including ones far below amax / 448 (quotients saturate)."""
-    M, N, K = 5, 384, 1024
+    M, K = 5, 1024
     a_bits = hard_input(71, M, K)
     rng = np.random.default_rng(72)
     shape = (1,) if scheme == "fp8_tensor" else (M, K // 128)
