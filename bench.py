@@ -43,7 +43,7 @@ RUNS = (("fp8_tensor_small", "fp8_tensor"), ("fp8_row_dit", "fp8_row"), ("mx_vid
 # --all adds the NEXT variants before the headline: int8 W8A8, the alpha / bias epilogue, static FP8 scales
 EXTRA = (("fp8_row_dit", "int8_row"), ("fp8_row_dit", "fp8_row+epilogue"), ("fp8_row_dit", "int8_row+epilogue"),
          ("fp8_block_dit", "fp8_block128+epilogue"), ("fp8_block_dit", "fp8_block128+static"),
-         ("fp8_tensor_small", "fp8_tensor+static"))
+         ("fp8_tensor_small", "fp8_tensor+static"), ("load_and_dequant", "w4a16_asym+fp8_block128"))
 DESCRIPTION = {
     "fp8_tensor_small": "FP8 e4m3 per-tensor dynamic scales, M=256 K=512 N=512",
     "fp8_row_dit": "FP8 e4m3 per-token activation x per-channel weight scales, M=4096 K=3072 N=12288, "
@@ -54,6 +54,8 @@ DESCRIPTION = {
     "w4a16_dit": "W4A16 int4 group-128 asymmetric, K=3072 N=12288",
     "fp8_decode": "FP8 per-token / block-128 qlinear for 1 and 16 tokens (fused activation quantize + GEMM), "
                   "K=3072 N=12288",
+    "load_and_dequant": "the int4 RTN weight quantizer on the W4A16 weight (N=12288 K=3072, once at load) and "
+                        "dequantize of that weight and of the block-128 activation (M=8192 K=5120)",
 }
 
 
@@ -65,8 +67,9 @@ def parse():
     p.add_argument("--only", default=None, help="time only this workload (NAME or NAME:SCHEME; its line is then "
                                                 "the last)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--all", action="store_true", help="also time int8 W8A8, the alpha / bias epilogue and static "
-                                                      "FP8 scales (before the headline)")
+    p.add_argument("--all", action="store_true", help="also time int8 W8A8, the alpha / bias epilogue, static "
+                                                      "FP8 scales, the load-time int4 quantizer and dequantize "
+                                                      "(before the headline)")
     p.add_argument("--copy-reference", action="store_true",
                    help="time torch's own bf16 -> fp8 cast at every quantizer size (the same bytes a quantizer "
                         "moves, without the scale arithmetic) and a cold read of the W4A16 weight, then exit")
@@ -273,6 +276,64 @@ def run_w4a16(torch, pql, steps, warmup):
     return lines
 
 
+# ----------------------------------------------------------------------------- load-time quantize, dequantize
+def run_load_and_dequant(torch, pql, steps, warmup):
+    """The two steps outside the per-call path: the int4 round-to-nearest weight quantizer (run once at
+    load) on the W4A16 weight, and dequantize (codes and scales back to bf16) of that weight and of the
+    block-128 activation.  Inputs rotate over >= 1 GiB of copies; HIP events per call; GB/s against the
+    algorithmic bytes (the input read once, the output written once)."""
+    import workloads as wl
+    lines = []
+
+    def line(scheme, role, op, rows, cols, kernel, byts, ms):
+        st = stats_us(ms)
+        return {"kind": "workload", "workload": "load_and_dequant", "scheme": scheme, "role": role, "op": op,
+                "M": rows, "N": 0, "K": cols, "kernel": kernel, **{k: round(v, 2) for k, v in st.items()},
+                "gbs_median": round(byts / (st["median_us"] * 1e-6) / 1e9, 1),
+                "hbm_frac_median": round(byts / (st["median_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "bytes": byts}
+
+    # int4 RTN quantize of the W4A16 weight (bf16 [12288, 3072] -> codes, scales, zero-points)
+    w = wl.WORKLOADS["w4a16_dit"]
+    w_bits = wl.weight(w)
+    byts = quant_bytes(pql, "w4a16_asym", "weight", w.N, w.K)
+    xs = [up(torch, w_bits)]
+    xs += [xs[0].clone() for _ in range(copies_for(2 * w.N * w.K) - 1)]
+    out = pql.quantize(xs[0], "w4a16_asym", "weight")
+    settle(torch, xs)
+
+    def qstep(i, ev):
+        f = lambda: pql.quantize(xs[i % len(xs)], "w4a16_asym", "weight", out=out)
+        ev(f) if ev else f()
+    _, ev = timed(torch, qstep, steps, warmup)
+    lines.append(line("w4a16_asym", "weight", "quantize", w.N, w.K, pql.kernel_name("quantize", "w4a16_asym", "weight"),
+                      byts, ev.ms()))
+    del xs
+
+    # dequantize: that weight, then the block-128 activation of the headline workload
+    wa = wl.WORKLOADS["fp8_block_dit"]
+    for scheme, role, q in (("w4a16_asym", "weight", out),
+                            ("fp8_block128", "activation", pql.quantize(up(torch, wl.activation(wa)), "fp8_block128",
+                                                                        "activation"))):
+        c, sc, z = pql.quantized_sizes(scheme, role, q.rows, q.cols)
+        byts = c + sc + z + 2 * q.rows * q.cols
+        qs = [q] + [pql.QTensor(q.scheme, q.role, q.rows, q.cols, q.codes.clone(), q.scales.clone(),
+                                None if q.zeros is None else q.zeros.clone())
+                    for _ in range(copies_for(c + sc + z) - 1)]
+        y = torch.empty((q.rows, q.cols), dtype=torch.bfloat16, device="cuda")
+        settle(torch, [t for x in qs for t in (x.codes, x.scales, x.zeros)])
+
+        def dstep(i, ev):
+            f = lambda: pql.dequantize(qs[i % len(qs)], out=y)
+            ev(f) if ev else f()
+        _, ev = timed(torch, dstep, steps, warmup)
+        lines.append(line(scheme, role, "dequantize", q.rows, q.cols, pql.kernel_name("dequantize", scheme, role),
+                          byts, ev.ms()))
+        del qs, y
+    del out
+    torch.cuda.empty_cache()
+    return lines
+
+
 # ----------------------------------------------------------------------------- few-token qlinear
 def run_decode(torch, pql, steps, warmup):
     """qlinear for 1 and 16 tokens on the per-token FP8 workload's weight (N=12288, K=3072):
@@ -463,13 +524,24 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    every = RUNS[:-1] + (EXTRA if args.all else ()) + RUNS[-1:]
+    # --only reaches an --all entry by its exact NAME:SCHEME, or by NAME when no default run has that name
+    extra = EXTRA if args.all else tuple(
+        r for r in EXTRA if args.only is not None and (args.only == f"{r[0]}:{r[1]}" or (
+            args.only == r[0] and all(x[0] != r[0] for x in RUNS))))
+    every = RUNS[:-1] + extra + RUNS[-1:]
     runs = [r for r in every if args.only is None or args.only in (r[0], f"{r[0]}:{r[1]}")]
     if not runs:
         print(f"unknown workload {args.only!r}", file=sys.stderr)
         sys.exit(2)
     summary, head, keep = {}, None, {}
     for name, scheme in runs:
+        if name == "load_and_dequant":
+            for line in run_load_and_dequant(torch, pql, args.steps, args.warmup):
+                summary[f"{name} {line['op']} {line['scheme']} {line['role']}"] = {
+                    "kernel": line["kernel"], "median_us": line["median_us"],
+                    "hbm_frac_median": line["hbm_frac_median"]}
+                print(json.dumps(line), flush=True)
+            continue
         if name in ("w4a16_dit", "fp8_decode"):
             lines = (run_w4a16 if name == "w4a16_dit" else run_decode)(torch, pql, args.steps, args.warmup)
             for line in lines:
@@ -483,6 +555,8 @@ def main():
         head = line
         if (name, scheme) != runs[-1]:
             print(json.dumps(line), flush=True)
+    if head is None:   # only the load-time quantizer and dequantize lines were asked for
+        return
     name, scheme = head["workload"], head["scheme"]
     g = head["gemm"]
     flops = 2 * head["M"] * head["N"] * head["K"]

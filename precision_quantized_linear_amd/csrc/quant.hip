@@ -450,64 +450,76 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-__global__ __launch_bounds__(256) void k_dequant(int kind, const uint8_t* __restrict__ codes,
-                                                 const void* __restrict__ scales,
-                                                 const uint8_t* __restrict__ zeros, int64_t rows,
-                                                 int64_t cols, uint16_t* __restrict__ y, int64_t ldy) {
+// Dequantize, one instance per code layout (KIND as numbered by the launcher):
+// every chunk's codes and scales are loaded before any is converted (a chunk
+// past the row repeats the row's last and is not stored), so the loads of a
+// lane are in flight together.
+template <int KIND>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes, const void* __restrict__ scales,
+                                                 const uint8_t* __restrict__ zeros, int64_t rows, int64_t cols,
+                                                 uint16_t* __restrict__ y, int64_t ldy) {
+  constexpr bool kFp4 = KIND == 5 || KIND == 8;   // MXFP4, dual-scale MXFP4: 4 code bytes per chunk
+  constexpr bool kInt4 = KIND == 6;               // W4A16: 4 code bytes, bf16 scale and zero-point per group
   const Seg g;
   if (g.row >= rows) return;
   const int64_t cpr = cols >> 3, r = g.row;
+  const float* sf = static_cast<const float*>(scales);
+  const uint8_t* sb = static_cast<const uint8_t*>(scales);
+  uint2 w8[kSegU];
+  uint32_t w4[kSegU];
+  float sc[kSegU], aux[kSegU];   // aux: the int4 zero-point, or the dual-scale coarse scale
+#pragma unroll
+  for (int u = 0; u < kSegU; ++u) {
+    const int64_t c = g.c0 + 64 * u < cpr ? g.c0 + 64 * u : cpr - 1;
+    if constexpr (kFp4) {
+      w4[u] = *reinterpret_cast<const uint32_t*>(codes + r * (cols >> 1) + c * 4);
+      const int64_t b = c >> 2;
+      sc[u] = e8m0_value(sb[((b >> 3) * rows + r) * 8 + (b & 7)]);
+      if constexpr (KIND == 8) aux[u] = reinterpret_cast<const float*>(zeros)[(c >> 6) * rows + r];
+    } else if constexpr (kInt4) {
+      w4[u] = reinterpret_cast<const uint32_t*>(codes)[r * cpr + c];
+      const int64_t gi = (c >> 4) * rows + r;   // group-major
+      sc[u] = __uint_as_float((uint32_t)static_cast<const uint16_t*>(scales)[gi] << 16);
+      aux[u] = (float)zeros[gi];
+    } else {
+      w8[u] = *reinterpret_cast<const uint2*>(codes + r * cols + c * 8);
+      if constexpr (KIND == 0) sc[u] = sf[0];
+      else if constexpr (KIND == 1 || KIND == 7) sc[u] = sf[r];
+      else if constexpr (KIND == 2) sc[u] = sf[r * (cols >> 7) + (c >> 4)];
+      else if constexpr (KIND == 3) sc[u] = sf[(r >> 7) * (cols >> 7) + (c >> 4)];
+      else {   // MXFP8
+        const int64_t b = c >> 2;
+        sc[u] = e8m0_value(sb[((b >> 2) * rows + r) * 4 + (b & 3)]);
+      }
+    }
+  }
 #pragma unroll
   for (int u = 0; u < kSegU; ++u) {
     const int64_t c = g.c0 + 64 * u;
-    if (c >= cpr) continue;
     float v[8];
-    if (kind <= 5 || kind == 8) {
-      if (kind == 5 || kind == 8) {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + r * (cols >> 1) + c * 4);
-        const int64_t b = c >> 2;
-        const float sc = e8m0_value(static_cast<const uint8_t*>(scales)[((b >> 3) * rows + r) * 8 + (b & 7)]);
+    if constexpr (kFp4) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((w >> (4 * j)) & 0xF) * sc;   // exact
-        if (kind == 8) {   // dual-scale: times the coarse scale (group-major [K/512, rows]), one rounding
-          const float cs = reinterpret_cast<const float*>(zeros)[(c >> 6) * rows + r];
+      for (int j = 0; j < 8; ++j) v[j] = e2m1_decode((w4[u] >> (4 * j)) & 0xF) * sc[u];   // exact
+      if constexpr (KIND == 8) {   // dual-scale: times the coarse scale, one rounding
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] *= cs;
-        }
-      } else {
-        const uint2 w = *reinterpret_cast<const uint2*>(codes + r * cols + c * 8);
-        float sc;
-        const float* sf = static_cast<const float*>(scales);
-        switch (kind) {
-          case 0: sc = sf[0]; break;
-          case 1: sc = sf[r]; break;
-          case 2: sc = sf[r * (cols >> 7) + (c >> 4)]; break;
-          case 3: sc = sf[(r >> 7) * (cols >> 7) + (c >> 4)]; break;
-          default: {
-            const int64_t b = c >> 2;
-            sc = e8m0_value(static_cast<const uint8_t*>(scales)[((b >> 2) * rows + r) * 4 + (b & 3)]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = e4m3_decode((w.x >> (8 * j)) & 0xFF) * sc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[4 + j] = e4m3_decode((w.y >> (8 * j)) & 0xFF) * sc;
+        for (int j = 0; j < 8; ++j) v[j] *= aux[u];
       }
-    } else if (kind == 7) {
-      const uint2 w = *reinterpret_cast<const uint2*>(codes + r * cols + c * 8);
-      const float sc = static_cast<const float*>(scales)[r];
+    } else if constexpr (kInt4) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = (float)(int8_t)(((j < 4 ? w.x : w.y) >> (8 * (j & 3))) & 0xFF) * sc;
+      for (int j = 0; j < 8; ++j) v[j] = ((float)((w4[u] >> (4 * j)) & 0xF) - aux[u]) * sc[u];
+    } else if constexpr (KIND == 7) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = (float)(int8_t)(((j < 4 ? w8[u].x : w8[u].y) >> (8 * (j & 3))) & 0xFF) * sc[u];
     } else {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(codes)[r * cpr + c];
-      const int64_t gi = (c >> 4) * rows + r;   // group-major
-      const float s = __uint_as_float((uint32_t)static_cast<const uint16_t*>(scales)[gi] << 16);
-      const float z = (float)zeros[gi];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = ((float)((w >> (4 * j)) & 0xF) - z) * s;
+      for (int j = 0; j < 4; ++j) v[j] = e4m3_decode((w8[u].x >> (8 * j)) & 0xFF) * sc[u];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[4 + j] = e4m3_decode((w8[u].y >> (8 * j)) & 0xFF) * sc[u];
     }
-    stg16(y + r * ldy + c * 8,
-          make_uint4(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]), bf16x2_rne(v[4], v[5]), bf16x2_rne(v[6], v[7])));
+    if (c < cpr)
+      stg16(y + r * ldy + c * 8, make_uint4(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]), bf16x2_rne(v[4], v[5]),
+                                            bf16x2_rne(v[6], v[7])));
   }
 }
 
@@ -595,8 +607,20 @@ hipError_t launch_quant_int4(bool sym, const uint16_t* x, int64_t rows, int64_t 
 
 hipError_t launch_dequant(int kind, const void* codes, const void* scales, const uint8_t* zeros,
                           int64_t rows, int64_t cols, uint16_t* y, int64_t ldy, hipStream_t st) {
-  hipLaunchKernelGGL(k_dequant, seg_grid(rows, cols), dim3(256), 0, st, kind, static_cast<const uint8_t*>(codes),
-                     scales, zeros, rows, cols, y, ldy);
+  const dim3 grid = seg_grid(rows, cols), block(256);
+  const uint8_t* cb = static_cast<const uint8_t*>(codes);
+  switch (kind) {
+    case 0: hipLaunchKernelGGL(k_dequant<0>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    case 1: hipLaunchKernelGGL(k_dequant<1>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    case 2: hipLaunchKernelGGL(k_dequant<2>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    case 3: hipLaunchKernelGGL(k_dequant<3>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    case 4: hipLaunchKernelGGL(k_dequant<4>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    case 5: hipLaunchKernelGGL(k_dequant<5>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    case 6: hipLaunchKernelGGL(k_dequant<6>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    case 7: hipLaunchKernelGGL(k_dequant<7>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    case 8: hipLaunchKernelGGL(k_dequant<8>, grid, block, 0, st, cb, scales, zeros, rows, cols, y, ldy); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
