@@ -67,6 +67,13 @@ CASES = [
     ("w4a16_sym", 3, 130, 2048, "k_w4a16_gemv<16 cols>"),
     ("w4a16_asym", 16, 4100, 1536, "k_w4a16_gemv<48 cols>"),
     ("w4a16_asym", 7, 100, 512, "k_w4a16_gemv<48 cols>"),
+    # the 48-column GEMV's 12 waves with full 3-group batches and a partial last one (K / 128 = 48, 34, 25),
+    # and the 16-column GEMV looping over several 4-group batches (64, 100 groups)
+    ("w4a16_asym", 8, 4100, 6144, "k_w4a16_gemv<48 cols>"),
+    ("w4a16_asym", 12, 520, 4352, "k_w4a16_gemv<48 cols>"),
+    ("w4a16_sym", 5, 388, 3200, "k_w4a16_gemv<48 cols>"),
+    ("w4a16_asym", 1, 260, 8192, "k_w4a16_gemv<16 cols>"),
+    ("w4a16_asym", 2, 130, 12800, "k_w4a16_gemv<16 cols>"),
     ("w4a16_sym", 33, 388, 1152, "k_w4a16_small"),
     ("w4a16_asym", 300, 388, 1152, "k_w4a16_mm_256x64x64"),
     ("w4a16_asym", 2304, 4100, 512, "k_w4a16_mm_256x128x64"),
