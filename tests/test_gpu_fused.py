@@ -61,7 +61,8 @@ def test_fused_exact(scheme, M):
 @pytest.mark.parametrize("scheme", FUSED)
 @pytest.mark.parametrize("M,N,K", [(1, 256, 128), (3, 300 * 4, 640), (16, 4100, 3072), (9, 384, 1152),
                                    (1, 256, 6144), (1, 256, 8320), (2, 384, 4224), (16, 256, 4352),
-                                   (1, 8232, 640), (3, 8232, 640), (16, 8232, 1152)])
+                                   (1, 8232, 640), (3, 8232, 640), (16, 8232, 1152), (1, 8232, 6144),
+                                   (16, 8232, 4096)])
 def test_fused_matches_oracle(scheme, M, N, K):
     if scheme == "fp8_block128":
         N = -(-N // 128) * 128
