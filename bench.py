@@ -507,6 +507,17 @@ def copy_reference(torch, steps):
                           "tbs_median": round(byts / (st["median_us"] * 1e-6) / 1e12, 2)}), flush=True)
 
 
+def select_runs(only, all_):
+    """The (workload, scheme) runs of one invocation, the headline last: every default run, the --all
+    entries before the headline when asked for, or the one --only names (NAME or NAME:SCHEME).  --only
+    reaches an --all entry by its exact NAME:SCHEME, or by NAME when no default run has that name."""
+    extra = EXTRA if all_ else tuple(
+        r for r in EXTRA if only is not None and (only == f"{r[0]}:{r[1]}" or (
+            only == r[0] and all(x[0] != r[0] for x in RUNS))))
+    every = RUNS[:-1] + extra + RUNS[-1:]
+    return [r for r in every if only is None or only in (r[0], f"{r[0]}:{r[1]}")]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -524,12 +535,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    # --only reaches an --all entry by its exact NAME:SCHEME, or by NAME when no default run has that name
-    extra = EXTRA if args.all else tuple(
-        r for r in EXTRA if args.only is not None and (args.only == f"{r[0]}:{r[1]}" or (
-            args.only == r[0] and all(x[0] != r[0] for x in RUNS))))
-    every = RUNS[:-1] + extra + RUNS[-1:]
-    runs = [r for r in every if args.only is None or args.only in (r[0], f"{r[0]}:{r[1]}")]
+    runs = select_runs(args.only, args.all)
     if not runs:
         print(f"unknown workload {args.only!r}", file=sys.stderr)
         sys.exit(2)
