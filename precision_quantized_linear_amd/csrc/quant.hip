@@ -381,35 +381,43 @@ __global__ __launch_bounds__(256) void k_int4(const uint16_t* __restrict__ x, in
     const int64_t c = g.c0 + 64 * u;
     float f[8];
     chunk_to_f32(v[u], f);
-    float s, z;
+    // The group's range over its fixed divisor (7 or 15) and -lo / s are correctly rounded
+    // quotients: by reciprocal and one correction where the quotient is a normal number (a
+    // finite dividend of at least 2^-100), by the IEEE division otherwise.
+    auto by_const = [](float d, float den, float rcp_den) {
+      return d >= 0x1p-100f && d <= 0x1.fffffep127f ? div_rn_markstein(d, den, rcp_den) : __fdiv_rn(d, den);
+    };
+    float s, z, lo = 0.0f, hi = 0.0f;
     if constexpr (SYM) {
       const float amax = group16_max(chunk_absmax(v[u]));
-      s = __uint_as_float(f32_to_bf16_rne(__fdiv_rn(amax, 7.0f)) << 16);
+      s = __uint_as_float(f32_to_bf16_rne(by_const(amax, 7.0f, 1.0f / 7.0f)) << 16);
       z = 8.0f;
       if (s == 0.0f) s = 1.0f;
     } else {
-      float lo = 0.0f, hi = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) { lo = fminf(lo, f[j]); hi = fmaxf(hi, f[j]); }
       lo = group16_min(lo);
       hi = group16_max(hi);
-      s = __uint_as_float(f32_to_bf16_rne(__fdiv_rn(hi - lo, 15.0f)) << 16);
-      if (s == 0.0f) {
-        s = 1.0f;
-        z = 0.0f;
-      } else {
-        z = fminf(fmaxf(__builtin_rintf(__fdiv_rn(-lo, s)), 0.0f), 15.0f);
-      }
+      s = __uint_as_float(f32_to_bf16_rne(by_const(hi - lo, 15.0f, 1.0f / 15.0f)) << 16);
+      z = 0.0f;
+      if (s == 0.0f) s = 1.0f;
     }
     if (c >= cpr) continue;
+    // Element quotients x / s (and -lo / s): a zero quotient's sign cannot change a code
+    // (rint(+-0) + z = z), so the correction's +0 for -0 needs no sign fix-up.
+    const bool fast = s >= kSmallestFastScale;
+    const float rcp = fast ? __fdiv_rn(1.0f, s) : 0.0f;
+    if constexpr (!SYM) {
+      if (hi - lo > 0.0f)   // s == 1 from a zero range keeps z = 0
+        z = fminf(fmaxf(__builtin_rintf(fast ? div_rn_markstein(-lo, s, rcp) : __fdiv_rn(-lo, s)), 0.0f), 15.0f);
+    }
     float q[8];
-    if (s >= kSmallestFastScale) {
-      const float rcp = __fdiv_rn(1.0f, s);
+    if (fast) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = quot<true>(f[j], s, rcp);
+      for (int j = 0; j < 8; ++j) q[j] = div_rn_markstein(f[j], s, rcp);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) q[j] = quot<false>(f[j], s, 0.0f);
+      for (int j = 0; j < 8; ++j) q[j] = __fdiv_rn(f[j], s);
     }
     uint32_t w = 0;
 #pragma unroll
